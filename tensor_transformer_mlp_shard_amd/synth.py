@@ -1,0 +1,125 @@
+"""Seeded synthetic inputs and the workload table.
+
+This module only draws random tensors and describes shapes. It holds none of the
+method's arithmetic (no products, no activation, no reduction), so that both the
+fp64 oracle's tests and the HIP path can take their inputs from it.
+
+Every tensor is drawn on the host with a seeded ``torch.Generator`` as float32
+``randn * sigma`` and then rounded to nearest-even to the storage dtype (bf16, or
+kept fp32 for the fp32 workload).  Draw order is fixed per workload kind and
+given in each generator below.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "seeded", "randn", "mlp_inputs", "attn_inputs", "inputs_for"]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str            # "mlp" or "attn"
+    T: int               # tokens (micro-batch x sequence, flattened)
+    h: int               # hidden size
+    F: int               # full FFN width (mlp) or full QKV width (attn)
+    tp: int              # tensor-parallel degree
+    dtype: str           # "bf16" or "fp32"
+    sigma_w: float       # weight / bias std
+    seed: int
+    full: bool           # draw unsharded weights (then slice) or the rank's shard only
+    note: str = field(default="", compare=False)
+
+    @property
+    def f(self) -> int:
+        return self.F // self.tp
+
+
+# Sizes follow the pages' workloads: the GPT launch example of the tutorial
+# (24 layers, hidden 1024, 16 heads, sequence 1024, micro-batch 4, TP=2), the
+# 1.3B single-GPU case of the course introduction (hidden 2048, sequence 1024,
+# micro-batch 4) and the 175B tensor-parallel case (hidden 12288, QKV
+# 12288 x 36864 in 8 shards of 12288 x 4608).  FFN width = 4 x hidden.
+WORKLOADS = {
+    "tiny_tp2_fp32": Workload("tiny_tp2_fp32", "mlp", 128, 256, 1024, 2, "fp32", 0.02, 1235, True,
+                              "X[128x256], A_i[256x512], B_i[512x256]; unsharded A[256x1024] too"),
+    "gpt_h1024_tp2": Workload("gpt_h1024_tp2", "mlp", 4096, 1024, 4096, 2, "bf16", 0.02, 1236, True,
+                              "GPT 24-layer h=1024, seq 1024 x micro-batch 4, TP=2 rank MLP shard"),
+    "gpt_1p3b_tp1": Workload("gpt_1p3b_tp1", "mlp", 4096, 2048, 8192, 1, "bf16", 0.02, 1237, True,
+                             "1.3B GPT h=2048 ffn=8192, seq 1024 x micro-batch 4, TP=1 (whole MLP)"),
+    "gpt175b_mlp_tp8": Workload("gpt175b_mlp_tp8", "mlp", 2048, 12288, 49152, 8, "bf16", 0.006, 1238, False,
+                                "175B MLP shard at TP=8: X[2048x12288], A_i[12288x6144], B_i[6144x12288]"),
+    "gpt175b_attn_tp8": Workload("gpt175b_attn_tp8", "attn", 8192, 12288, 36864, 8, "bf16", 0.006, 1239, False,
+                                 "175B attention linears at TP=8: QKV 12288->4608 column shard, "
+                                 "out-proj 1536->12288 row shard"),
+}
+
+_TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}
+
+
+def seeded(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def randn(gen: torch.Generator, shape, sigma: float, dtype: str) -> torch.Tensor:
+    """float32 N(0, sigma^2) draw, rounded to ``dtype`` (round-to-nearest-even)."""
+    t = torch.randn(*shape, generator=gen, dtype=torch.float32)
+    if sigma != 1.0:
+        t.mul_(sigma)
+    return t.to(_TORCH_DTYPE[dtype]).contiguous()
+
+
+def mlp_inputs(T: int, h: int, F: int, tp: int, dtype: str, sigma_w: float, seed: int,
+               full: bool = True, sigma_x: float = 1.0, sigma_dy: float = 1.0) -> dict:
+    """Inputs of one MLP shard.  Draw order: X, A, b1, B, b2, dY.
+
+    With ``full`` the unsharded A[h x F], b1[F], B[F x h] are drawn (callers take
+    rank shards by slicing); otherwise A, b1, B are already the rank's shard of
+    width f = F / tp.  b2[h] is the row-parallel output bias.
+    """
+    if F % tp:
+        raise ValueError("F must be divisible by tp")
+    width = F if full else F // tp
+    g = seeded(seed)
+    out = {}
+    out["X"] = randn(g, (T, h), sigma_x, dtype)
+    out["A"] = randn(g, (h, width), sigma_w, dtype)
+    out["b1"] = randn(g, (width,), sigma_w, dtype)
+    out["B"] = randn(g, (width, h), sigma_w, dtype)
+    out["b2"] = randn(g, (h,), sigma_w, dtype)
+    out["dY"] = randn(g, (T, h), sigma_dy, dtype)
+    out["full"] = full
+    return out
+
+
+def attn_inputs(T: int, h: int, qkv_width: int, tp: int, dtype: str, sigma_w: float, seed: int) -> dict:
+    """Inputs of the two attention-linear shards (rank shards drawn directly).
+
+    Draw order: X[T x h], W_qkv[h x qkv/tp], b_qkv[qkv/tp], O[T x h/tp],
+    W_o[h/tp x h], b_o[h], dQKV[T x qkv/tp], dY[T x h].
+    """
+    if qkv_width % tp or h % tp:
+        raise ValueError("widths must be divisible by tp")
+    g = seeded(seed)
+    q = qkv_width // tp
+    k = h // tp
+    out = {}
+    out["X"] = randn(g, (T, h), 1.0, dtype)
+    out["W_qkv"] = randn(g, (h, q), sigma_w, dtype)
+    out["b_qkv"] = randn(g, (q,), sigma_w, dtype)
+    out["O"] = randn(g, (T, k), 1.0, dtype)
+    out["W_o"] = randn(g, (k, h), sigma_w, dtype)
+    out["b_o"] = randn(g, (h,), sigma_w, dtype)
+    out["dQKV"] = randn(g, (T, q), 1.0, dtype)
+    out["dY"] = randn(g, (T, h), 1.0, dtype)
+    return out
+
+
+def inputs_for(w: Workload) -> dict:
+    if w.kind == "mlp":
+        return mlp_inputs(w.T, w.h, w.F, w.tp, w.dtype, w.sigma_w, w.seed, full=w.full)
+    return attn_inputs(w.T, w.h, w.F, w.tp, w.dtype, w.sigma_w, w.seed)

@@ -1,0 +1,41 @@
+"""Seeded input generator: determinism, rounding, shapes."""
+import numpy as np
+import torch
+
+from tensor_transformer_mlp_shard_amd import synth
+
+
+def test_same_seed_same_bytes():
+    a = synth.mlp_inputs(16, 32, 64, 2, "bf16", 0.02, seed=99)
+    b = synth.mlp_inputs(16, 32, 64, 2, "bf16", 0.02, seed=99)
+    for k in ("X", "A", "b1", "B", "b2", "dY"):
+        assert torch.equal(a[k].view(torch.int16), b[k].view(torch.int16)), k
+    c = synth.mlp_inputs(16, 32, 64, 2, "bf16", 0.02, seed=100)
+    assert not torch.equal(a["X"], c["X"])
+
+
+def test_bf16_rounding_is_nearest_even():
+    # halfway cases between two bf16 values round to the even mantissa
+    bits = np.array([0x3F808000, 0x3F818000, 0xBF808000, 0x3F80C000, 0x3F807FFF], dtype=np.uint32)
+    x = torch.from_numpy(bits.view(np.float32).copy())
+    got = x.to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    assert list(got) == [0x3F80, 0x3F82, 0xBF80, 0x3F81, 0x3F80]
+
+
+def test_workload_shapes():
+    w = synth.WORKLOADS
+    assert (w["gpt175b_mlp_tp8"].T, w["gpt175b_mlp_tp8"].h, w["gpt175b_mlp_tp8"].f) == (2048, 12288, 6144)
+    assert (w["gpt_h1024_tp2"].f, w["gpt_1p3b_tp1"].f, w["tiny_tp2_fp32"].f) == (2048, 8192, 512)
+    assert w["gpt175b_attn_tp8"].F // w["gpt175b_attn_tp8"].tp == 4608
+    d = synth.mlp_inputs(8, 16, 64, 4, "fp32", 0.02, seed=1, full=False)
+    assert d["A"].shape == (16, 16) and d["B"].shape == (16, 16) and d["b1"].shape == (16,)
+    assert d["X"].dtype == torch.float32
+    e = synth.attn_inputs(8, 64, 192, 8, "bf16", 0.006, seed=2)
+    assert e["W_qkv"].shape == (64, 24) and e["O"].shape == (8, 8) and e["W_o"].shape == (8, 64)
+    assert e["X"].dtype == torch.bfloat16
+
+
+def test_sigma_scaling():
+    d = synth.mlp_inputs(256, 512, 512, 1, "fp32", 0.02, seed=3)
+    assert abs(float(d["A"].std()) - 0.02) < 0.001
+    assert abs(float(d["X"].std()) - 1.0) < 0.02
