@@ -1,0 +1,278 @@
+"""Throughput of one rank's tensor-parallel Transformer-layer shard, fwd + bwd, bf16.
+
+One step runs every operation of the shard once, through the C ABI, on
+synthetic inputs already resident in HBM:
+  * the 175B-shaped MLP shard at TP=8 (T=2048 tokens, h=12288, f=6144):
+    forward (X A_i + b1 -> GeLU -> H B_i) and backward (dZ with GeLU', dB, dA,
+    dX, db1, db2);
+  * the 175B-shaped attention linears at TP=8 (T=8192 tokens): the QKV column
+    shard (12288 -> 4608, with bias) and the output-projection row shard
+    (1536 -> 12288), each forward and backward (dX, dW, db).
+The metric is algorithmic matrix FLOP per step (2 M N K per product) divided by
+the step time, in TFLOP/s, and its fraction of the MI355X dense bf16 matrix
+peak (2.5 PFLOP/s).
+
+Prints one JSON line.  Extra fields: per-part times, a roofline entry for the
+kernel with the most time in the step (timed with HIP events around its
+launches by the library's trace), and the fp64 CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+HBM_PEAK_GBS = 8000.0
+METRIC = "TFLOP/s per TP shard fwd+bwd (bf16) + % of MI355X bf16 MFMA peak"
+
+
+def _flops_mlp(T, h, f):
+    return 2.0 * T * h * f * 2 * 3      # 2 forward + 4 backward products, each 2 T h f
+
+
+def _flops_attn(T, h, q, k):
+    qkv = 2.0 * T * h * q
+    proj = 2.0 * T * k * h
+    return 3 * qkv + 3 * proj
+
+
+class Shard:
+    """Device-resident inputs, outputs and workspaces of the two parts."""
+
+    def __init__(self, device):
+        import torch
+
+        import tensor_transformer_mlp_shard_amd as tps
+        from tensor_transformer_mlp_shard_amd import _native, synth
+
+        self.tps = tps
+        self.torch = torch
+        wm = synth.WORKLOADS["gpt175b_mlp_tp8"]
+        wa = synth.WORKLOADS["gpt175b_attn_tp8"]
+        self.wm, self.wa = wm, wa
+        m = synth.inputs_for(wm)
+        a = synth.inputs_for(wa)
+        self.host_mlp, self.host_attn = m, a
+        d = lambda t: t.to(device)  # noqa: E731
+        self.X, self.A, self.b1, self.B, self.dY = (d(m[k]) for k in ("X", "A", "b1", "B", "dY"))
+        self.Xa, self.Wq, self.bq, self.O, self.Wo, self.dQ, self.dYa = (
+            d(a[k]) for k in ("X", "W_qkv", "b_qkv", "O", "W_o", "dQKV", "dY"))
+        T, h, f, p = wm.T, wm.h, wm.f, wm.tp
+        bf, fp = torch.bfloat16, torch.float32
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)  # noqa: E731
+        self.fwd_out = {"Z": e((T, f), bf), "H": e((T, f), bf), "Y": e((T, h), bf)}
+        self.bwd_out = {"dX": e((T, h), bf), "dA": e((h, f), fp), "dB": e((f, h), fp), "db1": e((f,), fp),
+                        "db2": e((h,), fp)}
+        self.ws_mlp = e((tps.workspace_size(_native.TP_OP_MLP_SHARD_BWD, T, h, wm.F, p, bf),), torch.uint8)
+        Ta, ha, q, k = wa.T, wa.h, wa.F // wa.tp, wa.h // wa.tp
+        self.q_out = {"dX": e((Ta, ha), bf), "dW": e((ha, q), fp), "db": e((q,), fp)}
+        self.o_out = {"dX": e((Ta, k), bf), "dW": e((k, ha), fp), "db": e((ha,), fp)}
+        self.ws_q = e((tps.workspace_size(_native.TP_OP_COLUMN_LINEAR_BWD, Ta, ha, wa.F, wa.tp, bf),), torch.uint8)
+        self.ws_o = e((tps.workspace_size(_native.TP_OP_ROW_LINEAR_BWD, Ta, ha, ha, wa.tp, bf),), torch.uint8)
+        self.flops_mlp = _flops_mlp(T, h, f)
+        self.flops_attn = _flops_attn(Ta, ha, q, k)
+
+    def mlp_step(self):
+        tps = self.tps
+        o = self.fwd_out
+        tps.mlp_shard_fwd(self.X, self.A, self.b1, self.B, tp_size=self.wm.tp, out=o)
+        tps.mlp_shard_bwd(self.X, self.A, self.B, o["Z"], o["H"], self.dY, tp_size=self.wm.tp, want_db2=True,
+                          out=self.bwd_out, workspace=self.ws_mlp)
+
+    def attn_step(self):
+        tps = self.tps
+        p = self.wa.tp
+        tps.column_linear(self.Xa, self.Wq, self.bq, tp_size=p)
+        tps.column_linear_bwd(self.Xa, self.Wq, self.dQ, tp_size=p, out=self.q_out, workspace=self.ws_q)
+        tps.row_linear(self.O, self.Wo, None, tp_size=p)
+        tps.row_linear_bwd(self.O, self.Wo, self.dYa, tp_size=p, out=self.o_out, workspace=self.ws_o)
+
+    def step(self):
+        self.mlp_step()
+        self.attn_step()
+
+
+def time_steps(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(stop) / steps, wall * 1e3 / steps
+
+
+def roofline_from_trace(tps, torch, fn, steps):
+    """Per-kernel HIP-event times over `steps` steps (the library brackets each
+    launch on its own stream); returns (dominant kernel entry, all entries)."""
+    tps.trace_start(4096)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    kernels = tps.trace_stop()
+    dom = max(kernels, key=lambda k: k["total_ms"])
+    return dom, kernels
+
+
+def _source_hash():
+    h = hashlib.sha256()
+    for name in ("gemm_bf16.hip", "common.h"):
+        with open(os.path.join(ROOT, "tensor_transformer_mlp_shard_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, launches):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        data = json.load(fh)
+    ent = data.get("kernels", {}).get(kernel)
+    if not ent or data.get("source_hash") != _source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(shard, frac_tokens=1):
+    """The fp64 oracle timed on 1/frac_tokens of each part's tokens (same
+    weights, same formulas) on this host."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    f64 = lambda t: t.to(dtype=shard.torch.float64).numpy()  # noqa: E731
+    m, a = shard.host_mlp, shard.host_attn
+    Tm = shard.wm.T // frac_tokens
+    Ta = shard.wa.T // frac_tokens
+    X, A, b1, B, dY = f64(m["X"][:Tm]), f64(m["A"]), f64(m["b1"]), f64(m["B"]), f64(m["dY"][:Tm])
+    Xa, Wq, bq, O, Wo, dQ, dYa = (f64(a["X"][:Ta]), f64(a["W_qkv"]), f64(a["b_qkv"]), f64(a["O"][:Ta]),
+                                 f64(a["W_o"]), f64(a["dQKV"][:Ta]), f64(a["dY"][:Ta]))
+    t0 = time.perf_counter()
+    oracle.mlp_shard_fwd(X, A, b1, B)
+    r = oracle.mlp_shard_bwd(X, A, b1, B, dY)
+    oracle.bias_grad(dY)
+    oracle.column_linear_fwd(Xa, Wq, bq)
+    oracle.linear_bwd(Xa, Wq, dQ)
+    oracle.row_linear_fwd(O, Wo)
+    oracle.linear_bwd(O, Wo, dYa)
+    dt = time.perf_counter() - t0
+    del r
+    flops = _flops_mlp(Tm, shard.wm.h, shard.wm.f) + _flops_attn(Ta, shard.wa.h, shard.wa.F // shard.wa.tp,
+                                                                 shard.wa.h // shard.wa.tp)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, one step on 1/{frac_tokens} of the tokens "
+                      f"(MLP T={Tm}, attention T={Ta}; full weights): {flops:.3e} FLOP in {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-frac", type=int, default=1, help="oracle sample = 1/N of the tokens")
+    ap.add_argument("--part", choices=["all", "mlp", "attn"], default="all",
+                    help="run only one part (for profiling runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's shard; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path: run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from tensor_transformer_mlp_shard_amd import _native
+
+    if not os.path.exists(_native.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    device = torch.device("cuda:0")
+    shard = Shard(device)
+    fn = {"all": shard.step, "mlp": shard.mlp_step, "attn": shard.attn_step}[args.part]
+    flops = {"all": shard.flops_mlp + shard.flops_attn, "mlp": shard.flops_mlp, "attn": shard.flops_attn}[args.part]
+
+    ms, wall_ms = time_steps(torch, fn, args.steps, args.warmup)
+    value = flops / (ms * 1e-3) / 1e12
+    parts = {}
+    if args.part == "all":
+        for name, f_, fl in (("mlp", shard.mlp_step, shard.flops_mlp), ("attn", shard.attn_step, shard.flops_attn)):
+            pms, _ = time_steps(torch, f_, args.steps, 2)
+            parts[name] = {"ms": round(pms, 4), "tflops": round(fl / (pms * 1e-3) / 1e12, 1),
+                           "pct_peak": round(100 * fl / (pms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2)}
+
+    dom, kernels = roofline_from_trace(shard.tps, torch, fn, args.steps)
+    avg_ms = dom["total_ms"] / dom["launches"]
+    if dom["flops"] > 0:
+        achieved = dom["flops"] / dom["launches"] / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+    else:
+        achieved = dom["bytes"] / dom["launches"] / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = traffic_for(dom["name"], dom["launches"])
+    roof["kernel"] = dom["name"]
+    roof["launches_per_step"] = dom["launches"] // args.steps
+    roof["avg_launch_ms"] = round(avg_ms, 5)
+    kern = [{"name": k["name"], "launches_per_step": k["launches"] // args.steps,
+             "ms_per_step": round(k["total_ms"] / args.steps, 4),
+             "tflops": round(k["flops"] / (k["total_ms"] * 1e-3) / 1e12, 1) if k["flops"] else None,
+             "gbs": round(k["bytes"] / (k["total_ms"] * 1e-3) / 1e9, 1)} for k in kernels]
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normals, random-init weights)",
+        "config": {
+            "workload": ("175B-shaped TP=8 layer shard, one rank: MLP T=2048 h=12288 f=6144 fwd+bwd "
+                         "+ attention linears T=8192 QKV 12288->4608 (bias) and out-proj 1536->12288 fwd+bwd"
+                         if args.part == "all" else f"part={args.part}"),
+            "tp": 8,
+            "flop_per_step": flops,
+        },
+        "pct_of_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
+        "wall_ms_per_step": round(wall_ms, 4),
+        "parts": parts,
+        "roofline": roof,
+        "kernels": kern,
+    }
+    if not args.no_cpu_baseline and args.part == "all":
+        out["cpu_baseline"] = cpu_baseline(shard, args.cpu_frac)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

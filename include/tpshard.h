@@ -1,0 +1,223 @@
+/*
+ * tpshard.h — C ABI of libtpshard.so: one rank's share of a tensor-parallel
+ * Transformer block on one AMD Instinct MI355X (gfx950).
+ *
+ * The operations are those of the tensor-parallel split described on the
+ * freeguideonline tutorial "Megatron-LM：NVIDIA 的大规模并行训练方案", section
+ * "Megatron-LM 核心架构 / 张量并行原理", and on "分布式训练基础：数据并行、模型
+ * 并行、流水线并行的基本概念与区别", section 2.2 ("核心原理"):
+ *   - a column-parallel linear Y = XA with A = [A_1, ..., A_p] split by columns:
+ *     rank i computes Y_i = X A_i from the replicated input X;
+ *   - a row-parallel linear with A split by rows and X by columns: rank i
+ *     computes the partial X_i A_i that an AllReduce would sum;
+ *   - in a Transformer, QKV and the MLP's first layer are column-parallel, the
+ *     attention output projection and the MLP's second layer row-parallel, and
+ *     (tutorial, section "融合优化技术") the bias add and GeLU are fused into
+ *     the producing kernel instead of making extra memory round-trips.
+ * The backward entry points are the chain rule of these products (the pages
+ * say only that tensor parallelism communicates in every layer's forward and
+ * backward; the library stops at the per-rank partials, before any sum).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.  All matrices are dense, row-major, leading dimension = number of
+ *   columns.  Activations are [T x features] with T = tokens (micro-batch x
+ *   sequence flattened).  Weights are [in x out] (Y = X W).  Rank i owns the
+ *   contiguous column block i (column-parallel) or row block i (row-parallel);
+ *   callers pass the shard itself, already sliced and contiguous.
+ * Dimensions.  K = full in-features, N = full out-features, p = tp_size >= 1.
+ *   The shard width is N/p (column) or K/p (row) and must be an integer
+ *   (TP_ERR_TP_DIVISIBILITY).  T >= 1 is arbitrary; every feature dimension
+ *   (K, N, and their shard widths) must be a positive multiple of 8
+ *   (TP_ERR_ALIGNMENT), and every dimension must be <= 2^30 (TP_ERR_DIM).
+ * Dtypes.  dtype = TP_BF16: activations, weights, biases and activation
+ *   outputs are bfloat16; products accumulate in fp32 on the matrix cores
+ *   and are rounded to nearest-even on store.  dtype = TP_FP32: everything is
+ *   fp32 with fp32 arithmetic (a check path).  Parameter gradients (dW, db)
+ *   are always fp32, for both dtypes.
+ * Pointers.  Device pointers (hipMalloc / torch CUDA tensors), 16-byte aligned
+ *   (TP_ERR_ALIGNMENT).  Required pointers must be non-NULL (TP_ERR_NULLPTR).
+ *   No output may overlap any input or another output (TP_ERR_ALIAS).
+ * Ownership.  The caller owns every buffer.  The library never allocates,
+ *   frees or retains device memory; scratch comes only from `workspace`,
+ *   whose size is given by tp_workspace_size().
+ * Streams.  `stream` is a hipStream_t (NULL = the legacy default stream).
+ *   Every call only enqueues work on it and returns; the caller synchronises.
+ *   Calls that share a workspace must be ordered on one stream.
+ * Errors.  Returns TP_OK (0) or a negative status (tp_status_string gives the
+ *   text).  All argument checks run before anything is enqueued: on a
+ *   validation error nothing is launched and no output is touched.  A failed
+ *   launch returns TP_ERR_HIP.  No C++ exception or abort crosses the ABI.
+ * Determinism.  No floating-point atomics: equal inputs give bitwise equal
+ *   outputs on every run.
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { TP_BF16 = 0, TP_FP32 = 1 } tp_dtype;
+typedef enum { TP_ACT_NONE = 0, TP_ACT_GELU = 1 } tp_act;
+
+enum {
+  TP_OK = 0,
+  TP_ERR_NULLPTR = -1,          /* a required pointer is NULL */
+  TP_ERR_DIM = -2,              /* a dimension is < 1 or > 2^30 */
+  TP_ERR_TP_DIVISIBILITY = -3,  /* tp_size < 1 or the sharded dimension not divisible by it */
+  TP_ERR_ALIGNMENT = -4,        /* pointer not 16-byte aligned or feature dim not a multiple of 8 */
+  TP_ERR_DTYPE = -5,            /* unknown dtype or activation code */
+  TP_ERR_ALIAS = -6,            /* an output overlaps an input or another output */
+  TP_ERR_WORKSPACE = -7,        /* workspace NULL or smaller than tp_workspace_size() */
+  TP_ERR_HIP = -8,              /* a HIP runtime call or kernel launch failed */
+  TP_ERR_ARG = -9               /* other invalid argument (flag value, unexpected pointer) */
+};
+
+/* Operation codes for tp_workspace_size(). */
+enum {
+  TP_OP_COLUMN_LINEAR_BWD = 1,
+  TP_OP_ROW_LINEAR_BWD = 2,
+  TP_OP_MLP_SHARD_BWD = 3,
+  TP_OP_BIAS_GRAD = 4
+};
+
+/*
+ * Column-parallel linear, forward (tutorial "张量并行原理": Y_i = X A_i).
+ *   X   [T x K]     replicated input
+ *   W_i [K x N/p]   this rank's column block of W
+ *   b_i [N/p]       this rank's bias block, or NULL
+ *   act TP_ACT_NONE: Y_i = X W_i + b_i; Z_i must be NULL.
+ *       TP_ACT_GELU: Z_i = X W_i + b_i (stored only if Z_i != NULL) and
+ *                    Y_i = GeLU(Z_i) = Z_i * Phi(Z_i) (exact erf form), both
+ *                    computed from the fp32 accumulators in one kernel.
+ *   Y_i, Z_i [T x N/p], dtype.
+ */
+int tp_column_linear(const void* X, const void* W_i, const void* b_i, void* Y_i, void* Z_i,
+                     int64_t T, int64_t K, int64_t N, int32_t tp_size, int32_t act, int32_t dtype,
+                     void* stream);
+
+/*
+ * Row-parallel linear, forward (tutorial "张量并行原理": A split by rows, X by
+ * columns; the partials are summed by an AllReduce outside this library).
+ *   X_i [T x K/p]   this rank's column block of the input
+ *   W_i [K/p x N]   this rank's row block of W
+ *   b   [N]         output bias or NULL; pass it on exactly one rank, since the
+ *                   partials are summed afterwards
+ *   Y_i [T x N]     partial output X_i W_i (+ b), dtype
+ */
+int tp_row_linear(const void* X_i, const void* W_i, const void* b, void* Y_i,
+                  int64_t T, int64_t K, int64_t N, int32_t tp_size, int32_t dtype, void* stream);
+
+/*
+ * MLP shard, forward: the first layer column-parallel, then the fused bias +
+ * GeLU, then the second layer row-parallel (tutorial "张量并行原理", last
+ * paragraph, and "融合优化技术").  With f = F/p:
+ *   X    [T x h]  replicated input        A_i [h x f]   B_i [f x h]
+ *   b1_i [f] or NULL
+ *   Z_i  [T x f]  = X A_i + b1_i, saved for the backward; NULL = inference
+ *   H_i  [T x f]  = GeLU(Z_i)  (written once, already activated)
+ *   Y_i  [T x h]  = H_i B_i, the rank's partial (no output bias; it is added
+ *                   once after the row-parallel sum)
+ */
+int tp_mlp_shard_fwd(const void* X, const void* A_i, const void* b1_i, const void* B_i,
+                     void* Z_i, void* H_i, void* Y_i,
+                     int64_t T, int64_t h, int64_t F, int32_t tp_size, int32_t dtype, void* stream);
+
+/*
+ * MLP shard, backward.  Inputs are the forward's X, A_i, B_i and the saved
+ * Z_i, H_i, plus dY [T x h] = dL/dY (gradient of the summed output).
+ *   dB_i  [f x h] fp32 = H_i^T dY
+ *   dZ            = (dY B_i^T) * GeLU'(Z_i), GeLU'(z) = Phi(z) + z phi(z)
+ *                   (kept in the workspace, dtype)
+ *   db1_i [f]     fp32 = sum over tokens of dZ, or NULL to skip
+ *   dA_i  [h x f] fp32 = X^T dZ
+ *   dX_i  [T x h] dtype = dZ A_i^T (this rank's partial of dX)
+ *   db2   [h]     fp32 = sum over tokens of dY (gradient of the row-parallel
+ *                   output bias; compute it on one rank), or NULL to skip
+ *   accumulate 0: overwrite dA_i, dB_i, db1_i, db2; 1: add to them.
+ *   workspace: >= tp_workspace_size(TP_OP_MLP_SHARD_BWD, T, h, F, p, dtype) bytes.
+ */
+int tp_mlp_shard_bwd(const void* X, const void* A_i, const void* B_i, const void* Z_i,
+                     const void* H_i, const void* dY, void* dX_i, float* dA_i, float* db1_i,
+                     float* dB_i, float* db2, void* workspace, size_t workspace_bytes,
+                     int32_t accumulate, int64_t T, int64_t h, int64_t F, int32_t tp_size,
+                     int32_t dtype, void* stream);
+
+/*
+ * Column-parallel linear, backward (no activation; for the GeLU layer use
+ * tp_mlp_shard_bwd).  X [T x K], W_i [K x N/p], dY_i [T x N/p]:
+ *   dX_partial [T x K]   dtype = dY_i W_i^T (summed over ranks outside)
+ *   dW_i       [K x N/p] fp32  = X^T dY_i
+ *   db_i       [N/p]     fp32  = sum over tokens of dY_i, or NULL
+ *   accumulate as in tp_mlp_shard_bwd.  workspace: TP_OP_COLUMN_LINEAR_BWD.
+ */
+int tp_column_linear_bwd(const void* X, const void* W_i, const void* dY_i, void* dX_partial,
+                         float* dW_i, float* db_i, void* workspace, size_t workspace_bytes,
+                         int32_t accumulate, int64_t T, int64_t K, int64_t N, int32_t tp_size,
+                         int32_t dtype, void* stream);
+
+/*
+ * Row-parallel linear, backward.  X_i [T x K/p], W_i [K/p x N], dY [T x N]:
+ *   dX_i [T x K/p] dtype = dY W_i^T (exact gradient of this rank's input block)
+ *   dW_i [K/p x N] fp32  = X_i^T dY
+ *   db   [N]       fp32  = sum over tokens of dY, or NULL (one rank only)
+ *   accumulate as above.  workspace: TP_OP_ROW_LINEAR_BWD.
+ */
+int tp_row_linear_bwd(const void* X_i, const void* W_i, const void* dY, void* dX_i,
+                      float* dW_i, float* db, void* workspace, size_t workspace_bytes,
+                      int32_t accumulate, int64_t T, int64_t K, int64_t N, int32_t tp_size,
+                      int32_t dtype, void* stream);
+
+/*
+ * Bias gradient alone: db [N] fp32 (=, or += with accumulate) sum over the T
+ * rows of dY [T x N] (dtype).  workspace: TP_OP_BIAS_GRAD with d_in = N.
+ */
+int tp_bias_grad(const void* dY, float* db, void* workspace, size_t workspace_bytes,
+                 int32_t accumulate, int64_t T, int64_t N, int32_t dtype, void* stream);
+
+/*
+ * The bias + GeLU step as a separate elementwise pass (the unfused form that
+ * the fused epilogue replaces; kept for measurement):
+ *   H [T x N] = GeLU(Z + b), Z [T x N], b [N] (or NULL), dtype.
+ */
+int tp_bias_gelu(const void* Z, const void* b, void* H, int64_t T, int64_t N, int32_t dtype,
+                 void* stream);
+
+/*
+ * Workspace bytes needed by `op` (TP_OP_*).  Arguments are those of the
+ * matching call: T, d_in, d_out = (T, K, N) for the linears, (T, h, F) for the
+ * MLP, (T, N, unused) for the bias gradient.  Returns 0 for invalid arguments.
+ */
+size_t tp_workspace_size(int32_t op, int64_t T, int64_t d_in, int64_t d_out, int32_t tp_size,
+                         int32_t dtype);
+
+/* Static, NUL-terminated text for a status code. */
+const char* tp_status_string(int status);
+
+/*
+ * Kernel timing trace (measurement aid).  While a trace is open, every kernel
+ * the library launches is bracketed by a pair of hipEvents recorded on the
+ * stream it is launched on, together with its algorithmic FLOP and HBM byte
+ * counts.  tp_trace_start(max_launches) opens a trace with room for that many
+ * launches (events are created here; launches past the limit are not
+ * recorded); tp_trace_stop() waits for the recorded events and aggregates
+ * them per kernel name.  Not thread-safe: one host thread drives a trace.
+ */
+int tp_trace_start(int32_t max_launches);
+int tp_trace_stop(void);
+/* Number of distinct kernels in the last stopped trace. */
+int tp_trace_num_kernels(void);
+/* Kernel `idx` of the last stopped trace: name (truncated to name_len-1),
+ * number of launches, summed duration (ms), summed algorithmic FLOP and bytes. */
+int tp_trace_kernel(int32_t idx, char* name, size_t name_len, int64_t* launches,
+                    double* total_ms, double* flops, double* bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPSHARD_H */

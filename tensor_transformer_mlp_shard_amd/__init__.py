@@ -1,1 +1,280 @@
-"""MI355X-native tensor-parallel Transformer shard (placeholder; binding follows)."""
+"""MI355X-native tensor-parallel Transformer shard: Python binding of libtpshard.so.
+
+Each function marshals torch CUDA tensors (device memory and the current HIP
+stream) into one call of the C ABI declared in include/tpshard.h; every step of
+the computation runs in the library's HIP kernels.  Outputs are allocated with
+``torch.empty`` on the inputs' device.  There is no fallback: without the built
+library every call raises.
+
+Shapes (rank i of a TP group of size p; weights are [in x out]):
+  column_linear   X[T x K], W_i[K x N/p]           -> Y_i[T x N/p]
+  row_linear      X_i[T x K/p], W_i[K/p x N]       -> Y_i[T x N] (partial)
+  mlp_shard_fwd   X[T x h], A_i[h x f], B_i[f x h] -> Z_i, H_i [T x f], Y_i[T x h]
+  *_bwd           the matching gradients; parameter gradients are fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _native
+from ._native import NativeLibraryMissing  # noqa: F401
+
+__all__ = [
+    "column_linear", "row_linear", "mlp_shard_fwd", "mlp_shard_bwd", "column_linear_bwd",
+    "row_linear_bwd", "bias_grad", "bias_gelu", "workspace_size", "trace_start", "trace_stop",
+    "library_path", "NativeLibraryMissing",
+]
+
+_DT = {torch.bfloat16: _native.TP_BF16, torch.float32: _native.TP_FP32}
+
+
+def library_path() -> str:
+    _native.lib()
+    return _native.LIB_PATH
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+    return _DT[t.dtype]
+
+
+def _check(name, t, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace_size(op: int, T: int, d_in: int, d_out: int, tp_size: int, dtype: torch.dtype) -> int:
+    return int(_native.lib().tp_workspace_size(op, T, d_in, d_out, tp_size, _DT[dtype]))
+
+
+def _workspace(op, T, d_in, d_out, tp_size, dtype, device, given):
+    need = workspace_size(op, T, d_in, d_out, tp_size, dtype)
+    if given is not None:
+        if given.device != device or given.numel() * given.element_size() < need:
+            raise ValueError(f"workspace needs {need} bytes on {device}")
+        return given
+    return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+
+
+def column_linear(x, w_i, b_i=None, *, tp_size: int, act: str = "none", save_z: bool = False):
+    """Column-parallel linear (rank's shard).  Returns Y_i, or (Y_i, Z_i) when
+    act == "gelu" and save_z."""
+    T, K = x.shape
+    n = w_i.shape[1]
+    dt = x.dtype
+    _check("x", x, (T, K), dt, x.device)
+    _check("w_i", w_i, (K, n), dt, x.device)
+    if b_i is not None:
+        _check("b_i", b_i, (n,), dt, x.device)
+    if act not in ("none", "gelu"):
+        raise ValueError("act must be 'none' or 'gelu'")
+    if save_z and act != "gelu":
+        raise ValueError("save_z needs act='gelu'")
+    y = torch.empty((T, n), dtype=dt, device=x.device)
+    z = torch.empty((T, n), dtype=dt, device=x.device) if save_z else None
+    st = _native.lib().tp_column_linear(
+        _ptr(x), _ptr(w_i), _ptr(b_i), _ptr(y), _ptr(z), T, K, n * tp_size, tp_size,
+        _native.TP_ACT_GELU if act == "gelu" else _native.TP_ACT_NONE, _dtype_code(x), _stream(x.device))
+    _native.check(st, "tp_column_linear")
+    return (y, z) if save_z else y
+
+
+def row_linear(x_i, w_i, b=None, *, tp_size: int):
+    """Row-parallel linear: the rank's partial X_i W_i (+ b)."""
+    T, k = x_i.shape
+    N = w_i.shape[1]
+    dt = x_i.dtype
+    _check("x_i", x_i, (T, k), dt, x_i.device)
+    _check("w_i", w_i, (k, N), dt, x_i.device)
+    if b is not None:
+        _check("b", b, (N,), dt, x_i.device)
+    y = torch.empty((T, N), dtype=dt, device=x_i.device)
+    st = _native.lib().tp_row_linear(_ptr(x_i), _ptr(w_i), _ptr(b), _ptr(y), T, k * tp_size, N, tp_size,
+                                     _dtype_code(x_i), _stream(x_i.device))
+    _native.check(st, "tp_row_linear")
+    return y
+
+
+def mlp_shard_fwd(x, a_i, b1_i, b_i, *, tp_size: int, save_z: bool = True, out=None):
+    """MLP shard forward.  Returns (Z_i or None, H_i, Y_i).  ``out`` may hold
+    preallocated "Z", "H", "Y" tensors."""
+    T, h = x.shape
+    f = a_i.shape[1]
+    dt = x.dtype
+    dev = x.device
+    _check("x", x, (T, h), dt, dev)
+    _check("a_i", a_i, (h, f), dt, dev)
+    _check("b_i", b_i, (f, h), dt, dev)
+    if b1_i is not None:
+        _check("b1_i", b1_i, (f,), dt, dev)
+    out = out or {}
+    z = out.get("Z") if save_z else None
+    if save_z and z is None:
+        z = torch.empty((T, f), dtype=dt, device=dev)
+    hh = out.get("H")
+    if hh is None:
+        hh = torch.empty((T, f), dtype=dt, device=dev)
+    y = out.get("Y")
+    if y is None:
+        y = torch.empty((T, h), dtype=dt, device=dev)
+    st = _native.lib().tp_mlp_shard_fwd(_ptr(x), _ptr(a_i), _ptr(b1_i), _ptr(b_i), _ptr(z), _ptr(hh), _ptr(y),
+                                        T, h, f * tp_size, tp_size, _dtype_code(x), _stream(dev))
+    _native.check(st, "tp_mlp_shard_fwd")
+    return z, hh, y
+
+
+def mlp_shard_bwd(x, a_i, b_i, z_i, h_i, dy, *, tp_size: int, want_db1: bool = True, want_db2: bool = False,
+                  accumulate: bool = False, out=None, workspace=None):
+    """MLP shard backward.  Returns dict(dX, dA, db1, dB, db2) (db1 / db2 None
+    unless wanted).  With ``accumulate`` the fp32 parameter gradients in ``out``
+    ("dA", "dB", "db1", "db2") are added to instead of overwritten."""
+    T, h = x.shape
+    f = a_i.shape[1]
+    dt = x.dtype
+    dev = x.device
+    for name, t, shp in (("x", x, (T, h)), ("a_i", a_i, (h, f)), ("b_i", b_i, (f, h)), ("z_i", z_i, (T, f)),
+                         ("h_i", h_i, (T, f)), ("dy", dy, (T, h))):
+        _check(name, t, shp, dt, dev)
+    out = dict(out or {})
+    if accumulate:
+        for k in ("dA", "dB") + (("db1",) if want_db1 else ()) + (("db2",) if want_db2 else ()):
+            if out.get(k) is None:
+                raise ValueError(f"accumulate needs out[{k!r}]")
+
+    def get(k, shape, dtype):
+        t = out.get(k)
+        if t is None:
+            return torch.empty(shape, dtype=dtype, device=dev)
+        _check(f"out[{k}]", t, shape, dtype, dev)
+        return t
+
+    dX = get("dX", (T, h), dt)
+    dA = get("dA", (h, f), torch.float32)
+    dB = get("dB", (f, h), torch.float32)
+    db1 = get("db1", (f,), torch.float32) if want_db1 else None
+    db2 = get("db2", (h,), torch.float32) if want_db2 else None
+    ws = _workspace(_native.TP_OP_MLP_SHARD_BWD, T, h, f * tp_size, tp_size, dt, dev, workspace)
+    st = _native.lib().tp_mlp_shard_bwd(
+        _ptr(x), _ptr(a_i), _ptr(b_i), _ptr(z_i), _ptr(h_i), _ptr(dy), _ptr(dX), _ptr(dA), _ptr(db1), _ptr(dB),
+        _ptr(db2), _ptr(ws), ws.numel(), int(accumulate), T, h, f * tp_size, tp_size, _dtype_code(x), _stream(dev))
+    _native.check(st, "tp_mlp_shard_bwd")
+    return {"dX": dX, "dA": dA, "db1": db1, "dB": dB, "db2": db2}
+
+
+def _linear_bwd(fn_name, op, x, w, dy, T, K, N, tp_size, dx_shape, want_db, accumulate, out, workspace):
+    dev = x.device
+    dt = x.dtype
+    out = dict(out or {})
+    if accumulate:
+        for k in ("dW",) + (("db",) if want_db else ()):
+            if out.get(k) is None:
+                raise ValueError(f"accumulate needs out[{k!r}]")
+
+    def get(k, shape, dtype):
+        t = out.get(k)
+        if t is None:
+            return torch.empty(shape, dtype=dtype, device=dev)
+        _check(f"out[{k}]", t, shape, dtype, dev)
+        return t
+
+    dX = get("dX", dx_shape, dt)
+    dW = get("dW", tuple(w.shape), torch.float32)
+    db = get("db", (dy.shape[1],), torch.float32) if want_db else None
+    ws = _workspace(op, T, K, N, tp_size, dt, dev, workspace) if want_db else None
+    fn = getattr(_native.lib(), fn_name)
+    st = fn(_ptr(x), _ptr(w), _ptr(dy), _ptr(dX), _ptr(dW), _ptr(db), _ptr(ws), 0 if ws is None else ws.numel(),
+            int(accumulate), T, K, N, tp_size, _dtype_code(x), _stream(dev))
+    _native.check(st, fn_name)
+    return {"dX": dX, "dW": dW, "db": db}
+
+
+def column_linear_bwd(x, w_i, dy_i, *, tp_size: int, want_db: bool = True, accumulate: bool = False, out=None,
+                      workspace=None):
+    """Column-parallel linear backward: dict(dX (partial), dW, db)."""
+    T, K = x.shape
+    n = w_i.shape[1]
+    dt = x.dtype
+    _check("x", x, (T, K), dt, x.device)
+    _check("w_i", w_i, (K, n), dt, x.device)
+    _check("dy_i", dy_i, (T, n), dt, x.device)
+    return _linear_bwd("tp_column_linear_bwd", _native.TP_OP_COLUMN_LINEAR_BWD, x, w_i, dy_i, T, K, n * tp_size,
+                       tp_size, (T, K), want_db, accumulate, out, workspace)
+
+
+def row_linear_bwd(x_i, w_i, dy, *, tp_size: int, want_db: bool = True, accumulate: bool = False, out=None,
+                   workspace=None):
+    """Row-parallel linear backward: dict(dX (this rank's input block), dW, db)."""
+    T, k = x_i.shape
+    N = w_i.shape[1]
+    dt = x_i.dtype
+    _check("x_i", x_i, (T, k), dt, x_i.device)
+    _check("w_i", w_i, (k, N), dt, x_i.device)
+    _check("dy", dy, (T, N), dt, x_i.device)
+    return _linear_bwd("tp_row_linear_bwd", _native.TP_OP_ROW_LINEAR_BWD, x_i, w_i, dy, T, k * tp_size, N,
+                       tp_size, (T, k), want_db, accumulate, out, workspace)
+
+
+def bias_grad(dy, *, accumulate_into=None, workspace=None):
+    """Sum over tokens of dy [T x N] -> fp32 [N]."""
+    T, N = dy.shape
+    dev = dy.device
+    _check("dy", dy, (T, N), dy.dtype, dev)
+    db = accumulate_into if accumulate_into is not None else torch.empty((N,), dtype=torch.float32, device=dev)
+    ws = _workspace(_native.TP_OP_BIAS_GRAD, T, N, 0, 1, dy.dtype, dev, workspace)
+    st = _native.lib().tp_bias_grad(_ptr(dy), _ptr(db), _ptr(ws), ws.numel(), int(accumulate_into is not None),
+                                    T, N, _dtype_code(dy), _stream(dev))
+    _native.check(st, "tp_bias_grad")
+    return db
+
+
+def bias_gelu(z, b=None):
+    """Unfused H = GeLU(Z + b)."""
+    T, N = z.shape
+    _check("z", z, (T, N), z.dtype, z.device)
+    if b is not None:
+        _check("b", b, (N,), z.dtype, z.device)
+    hh = torch.empty_like(z)
+    st = _native.lib().tp_bias_gelu(_ptr(z), _ptr(b), _ptr(hh), T, N, _dtype_code(z), _stream(z.device))
+    _native.check(st, "tp_bias_gelu")
+    return hh
+
+
+def trace_start(max_launches: int = 4096) -> None:
+    _native.check(_native.lib().tp_trace_start(max_launches), "tp_trace_start")
+
+
+def trace_stop():
+    """Stop the trace; returns a list of dicts(name, launches, total_ms, flops, bytes)."""
+    L = _native.lib()
+    _native.check(L.tp_trace_stop(), "tp_trace_stop")
+    out = []
+    buf = ctypes.create_string_buffer(256)
+    for i in range(L.tp_trace_num_kernels()):
+        n = ctypes.c_int64()
+        ms, fl, by = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+        _native.check(L.tp_trace_kernel(i, buf, 256, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(fl),
+                                        ctypes.byref(by)), "tp_trace_kernel")
+        out.append({"name": buf.value.decode(), "launches": n.value, "total_ms": ms.value, "flops": fl.value,
+                    "bytes": by.value})
+    return out

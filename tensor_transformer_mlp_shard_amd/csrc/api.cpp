@@ -1,0 +1,474 @@
+// C ABI of libtpshard.so: argument validation, workspace sizing, launch
+// sequencing on the caller's stream, and the optional kernel-timing trace.
+// The operations and their sources are documented in include/tpshard.h.
+#include "tpshard.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace tps {
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kMaxElems = int64_t(1) << 36;
+constexpr size_t kAlign = 256;  // workspace sub-buffer alignment
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t elsize(int32_t dtype) { return dtype == TP_FP32 ? 4 : 2; }
+
+// A device buffer an entry point reads or writes, for the overlap check.
+struct Buf {
+  const void* p;
+  size_t bytes;
+  Buf(const void* p_, int64_t b) : p(p_), bytes((size_t)b) {}
+};
+
+bool overlap(const Buf& a, const Buf& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + a.bytes;
+  const uintptr_t b0 = (uintptr_t)b.p, b1 = b0 + b.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+int check_dims(std::initializer_list<int64_t> dims) {
+  for (int64_t d : dims)
+    if (d < 1 || d > kMaxDim) return TP_ERR_DIM;
+  return TP_OK;
+}
+
+int check_elems(std::initializer_list<std::pair<int64_t, int64_t>> mats) {
+  for (const auto& m : mats)
+    if (m.first * m.second > kMaxElems) return TP_ERR_DIM;
+  return TP_OK;
+}
+
+int check_feature(std::initializer_list<int64_t> dims) {
+  for (int64_t d : dims)
+    if (d % 8 != 0) return TP_ERR_ALIGNMENT;
+  return TP_OK;
+}
+
+int check_ptrs_aligned(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (p && ((uintptr_t)p % 16) != 0) return TP_ERR_ALIGNMENT;
+  return TP_OK;
+}
+
+int check_nonnull(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (!p) return TP_ERR_NULLPTR;
+  return TP_OK;
+}
+
+// No output may overlap an input or another output.
+int check_alias(const std::vector<Buf>& ins, const std::vector<Buf>& outs) {
+  for (size_t i = 0; i < outs.size(); ++i) {
+    for (const Buf& in : ins)
+      if (overlap(outs[i], in)) return TP_ERR_ALIAS;
+    for (size_t j = i + 1; j < outs.size(); ++j)
+      if (overlap(outs[i], outs[j])) return TP_ERR_ALIAS;
+  }
+  return TP_OK;
+}
+
+int check_dtype(int32_t dtype) { return (dtype == TP_BF16 || dtype == TP_FP32) ? TP_OK : TP_ERR_DTYPE; }
+
+#define TP_TRY(expr)              \
+  do {                            \
+    const int _st = (expr);       \
+    if (_st != TP_OK) return _st; \
+  } while (0)
+
+#define HIP_TRY(expr)                              \
+  do {                                             \
+    if ((expr) != hipSuccess) return TP_ERR_HIP;   \
+  } while (0)
+
+hipError_t gemm(int32_t dtype, const GemmArgs& g, bool ak, bool bk, Epi epi, hipStream_t s) {
+  return dtype == TP_FP32 ? gemm_f32(g, ak, bk, epi, s) : gemm_bf16(g, ak, bk, epi, s);
+}
+
+GemmArgs make_args(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N, int64_t K,
+                   void* C, int64_t ldc) {
+  GemmArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.A = A;
+  g.B = B;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.C = C;
+  g.ldc = ldc;
+  return g;
+}
+
+size_t colsum_ws_bytes(int64_t T, int64_t N) { return round_up((size_t)colsum_chunks(T, N) * (size_t)N * 4); }
+
+// ---------------------------------------------------------------- trace
+struct TraceAgg {
+  std::string name;
+  int64_t launches = 0;
+  double ms = 0, flops = 0, bytes = 0;
+};
+
+struct Trace {
+  std::mutex mu;
+  bool on = false;
+  int max = 0;
+  int n = 0;
+  std::vector<hipEvent_t> ev;
+  std::vector<LaunchInfo> info;
+  std::vector<TraceAgg> result;
+};
+
+Trace& trace() {
+  static Trace t;
+  return t;
+}
+
+}  // namespace
+
+void trace_begin(hipStream_t stream) {
+  Trace& t = trace();
+  if (t.on && t.n < t.max) (void)hipEventRecord(t.ev[2 * t.n], stream);
+}
+
+void trace_end(hipStream_t stream, const LaunchInfo& info) {
+  Trace& t = trace();
+  if (t.on && t.n < t.max) {
+    (void)hipEventRecord(t.ev[2 * t.n + 1], stream);
+    t.info[t.n] = info;
+    ++t.n;
+  }
+}
+
+}  // namespace tps
+
+using namespace tps;
+
+extern "C" {
+
+const char* tp_status_string(int status) {
+  switch (status) {
+    case TP_OK: return "ok";
+    case TP_ERR_NULLPTR: return "a required pointer is NULL";
+    case TP_ERR_DIM: return "a dimension is < 1 or too large";
+    case TP_ERR_TP_DIVISIBILITY: return "tp_size < 1 or the sharded dimension is not divisible by tp_size";
+    case TP_ERR_ALIGNMENT: return "pointer not 16-byte aligned or feature dimension not a multiple of 8";
+    case TP_ERR_DTYPE: return "unknown dtype or activation";
+    case TP_ERR_ALIAS: return "an output overlaps an input or another output";
+    case TP_ERR_WORKSPACE: return "workspace missing or too small";
+    case TP_ERR_HIP: return "HIP runtime or kernel launch error";
+    case TP_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+size_t tp_workspace_size(int32_t op, int64_t T, int64_t d_in, int64_t d_out, int32_t tp_size, int32_t dtype) {
+  if (check_dtype(dtype) != TP_OK || T < 1 || T > kMaxDim) return 0;
+  switch (op) {
+    case TP_OP_BIAS_GRAD:
+      if (d_in < 1 || d_in > kMaxDim) return 0;
+      return colsum_ws_bytes(T, d_in);
+    case TP_OP_COLUMN_LINEAR_BWD:
+      if (tp_size < 1 || d_out < 1 || d_out > kMaxDim || d_out % tp_size) return 0;
+      return colsum_ws_bytes(T, d_out / tp_size);
+    case TP_OP_ROW_LINEAR_BWD:
+      if (d_out < 1 || d_out > kMaxDim) return 0;
+      return colsum_ws_bytes(T, d_out);
+    case TP_OP_MLP_SHARD_BWD: {
+      if (tp_size < 1 || d_in < 1 || d_out < 1 || d_in > kMaxDim || d_out > kMaxDim || d_out % tp_size) return 0;
+      const int64_t f = d_out / tp_size;
+      const size_t dz = round_up((size_t)T * (size_t)f * elsize(dtype));
+      const size_t cs = colsum_ws_bytes(T, f) > colsum_ws_bytes(T, d_in) ? colsum_ws_bytes(T, f)
+                                                                          : colsum_ws_bytes(T, d_in);
+      return dz + cs;
+    }
+    default:
+      return 0;
+  }
+}
+
+int tp_column_linear(const void* X, const void* W_i, const void* b_i, void* Y_i, void* Z_i, int64_t T, int64_t K,
+                     int64_t N, int32_t tp_size, int32_t act, int32_t dtype, void* stream) {
+  TP_TRY(check_dtype(dtype));
+  if (act != TP_ACT_NONE && act != TP_ACT_GELU) return TP_ERR_DTYPE;
+  TP_TRY(check_nonnull({X, W_i, Y_i}));
+  if (act == TP_ACT_NONE && Z_i) return TP_ERR_ARG;
+  TP_TRY(check_dims({T, K, N}));
+  if (tp_size < 1 || N % tp_size) return TP_ERR_TP_DIVISIBILITY;
+  const int64_t n = N / tp_size;
+  TP_TRY(check_feature({K, n}));
+  TP_TRY(check_elems({{T, K}, {K, n}, {T, n}}));
+  TP_TRY(check_ptrs_aligned({X, W_i, b_i, Y_i, Z_i}));
+  const int64_t es = elsize(dtype);
+  TP_TRY(check_alias({{X, T * K * es}, {W_i, K * n * es}, {b_i, n * es}},
+                     {{Y_i, T * n * es}, {Z_i, Z_i ? T * n * es : 0}}));
+  hipStream_t s = (hipStream_t)stream;
+  GemmArgs g = make_args(X, K, W_i, n, T, n, K, Y_i, n);
+  g.bias = b_i;
+  g.C2 = Z_i;
+  g.ldc2 = n;
+  HIP_TRY(gemm(dtype, g, true, false, act == TP_ACT_GELU ? EPI_BIAS_GELU : EPI_STORE, s));
+  return TP_OK;
+}
+
+int tp_row_linear(const void* X_i, const void* W_i, const void* b, void* Y_i, int64_t T, int64_t K, int64_t N,
+                  int32_t tp_size, int32_t dtype, void* stream) {
+  TP_TRY(check_dtype(dtype));
+  TP_TRY(check_nonnull({X_i, W_i, Y_i}));
+  TP_TRY(check_dims({T, K, N}));
+  if (tp_size < 1 || K % tp_size) return TP_ERR_TP_DIVISIBILITY;
+  const int64_t k = K / tp_size;
+  TP_TRY(check_feature({k, N}));
+  TP_TRY(check_elems({{T, k}, {k, N}, {T, N}}));
+  TP_TRY(check_ptrs_aligned({X_i, W_i, b, Y_i}));
+  const int64_t es = elsize(dtype);
+  TP_TRY(check_alias({{X_i, T * k * es}, {W_i, k * N * es}, {b, N * es}}, {{Y_i, T * N * es}}));
+  GemmArgs g = make_args(X_i, k, W_i, N, T, N, k, Y_i, N);
+  g.bias = b;
+  HIP_TRY(gemm(dtype, g, true, false, EPI_STORE, (hipStream_t)stream));
+  return TP_OK;
+}
+
+int tp_mlp_shard_fwd(const void* X, const void* A_i, const void* b1_i, const void* B_i, void* Z_i, void* H_i,
+                     void* Y_i, int64_t T, int64_t h, int64_t F, int32_t tp_size, int32_t dtype, void* stream) {
+  TP_TRY(check_dtype(dtype));
+  TP_TRY(check_nonnull({X, A_i, B_i, H_i, Y_i}));
+  TP_TRY(check_dims({T, h, F}));
+  if (tp_size < 1 || F % tp_size) return TP_ERR_TP_DIVISIBILITY;
+  const int64_t f = F / tp_size;
+  TP_TRY(check_feature({h, f}));
+  TP_TRY(check_elems({{T, h}, {h, f}, {T, f}}));
+  TP_TRY(check_ptrs_aligned({X, A_i, b1_i, B_i, Z_i, H_i, Y_i}));
+  const int64_t es = elsize(dtype);
+  TP_TRY(check_alias({{X, T * h * es}, {A_i, h * f * es}, {b1_i, f * es}, {B_i, f * h * es}},
+                     {{Z_i, Z_i ? T * f * es : 0}, {H_i, T * f * es}, {Y_i, T * h * es}}));
+  hipStream_t s = (hipStream_t)stream;
+  GemmArgs g1 = make_args(X, h, A_i, f, T, f, h, H_i, f);
+  g1.bias = b1_i;
+  g1.C2 = Z_i;
+  g1.ldc2 = f;
+  HIP_TRY(gemm(dtype, g1, true, false, EPI_BIAS_GELU, s));
+  GemmArgs g2 = make_args(H_i, f, B_i, h, T, h, f, Y_i, h);
+  HIP_TRY(gemm(dtype, g2, true, false, EPI_STORE, s));
+  return TP_OK;
+}
+
+int tp_mlp_shard_bwd(const void* X, const void* A_i, const void* B_i, const void* Z_i, const void* H_i,
+                     const void* dY, void* dX_i, float* dA_i, float* db1_i, float* dB_i, float* db2,
+                     void* workspace, size_t workspace_bytes, int32_t accumulate, int64_t T, int64_t h, int64_t F,
+                     int32_t tp_size, int32_t dtype, void* stream) {
+  TP_TRY(check_dtype(dtype));
+  if (accumulate != 0 && accumulate != 1) return TP_ERR_ARG;
+  TP_TRY(check_nonnull({X, A_i, B_i, Z_i, H_i, dY, dX_i, dA_i, dB_i}));
+  TP_TRY(check_dims({T, h, F}));
+  if (tp_size < 1 || F % tp_size) return TP_ERR_TP_DIVISIBILITY;
+  const int64_t f = F / tp_size;
+  TP_TRY(check_feature({h, f}));
+  TP_TRY(check_elems({{T, h}, {h, f}, {T, f}}));
+  TP_TRY(check_ptrs_aligned({X, A_i, B_i, Z_i, H_i, dY, dX_i, dA_i, db1_i, dB_i, db2, workspace}));
+  const size_t need = tp_workspace_size(TP_OP_MLP_SHARD_BWD, T, h, F, tp_size, dtype);
+  if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
+  const int64_t es = elsize(dtype);
+  TP_TRY(check_alias({{X, T * h * es}, {A_i, h * f * es}, {B_i, f * h * es}, {Z_i, T * f * es},
+                      {H_i, T * f * es}, {dY, T * h * es}},
+                     {{dX_i, T * h * es}, {dA_i, h * f * 4}, {db1_i, db1_i ? f * 4 : 0}, {dB_i, f * h * 4},
+                      {db2, db2 ? h * 4 : 0}, {workspace, (int64_t)need}}));
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  void* dZ = ws;
+  float* part = (float*)(ws + round_up((size_t)T * (size_t)f * es));
+
+  // dZ = (dY B_i^T) * GeLU'(Z_i)          [T x f], contraction over h
+  GemmArgs g1 = make_args(dY, h, B_i, h, T, f, h, dZ, f);
+  g1.aux = Z_i;
+  g1.ldaux = f;
+  HIP_TRY(gemm(dtype, g1, true, true, EPI_DGELU, s));
+  // dB_i = H_i^T dY                       [f x h], contraction over T
+  GemmArgs g2 = make_args(H_i, f, dY, h, f, h, T, dB_i, h);
+  g2.accumulate = accumulate;
+  HIP_TRY(gemm(dtype, g2, false, false, EPI_F32, s));
+  // dA_i = X^T dZ                         [h x f], contraction over T
+  GemmArgs g3 = make_args(X, h, dZ, f, h, f, T, dA_i, f);
+  g3.accumulate = accumulate;
+  HIP_TRY(gemm(dtype, g3, false, false, EPI_F32, s));
+  // dX_i = dZ A_i^T                       [T x h], contraction over f
+  GemmArgs g4 = make_args(dZ, f, A_i, f, T, h, f, dX_i, h);
+  HIP_TRY(gemm(dtype, g4, true, true, EPI_STORE, s));
+  // db1_i = sum_t dZ, db2 = sum_t dY
+  if (db1_i) HIP_TRY(colsum(dZ, dtype == TP_BF16, db1_i, part, accumulate, T, f, s));
+  if (db2) HIP_TRY(colsum(dY, dtype == TP_BF16, db2, part, accumulate, T, h, s));
+  return TP_OK;
+}
+
+int tp_column_linear_bwd(const void* X, const void* W_i, const void* dY_i, void* dX_partial, float* dW_i,
+                         float* db_i, void* workspace, size_t workspace_bytes, int32_t accumulate, int64_t T,
+                         int64_t K, int64_t N, int32_t tp_size, int32_t dtype, void* stream) {
+  TP_TRY(check_dtype(dtype));
+  if (accumulate != 0 && accumulate != 1) return TP_ERR_ARG;
+  TP_TRY(check_nonnull({X, W_i, dY_i, dX_partial, dW_i}));
+  TP_TRY(check_dims({T, K, N}));
+  if (tp_size < 1 || N % tp_size) return TP_ERR_TP_DIVISIBILITY;
+  const int64_t n = N / tp_size;
+  TP_TRY(check_feature({K, n}));
+  TP_TRY(check_elems({{T, K}, {K, n}, {T, n}}));
+  TP_TRY(check_ptrs_aligned({X, W_i, dY_i, dX_partial, dW_i, db_i, workspace}));
+  const size_t need = db_i ? tp_workspace_size(TP_OP_COLUMN_LINEAR_BWD, T, K, N, tp_size, dtype) : 0;
+  if (db_i && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
+  const int64_t es = elsize(dtype);
+  TP_TRY(check_alias({{X, T * K * es}, {W_i, K * n * es}, {dY_i, T * n * es}},
+                     {{dX_partial, T * K * es}, {dW_i, K * n * 4}, {db_i, db_i ? n * 4 : 0},
+                      {workspace, (int64_t)need}}));
+  hipStream_t s = (hipStream_t)stream;
+  // dX = dY_i W_i^T  [T x K], contraction over n
+  GemmArgs g1 = make_args(dY_i, n, W_i, n, T, K, n, dX_partial, K);
+  HIP_TRY(gemm(dtype, g1, true, true, EPI_STORE, s));
+  // dW_i = X^T dY_i  [K x n], contraction over T
+  GemmArgs g2 = make_args(X, K, dY_i, n, K, n, T, dW_i, n);
+  g2.accumulate = accumulate;
+  HIP_TRY(gemm(dtype, g2, false, false, EPI_F32, s));
+  if (db_i) HIP_TRY(colsum(dY_i, dtype == TP_BF16, db_i, (float*)workspace, accumulate, T, n, s));
+  return TP_OK;
+}
+
+int tp_row_linear_bwd(const void* X_i, const void* W_i, const void* dY, void* dX_i, float* dW_i, float* db,
+                      void* workspace, size_t workspace_bytes, int32_t accumulate, int64_t T, int64_t K, int64_t N,
+                      int32_t tp_size, int32_t dtype, void* stream) {
+  TP_TRY(check_dtype(dtype));
+  if (accumulate != 0 && accumulate != 1) return TP_ERR_ARG;
+  TP_TRY(check_nonnull({X_i, W_i, dY, dX_i, dW_i}));
+  TP_TRY(check_dims({T, K, N}));
+  if (tp_size < 1 || K % tp_size) return TP_ERR_TP_DIVISIBILITY;
+  const int64_t k = K / tp_size;
+  TP_TRY(check_feature({k, N}));
+  TP_TRY(check_elems({{T, k}, {k, N}, {T, N}}));
+  TP_TRY(check_ptrs_aligned({X_i, W_i, dY, dX_i, dW_i, db, workspace}));
+  const size_t need = db ? tp_workspace_size(TP_OP_ROW_LINEAR_BWD, T, K, N, tp_size, dtype) : 0;
+  if (db && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
+  const int64_t es = elsize(dtype);
+  TP_TRY(check_alias({{X_i, T * k * es}, {W_i, k * N * es}, {dY, T * N * es}},
+                     {{dX_i, T * k * es}, {dW_i, k * N * 4}, {db, db ? N * 4 : 0}, {workspace, (int64_t)need}}));
+  hipStream_t s = (hipStream_t)stream;
+  // dX_i = dY W_i^T  [T x k], contraction over N
+  GemmArgs g1 = make_args(dY, N, W_i, N, T, k, N, dX_i, k);
+  HIP_TRY(gemm(dtype, g1, true, true, EPI_STORE, s));
+  // dW_i = X_i^T dY  [k x N], contraction over T
+  GemmArgs g2 = make_args(X_i, k, dY, N, k, N, T, dW_i, N);
+  g2.accumulate = accumulate;
+  HIP_TRY(gemm(dtype, g2, false, false, EPI_F32, s));
+  if (db) HIP_TRY(colsum(dY, dtype == TP_BF16, db, (float*)workspace, accumulate, T, N, s));
+  return TP_OK;
+}
+
+int tp_bias_grad(const void* dY, float* db, void* workspace, size_t workspace_bytes, int32_t accumulate, int64_t T,
+                 int64_t N, int32_t dtype, void* stream) {
+  TP_TRY(check_dtype(dtype));
+  if (accumulate != 0 && accumulate != 1) return TP_ERR_ARG;
+  TP_TRY(check_nonnull({dY, db}));
+  TP_TRY(check_dims({T, N}));
+  TP_TRY(check_feature({N}));
+  TP_TRY(check_elems({{T, N}}));
+  TP_TRY(check_ptrs_aligned({dY, db, workspace}));
+  const size_t need = tp_workspace_size(TP_OP_BIAS_GRAD, T, N, 0, 1, dtype);
+  if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
+  TP_TRY(check_alias({{dY, T * N * elsize(dtype)}}, {{db, N * 4}, {workspace, (int64_t)need}}));
+  HIP_TRY(colsum(dY, dtype == TP_BF16, db, (float*)workspace, accumulate, T, N, (hipStream_t)stream));
+  return TP_OK;
+}
+
+int tp_bias_gelu(const void* Z, const void* b, void* H, int64_t T, int64_t N, int32_t dtype, void* stream) {
+  TP_TRY(check_dtype(dtype));
+  TP_TRY(check_nonnull({Z, H}));
+  TP_TRY(check_dims({T, N}));
+  TP_TRY(check_feature({N}));
+  TP_TRY(check_elems({{T, N}}));
+  TP_TRY(check_ptrs_aligned({Z, b, H}));
+  const int64_t es = elsize(dtype);
+  TP_TRY(check_alias({{Z, T * N * es}, {b, N * es}}, {{H, T * N * es}}));
+  HIP_TRY(bias_gelu(Z, b, H, dtype == TP_BF16, T, N, (hipStream_t)stream));
+  return TP_OK;
+}
+
+// ---------------------------------------------------------------- trace
+int tp_trace_start(int32_t max_launches) {
+  Trace& t = trace();
+  std::lock_guard<std::mutex> lock(t.mu);
+  if (max_launches < 1) return TP_ERR_ARG;
+  if ((int)t.ev.size() < 2 * max_launches) {
+    const size_t old = t.ev.size();
+    t.ev.resize(2 * (size_t)max_launches);
+    for (size_t i = old; i < t.ev.size(); ++i)
+      if (hipEventCreate(&t.ev[i]) != hipSuccess) {
+        t.ev.resize(i);
+        return TP_ERR_HIP;
+      }
+  }
+  t.info.assign(max_launches, LaunchInfo{nullptr, 0, 0});
+  t.max = max_launches;
+  t.n = 0;
+  t.on = true;
+  return TP_OK;
+}
+
+int tp_trace_stop(void) {
+  Trace& t = trace();
+  std::lock_guard<std::mutex> lock(t.mu);
+  if (!t.on) return TP_ERR_ARG;
+  t.on = false;
+  t.result.clear();
+  if (t.n == 0) return TP_OK;
+  if (hipEventSynchronize(t.ev[2 * t.n - 1]) != hipSuccess) return TP_ERR_HIP;
+  std::map<std::string, size_t> index;
+  for (int i = 0; i < t.n; ++i) {
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, t.ev[2 * i], t.ev[2 * i + 1]) != hipSuccess) return TP_ERR_HIP;
+    const std::string name = t.info[i].name ? t.info[i].name : "?";
+    auto it = index.find(name);
+    if (it == index.end()) {
+      it = index.emplace(name, t.result.size()).first;
+      t.result.push_back(TraceAgg{name});
+    }
+    TraceAgg& a = t.result[it->second];
+    a.launches += 1;
+    a.ms += ms;
+    a.flops += t.info[i].flops;
+    a.bytes += t.info[i].bytes;
+  }
+  return TP_OK;
+}
+
+int tp_trace_num_kernels(void) {
+  Trace& t = trace();
+  std::lock_guard<std::mutex> lock(t.mu);
+  return (int)t.result.size();
+}
+
+int tp_trace_kernel(int32_t idx, char* name, size_t name_len, int64_t* launches, double* total_ms, double* flops,
+                    double* bytes) {
+  Trace& t = trace();
+  std::lock_guard<std::mutex> lock(t.mu);
+  if (idx < 0 || idx >= (int)t.result.size()) return TP_ERR_ARG;
+  const TraceAgg& a = t.result[idx];
+  if (name && name_len) {
+    std::strncpy(name, a.name.c_str(), name_len - 1);
+    name[name_len - 1] = '\0';
+  }
+  if (launches) *launches = a.launches;
+  if (total_ms) *total_ms = a.ms;
+  if (flops) *flops = a.flops;
+  if (bytes) *bytes = a.bytes;
+  return TP_OK;
+}
+
+}  // extern "C"

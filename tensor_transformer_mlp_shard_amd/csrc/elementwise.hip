@@ -1,0 +1,148 @@
+// Memory-bound side kernels: the token-sum of a gradient (bias gradients) and
+// the unfused bias + GeLU pass.
+//
+// Column sum.  out[n] (+)= sum_t in[t, n] over a row-major [T x N] matrix.
+// Pass 1: a workgroup (4 waves) owns 512 columns (a lane holds 8 consecutive
+// columns, so each wave reads one contiguous 1 KiB (bf16) run of a row) and a
+// chunk of rows; wave w sums rows w, w+4, ... of the chunk in fp32, the four
+// wave sums are added in a fixed order through LDS and written as one partial
+// row.  Pass 2 adds the partial rows of every column in chunk order.  There
+// are no atomics, so the result is bitwise reproducible.
+//
+// Bias + GeLU.  H = GeLU(Z + b) with 8 elements per lane (16-byte bf16 loads).
+#include "common.h"
+
+namespace tps {
+namespace {
+
+constexpr int CS_COLS = 512;  // columns per workgroup in pass 1
+constexpr int CS_THREADS = 256;
+
+template <bool IN_BF16>
+__device__ __forceinline__ void load8(const void* base, int64_t off, float* v) {
+  if (IN_BF16) {
+    const bf16x8 x = *(const bf16x8*)((const bf16*)base + off);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
+  } else {
+    const f32x4 a = *(const f32x4*)((const float*)base + off);
+    const f32x4 b = *(const f32x4*)((const float*)base + off + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
+  }
+}
+
+template <bool IN_BF16>
+__global__ void __launch_bounds__(CS_THREADS) colsum_partial_kernel(const void* in, float* part, int64_t T,
+                                                                    int64_t N, int64_t rows_per_chunk) {
+  __shared__ float red[4][CS_COLS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t col = (int64_t)blockIdx.x * CS_COLS + lane * 8;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_chunk;
+  const int64_t r1 = min(T, r0 + rows_per_chunk);
+  float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (col < N) {
+    for (int64_t r = r0 + wave; r < r1; r += 4) {
+      float v[8];
+      load8<IN_BF16>(in, r * N + col, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] += v[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[wave][lane * 8 + e] = s[e];
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = threadIdx.x + CS_THREADS * h;
+    const int64_t gc = (int64_t)blockIdx.x * CS_COLS + c;
+    if (gc < N) part[(int64_t)blockIdx.y * N + gc] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+  }
+}
+
+__global__ void __launch_bounds__(256) colsum_finalize_kernel(const float* part, float* out, int64_t N,
+                                                              int chunks, int accumulate) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  float s = accumulate ? out[n] : 0.0f;
+  float t = 0.0f;
+  for (int c = 0; c < chunks; ++c) t += part[(int64_t)c * N + n];
+  out[n] = s + t;
+}
+
+template <bool IS_BF16>
+__global__ void __launch_bounds__(256) bias_gelu_kernel(const void* Z, const void* b, void* H, int64_t T,
+                                                        int64_t N) {
+  const int64_t nv = N / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= T * nv) return;
+  const int64_t row = idx / nv;
+  const int64_t c = (idx - row * nv) * 8;
+  float z[8], bb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  load8<IS_BF16>(Z, row * N + c, z);
+  if (b != nullptr) load8<IS_BF16>(b, c, bb);
+  float h[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = z[e] + bb[e];
+    h[e] = 0.5f * x * (1.0f + erff(x * 0.7071067811865475f));
+  }
+  if (IS_BF16) {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16)h[e];
+    *(bf16x8*)((bf16*)H + row * N + c) = o;
+  } else {
+    float* p = (float*)H + row * N + c;
+    *(f32x4*)p = f32x4{h[0], h[1], h[2], h[3]};
+    *(f32x4*)(p + 4) = f32x4{h[4], h[5], h[6], h[7]};
+  }
+}
+
+}  // namespace
+
+int colsum_chunks(int64_t T, int64_t N) {
+  const int64_t col_blocks = (N + CS_COLS - 1) / CS_COLS;
+  int64_t chunks = (1024 + col_blocks - 1) / col_blocks;
+  const int64_t max_by_rows = (T + 3) / 4;
+  if (chunks > max_by_rows) chunks = max_by_rows;
+  if (chunks > 256) chunks = 256;
+  if (chunks < 1) chunks = 1;
+  return (int)chunks;
+}
+
+hipError_t colsum(const void* in, bool in_bf16, float* out, float* ws, int accumulate, int64_t T, int64_t N,
+                  hipStream_t s) {
+  const int chunks = colsum_chunks(T, N);
+  const int64_t rows_per_chunk = (T + chunks - 1) / chunks;
+  const dim3 grid1((unsigned)((N + CS_COLS - 1) / CS_COLS), (unsigned)chunks);
+  LaunchInfo info{"colsum_partial", 0.0, (in_bf16 ? 2.0 : 4.0) * T * (double)N + 4.0 * chunks * (double)N};
+  trace_begin(s);
+  if (in_bf16)
+    hipLaunchKernelGGL(colsum_partial_kernel<true>, grid1, dim3(CS_THREADS), 0, s, in, ws, T, N, rows_per_chunk);
+  else
+    hipLaunchKernelGGL(colsum_partial_kernel<false>, grid1, dim3(CS_THREADS), 0, s, in, ws, T, N, rows_per_chunk);
+  trace_end(s, info);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  LaunchInfo info2{"colsum_finalize", 0.0, 4.0 * chunks * (double)N + 4.0 * (accumulate ? 2 : 1) * N};
+  trace_begin(s);
+  hipLaunchKernelGGL(colsum_finalize_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s,
+                     (const float*)ws, out, N, chunks, accumulate);
+  trace_end(s, info2);
+  return hipGetLastError();
+}
+
+hipError_t bias_gelu(const void* Z, const void* b, void* H, bool is_bf16, int64_t T, int64_t N, hipStream_t s) {
+  const int64_t n = T * (N / 8);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  const double el = is_bf16 ? 2.0 : 4.0;
+  LaunchInfo info{"bias_gelu", 0.0, el * (2.0 * T * (double)N + (b ? N : 0))};
+  trace_begin(s);
+  if (is_bf16) hipLaunchKernelGGL(bias_gelu_kernel<true>, grid, dim3(256), 0, s, Z, b, H, T, N);
+  else hipLaunchKernelGGL(bias_gelu_kernel<false>, grid, dim3(256), 0, s, Z, b, H, T, N);
+  trace_end(s, info);
+  return hipGetLastError();
+}
+
+}  // namespace tps

@@ -1,0 +1,144 @@
+"""The C ABI: the library loads on a host without a GPU, exports every symbol
+include/*.h declares, and rejects invalid arguments before touching the GPU.
+
+Only validation paths are exercised here: each call below fails a check that
+runs before any HIP call, so no pointer is dereferenced and nothing is
+launched (the pointers are arbitrary aligned integers)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from tensor_transformer_mlp_shard_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_native.LIB_PATH):
+        import __graft_entry__  # builds the library in-tree
+        __graft_entry__.build()
+    return _native.lib()
+
+
+def _declared():
+    names = set()
+    for hdr in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(hdr).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(tp_\w+)\s*\(", text))
+    return names
+
+
+def test_header_declares_the_boundary():
+    d = _declared()
+    for n in ("tp_column_linear", "tp_row_linear", "tp_mlp_shard_fwd", "tp_mlp_shard_bwd",
+              "tp_column_linear_bwd", "tp_row_linear_bwd", "tp_workspace_size", "tp_status_string"):
+        assert n in d
+
+
+def test_every_declared_symbol_is_exported(lib):
+    d = _declared()
+    assert d
+    for name in d:
+        assert hasattr(lib, name), name
+        assert name in _native.PROTOTYPES, name
+
+
+def test_status_strings(lib):
+    for code in _native.STATUS:
+        s = lib.tp_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.tp_status_string(12345).decode() == "unknown status"
+
+
+P = ctypes.c_void_p
+A0, A1, A2, A3, A4, A5, A6 = (P(0x10000 * (i + 1)) for i in range(7))   # 16-byte aligned, disjoint-ish
+S = P(0)
+
+
+def test_column_linear_validation(lib):
+    f = lib.tp_column_linear
+    ok = dict(T=128, K=256, N=1024, tp=2)
+    # null pointers
+    assert f(None, A1, None, A2, None, 128, 256, 1024, 2, 0, 0, S) == -1
+    # non-positive dims
+    assert f(A0, A1, None, A2, None, 0, 256, 1024, 2, 0, 0, S) == -2
+    assert f(A0, A1, None, A2, None, 128, -8, 1024, 2, 0, 0, S) == -2
+    assert f(A0, A1, None, A2, None, 1 << 31, 256, 1024, 2, 0, 0, S) == -2
+    # TP divisibility
+    assert f(A0, A1, None, A2, None, 128, 256, 1000, 3, 0, 0, S) == -3
+    assert f(A0, A1, None, A2, None, 128, 256, 1024, 0, 0, 0, S) == -3
+    # feature alignment: K not a multiple of 8, shard width not a multiple of 8
+    assert f(A0, A1, None, A2, None, 128, 250, 1024, 2, 0, 0, S) == -4
+    assert f(A0, A1, None, A2, None, 128, 256, 1028, 2, 0, 0, S) == -4
+    # misaligned pointer
+    assert f(P(0x10008), A1, None, A2, None, 128, 256, 1024, 2, 0, 0, S) == -4
+    # dtype / activation codes
+    assert f(A0, A1, None, A2, None, 128, 256, 1024, 2, 0, 7, S) == -5
+    assert f(A0, A1, None, A2, None, 128, 256, 1024, 2, 5, 0, S) == -5
+    # Z given without activation
+    assert f(A0, A1, None, A2, A3, 128, 256, 1024, 2, 0, 0, S) == -9
+    # output aliasing an input (Y_i == X)
+    assert f(A0, A1, None, A0, None, 128, 256, 1024, 2, 0, 0, S) == -6
+    # Z overlapping Y
+    assert f(A0, A1, None, A2, P(A2.value + 64), 128, 256, 1024, 2, 1, 0, S) == -6
+
+
+def test_row_linear_validation(lib):
+    f = lib.tp_row_linear
+    assert f(A0, None, None, A2, 128, 1024, 256, 2, 0, S) == -1
+    assert f(A0, A1, None, A2, 128, 1024, 256, 3, 0, S) == -3
+    assert f(A0, A1, None, A2, 128, 1032, 256, 2, 0, S) == -4    # K/p = 516 not a multiple of 8
+    assert f(A0, A1, None, A1, 128, 1024, 256, 2, 0, S) == -6
+
+
+def test_mlp_fwd_validation(lib):
+    f = lib.tp_mlp_shard_fwd
+    assert f(A0, A1, None, A2, None, None, A4, 128, 256, 1024, 2, 0, S) == -1     # H missing
+    assert f(A0, A1, None, A2, None, A3, A4, 128, 256, 1024, 3, 0, S) == -3
+    assert f(A0, A1, None, A2, None, A3, A4, 128, 260, 1024, 2, 0, S) == -4
+    assert f(A0, A1, None, A2, A3, A3, A4, 128, 256, 1024, 2, 0, S) == -6          # Z == H
+    assert f(A0, A1, None, A2, None, A3, A4, 128, 256, 1024, 2, 2, S) == -5
+
+
+def test_mlp_bwd_validation(lib):
+    f = lib.tp_mlp_shard_bwd
+    need = lib.tp_workspace_size(_native.TP_OP_MLP_SHARD_BWD, 128, 256, 1024, 2, 0)
+    assert need > 128 * 512 * 2
+    base = [A0, A1, A2, A3, A4, A5, A6, P(0x100000), None, P(0x200000), None]
+    ws = P(0x1000000)
+    # workspace missing / too small
+    assert f(*base, None, 0, 0, 128, 256, 1024, 2, 0, S) == -7
+    assert f(*base, ws, need - 1, 0, 128, 256, 1024, 2, 0, S) == -7
+    # bad accumulate flag
+    assert f(*base, ws, need, 2, 128, 256, 1024, 2, 0, S) == -9
+    # dA_i aliasing dB_i
+    bad = list(base)
+    bad[9] = bad[7]
+    assert f(*bad, ws, need, 0, 128, 256, 1024, 2, 0, S) == -6
+
+
+def test_linear_bwd_validation(lib):
+    need = lib.tp_workspace_size(_native.TP_OP_ROW_LINEAR_BWD, 64, 512, 256, 2, 0)
+    assert need >= 256 * 4
+    f = lib.tp_row_linear_bwd
+    assert f(A0, A1, A2, A3, A4, A5, None, 0, 0, 64, 512, 256, 2, 0, S) == -7   # db wanted, no workspace
+    assert f(A0, A1, A2, A3, A4, A5, A6, need - 4, 0, 64, 512, 256, 2, 0, S) == -7
+    g = lib.tp_column_linear_bwd
+    assert g(A0, A1, A2, A0, A4, None, None, 0, 0, 64, 256, 512, 2, 0, S) == -6  # dX == X
+
+
+def test_workspace_size(lib):
+    ws = lib.tp_workspace_size
+    assert ws(99, 128, 256, 1024, 2, 0) == 0
+    assert ws(_native.TP_OP_MLP_SHARD_BWD, 0, 256, 1024, 2, 0) == 0
+    assert ws(_native.TP_OP_MLP_SHARD_BWD, 128, 256, 1000, 3, 0) == 0
+    a = ws(_native.TP_OP_MLP_SHARD_BWD, 2048, 12288, 49152, 8, 0)
+    assert a >= 2048 * 6144 * 2
+    assert ws(_native.TP_OP_MLP_SHARD_BWD, 2048, 12288, 49152, 8, 1) > a   # fp32 dZ
+    assert ws(_native.TP_OP_BIAS_GRAD, 4096, 1024, 0, 1, 0) >= 1024 * 4
+    assert ws(_native.TP_OP_COLUMN_LINEAR_BWD, 8192, 12288, 36864, 8, 0) >= 4608 * 4

@@ -1,0 +1,296 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Every output is compared by relative Frobenius error ||G - O||_F / ||O||_F:
+<= 5e-3 for bf16 storage with fp32 accumulation, <= 1e-5 for the fp32 path.
+Small workloads are compared element by element over the whole tensor; the
+175B-shaped workloads run at full size in the launch configuration the
+benchmark times, and are compared on sampled rows (forward outputs and dX,
+which depend only on their own token row) and sampled feature columns (dA, dB,
+db1 and dW, db, obtained from the oracle by narrowing the shard, which the
+column-shard identity makes exact).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tensor_transformer_mlp_shard_amd as tps
+from tensor_transformer_mlp_shard_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.bfloat16: 5e-3, torch.float32: 1e-5}
+DEV = "cuda:0"
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def dev(t):
+    return t.to(DEV)
+
+
+def _rel(name, got, ref, tol):
+    e = oracle.rel_fro(got, ref)
+    print(f"  {name:8s} rel_fro={e:.3e} (tol {tol:g})", flush=True)
+    assert e <= tol, f"{name}: rel_fro {e:.3e} > {tol:g}"
+    return e
+
+
+def _shard(d, p, rank):
+    """Rank `rank`'s MLP shard of unsharded weights (contiguous blocks)."""
+    f = d["A"].shape[1] // p
+    s = slice(rank * f, (rank + 1) * f)
+    return d["A"][:, s].contiguous(), d["b1"][s].contiguous(), d["B"][s, :].contiguous()
+
+
+def run_mlp(X, A, b1, B, dY, p, want_db2=True):
+    Xd, Ad, b1d, Bd, dYd = (dev(t) for t in (X, A, b1, B, dY))
+    Z, H, Y = tps.mlp_shard_fwd(Xd, Ad, b1d, Bd, tp_size=p)
+    g = tps.mlp_shard_bwd(Xd, Ad, Bd, Z, H, dYd, tp_size=p, want_db2=want_db2)
+    torch.cuda.synchronize()
+    return {"Z": Z, "H": H, "Y": Y, **g}
+
+
+def check_mlp_full(X, A, b1, B, dY, p, dtype):
+    tol = TOL[dtype]
+    got = run_mlp(X, A, b1, B, dY, p)
+    x, a, bb1, bb, dy = (f64(t) for t in (X, A, b1, B, dY))
+    Z, H, Y = oracle.mlp_shard_fwd(x, a, bb1, bb)
+    ref = oracle.mlp_shard_bwd(x, a, bb1, bb, dy)
+    _rel("Z", f64(got["Z"]), Z, tol)
+    _rel("H", f64(got["H"]), H, tol)
+    _rel("Y", f64(got["Y"]), Y, tol)
+    _rel("dX", f64(got["dX"]), ref["dX"], tol)
+    _rel("dA", f64(got["dA"]), ref["dA"], tol)
+    _rel("db1", f64(got["db1"]), ref["db1"], tol)
+    _rel("dB", f64(got["dB"]), ref["dB"], tol)
+    _rel("db2", f64(got["db2"]), oracle.bias_grad(dy), tol)
+    return got
+
+
+# ---------------------------------------------------------------------------
+# Workloads small enough for a whole-tensor comparison
+# ---------------------------------------------------------------------------
+def test_tiny_tp2_fp32_both_ranks_and_shard_sum():
+    w = synth.WORKLOADS["tiny_tp2_fp32"]
+    d = synth.inputs_for(w)
+    Ys = []
+    for rank in range(w.tp):
+        A, b1, B = _shard(d, w.tp, rank)
+        print(f"tiny fp32 rank {rank}", flush=True)
+        got = check_mlp_full(d["X"], A, b1, B, d["dY"], w.tp, torch.float32)
+        Ys.append(f64(got["Y"]))
+    # the row-parallel partials of the two ranks sum to the unsharded MLP
+    _, _, Y_full = oracle.mlp_shard_fwd(*(f64(d[k]) for k in ("X", "A", "b1", "B")))
+    _rel("sumY", Ys[0] + Ys[1], Y_full, 1e-5)
+
+
+def test_gpt_h1024_tp2_rank_shards():
+    w = synth.WORKLOADS["gpt_h1024_tp2"]
+    d = synth.inputs_for(w)
+    Ys = []
+    for rank in range(w.tp):
+        A, b1, B = _shard(d, w.tp, rank)
+        print(f"gpt h1024 bf16 rank {rank}", flush=True)
+        got = check_mlp_full(d["X"], A, b1, B, d["dY"], w.tp, torch.bfloat16)
+        Ys.append(f64(got["Y"]))
+    _, _, Y_full = oracle.mlp_shard_fwd(*(f64(d[k]) for k in ("X", "A", "b1", "B")))
+    _rel("sumY", Ys[0] + Ys[1], Y_full, 5e-3)
+
+
+# ---------------------------------------------------------------------------
+# Large workloads: full-size runs, sampled comparison
+# ---------------------------------------------------------------------------
+def _sample(n, k, seed):
+    rng = np.random.default_rng(seed)
+    idx = set(rng.choice(n, size=min(k, n), replace=False).tolist())
+    idx |= {0, n - 1}
+    return np.array(sorted(idx))
+
+
+def check_mlp_sampled(X, A, b1, B, dY, p, rows, cols):
+    tol = 5e-3
+    got = run_mlp(X, A, b1, B, dY, p)
+    R = torch.from_numpy(rows)
+    J = torch.from_numpy(cols)
+    x_r, dy_r = f64(X[R]), f64(dY[R])
+    a, bb1, bb = f64(A), f64(b1), f64(B)
+    Z, H, Y = oracle.mlp_shard_fwd(x_r, a, bb1, bb)
+    _rel("Z[R]", f64(got["Z"][R.to(DEV)]), Z, tol)
+    _rel("H[R]", f64(got["H"][R.to(DEV)]), H, tol)
+    _rel("Y[R]", f64(got["Y"][R.to(DEV)]), Y, tol)
+    _rel("dX[R]", f64(got["dX"][R.to(DEV)]), oracle.mlp_shard_bwd(x_r, a, bb1, bb, dy_r)["dX"], tol)
+    x, dy = f64(X), f64(dY)
+    refc = oracle.mlp_shard_bwd(x, a[:, cols], bb1[cols], bb[cols, :], dy)
+    Jd = J.to(DEV)
+    _rel("dA[:,J]", f64(got["dA"][:, Jd]), refc["dA"], tol)
+    _rel("dB[J]", f64(got["dB"][Jd]), refc["dB"], tol)
+    _rel("db1[J]", f64(got["db1"][Jd]), refc["db1"], tol)
+    _rel("db2", f64(got["db2"]), oracle.bias_grad(dy), tol)
+
+
+def test_gpt_1p3b_tp1_sampled():
+    w = synth.WORKLOADS["gpt_1p3b_tp1"]
+    d = synth.inputs_for(w)
+    print("gpt 1.3B tp1 bf16", flush=True)
+    check_mlp_sampled(d["X"], d["A"], d["b1"], d["B"], d["dY"], w.tp,
+                      _sample(w.T, 96, 11), _sample(w.f, 96, 12))
+
+
+def test_gpt175b_mlp_tp8_sampled():
+    w = synth.WORKLOADS["gpt175b_mlp_tp8"]
+    d = synth.inputs_for(w)
+    print("gpt175b mlp tp8 bf16", flush=True)
+    check_mlp_sampled(d["X"], d["A"], d["b1"], d["B"], d["dY"], w.tp,
+                      _sample(w.T, 64, 13), _sample(w.f, 64, 14))
+
+
+def test_gpt175b_attn_tp8_sampled():
+    w = synth.WORKLOADS["gpt175b_attn_tp8"]
+    d = synth.inputs_for(w)
+    tol = 5e-3
+    print("gpt175b attention linears tp8 bf16", flush=True)
+    X, Wq, bq, O, Wo, dQ, dY = (dev(d[k]) for k in ("X", "W_qkv", "b_qkv", "O", "W_o", "dQKV", "dY"))
+    QKV = tps.column_linear(X, Wq, bq, tp_size=w.tp)
+    gq = tps.column_linear_bwd(X, Wq, dQ, tp_size=w.tp)
+    Yo = tps.row_linear(O, Wo, None, tp_size=w.tp)
+    go = tps.row_linear_bwd(O, Wo, dY, tp_size=w.tp)
+    torch.cuda.synchronize()
+    R = torch.from_numpy(_sample(w.T, 48, 15))
+    Rd = R.to(DEV)
+    Jq = _sample(Wq.shape[1], 48, 16)
+    Jo = _sample(Wo.shape[1], 48, 17)
+    x_r = f64(d["X"][R])
+    wq, wo = f64(d["W_qkv"]), f64(d["W_o"])
+    _, ref = oracle.column_linear_fwd(x_r, wq, f64(d["b_qkv"]))
+    _rel("QKV[R]", f64(QKV[Rd]), ref, tol)
+    _rel("dXq[R]", f64(gq["dX"][Rd]), oracle.linear_bwd(x_r, wq, f64(d["dQKV"][R]))["dX"], tol)
+    rq = oracle.linear_bwd(f64(d["X"]), wq[:, Jq], f64(d["dQKV"])[:, Jq])
+    _rel("dWq[:,J]", f64(gq["dW"][:, torch.from_numpy(Jq).to(DEV)]), rq["dW"], tol)
+    _rel("dbq[J]", f64(gq["db"][torch.from_numpy(Jq).to(DEV)]), rq["db"], tol)
+    o_r = f64(d["O"][R])
+    _rel("Yo[R]", f64(Yo[Rd]), oracle.row_linear_fwd(o_r, wo), tol)
+    _rel("dO[R]", f64(go["dX"][Rd]), oracle.linear_bwd(o_r, wo, f64(d["dY"][R]))["dX"], tol)
+    ro = oracle.linear_bwd(f64(d["O"]), wo[:, Jo], f64(d["dY"])[:, Jo])
+    _rel("dWo[:,J]", f64(go["dW"][:, torch.from_numpy(Jo).to(DEV)]), ro["dW"], tol)
+    _rel("dbo[J]", f64(go["db"][torch.from_numpy(Jo).to(DEV)]), ro["db"], tol)
+
+
+# ---------------------------------------------------------------------------
+# Edges: ragged tiles, tiny T, several TP degrees, both dtypes
+# ---------------------------------------------------------------------------
+EDGE = [
+    # (T, h, f, p)
+    (1, 8, 8, 1),
+    (7, 64, 40, 2),
+    (131, 264, 136, 4),
+    (257, 520, 392, 2),
+    (300, 128, 1032, 1),
+    (513, 1288, 264, 8),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("shape", EDGE, ids=[f"T{s[0]}_h{s[1]}_f{s[2]}_p{s[3]}" for s in EDGE])
+def test_mlp_edges(shape, dtype):
+    T, h, f, p = shape
+    dt = "bf16" if dtype == torch.bfloat16 else "fp32"
+    d = synth.mlp_inputs(T, h, f * p, p, dt, 0.05, seed=T * 7 + h, full=False)
+    print(f"edge {shape} {dt}", flush=True)
+    check_mlp_full(d["X"], d["A"], d["b1"], d["B"], d["dY"], p, dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_linears_edges(dtype):
+    dt = "bf16" if dtype == torch.bfloat16 else "fp32"
+    tol = TOL[dtype]
+    for T, K, N, p in [(5, 48, 96, 2), (133, 288, 544, 4), (300, 1024, 264, 1)]:
+        print(f"linears T{T} K{K} N{N} p{p} {dt}", flush=True)
+        g = synth.seeded(T + K + N)
+        X = synth.randn(g, (T, K), 1.0, dt)
+        W = synth.randn(g, (K, N // p), 0.05, dt)
+        b = synth.randn(g, (N // p,), 0.05, dt)
+        dY = synth.randn(g, (T, N // p), 1.0, dt)
+        Xi = synth.randn(g, (T, K // p), 1.0, dt)
+        Wr = synth.randn(g, (K // p, N), 0.05, dt)
+        br = synth.randn(g, (N,), 0.05, dt)
+        dYr = synth.randn(g, (T, N), 1.0, dt)
+        y = tps.column_linear(dev(X), dev(W), dev(b), tp_size=p)
+        yg, zg = tps.column_linear(dev(X), dev(W), dev(b), tp_size=p, act="gelu", save_z=True)
+        gc = tps.column_linear_bwd(dev(X), dev(W), dev(dY), tp_size=p)
+        yr = tps.row_linear(dev(Xi), dev(Wr), dev(br), tp_size=p)
+        gr = tps.row_linear_bwd(dev(Xi), dev(Wr), dev(dYr), tp_size=p)
+        torch.cuda.synchronize()
+        zr, yr_ref = oracle.column_linear_fwd(f64(X), f64(W), f64(b))
+        _rel("col.Y", f64(y), yr_ref, tol)
+        zg_ref, yg_ref = oracle.column_linear_fwd(f64(X), f64(W), f64(b), act="gelu")
+        _rel("col.Zg", f64(zg), zg_ref, tol)
+        _rel("col.Yg", f64(yg), yg_ref, tol)
+        rc = oracle.linear_bwd(f64(X), f64(W), f64(dY))
+        _rel("col.dX", f64(gc["dX"]), rc["dX"], tol)
+        _rel("col.dW", f64(gc["dW"]), rc["dW"], tol)
+        _rel("col.db", f64(gc["db"]), rc["db"], tol)
+        _rel("row.Y", f64(yr), oracle.row_linear_fwd(f64(Xi), f64(Wr), f64(br)), tol)
+        rr = oracle.linear_bwd(f64(Xi), f64(Wr), f64(dYr))
+        _rel("row.dX", f64(gr["dX"]), rr["dX"], tol)
+        _rel("row.dW", f64(gr["dW"]), rr["dW"], tol)
+        _rel("row.db", f64(gr["db"]), rr["db"], tol)
+
+
+# ---------------------------------------------------------------------------
+# Properties
+# ---------------------------------------------------------------------------
+def test_deterministic_repeat():
+    d = synth.mlp_inputs(1000, 1024, 2048, 1, "bf16", 0.02, seed=21, full=False)
+    a = run_mlp(d["X"], d["A"], d["b1"], d["B"], d["dY"], 1)
+    b = run_mlp(d["X"], d["A"], d["b1"], d["B"], d["dY"], 1)
+    for k in ("Z", "H", "Y", "dX", "dA", "dB", "db1", "db2"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_inference_mode_matches():
+    d = synth.mlp_inputs(200, 256, 512, 1, "bf16", 0.02, seed=22, full=False)
+    Xd, Ad, b1d, Bd = (dev(d[k]) for k in ("X", "A", "b1", "B"))
+    z, h1, y1 = tps.mlp_shard_fwd(Xd, Ad, b1d, Bd, tp_size=1, save_z=True)
+    none, h2, y2 = tps.mlp_shard_fwd(Xd, Ad, b1d, Bd, tp_size=1, save_z=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(h1, h2) and torch.equal(y1, y2)
+
+
+def test_accumulate_adds():
+    d = synth.mlp_inputs(96, 128, 256, 2, "bf16", 0.05, seed=23, full=False)
+    Xd, Ad, b1d, Bd, dYd = (dev(d[k]) for k in ("X", "A", "b1", "B", "dY"))
+    Z, H, _ = tps.mlp_shard_fwd(Xd, Ad, b1d, Bd, tp_size=2)
+    g1 = tps.mlp_shard_bwd(Xd, Ad, Bd, Z, H, dYd, tp_size=2, want_db2=True)
+    base = {k: torch.full_like(g1[k], 0.5) for k in ("dA", "dB", "db1", "db2")}
+    acc = {k: v.clone() for k, v in base.items()}
+    tps.mlp_shard_bwd(Xd, Ad, Bd, Z, H, dYd, tp_size=2, want_db2=True, accumulate=True, out=acc)
+    torch.cuda.synchronize()
+    for k in base:
+        torch.testing.assert_close(acc[k], base[k] + g1[k], rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_bias_gelu_and_bias_grad(dtype):
+    dt = "bf16" if dtype == torch.bfloat16 else "fp32"
+    g = synth.seeded(31)
+    Z = synth.randn(g, (333, 1048), 2.0, dt)
+    b = synth.randn(g, (1048,), 0.5, dt)
+    H = tps.bias_gelu(dev(Z), dev(b))
+    db = tps.bias_grad(dev(Z))
+    torch.cuda.synchronize()
+    _rel("gelu", f64(H), oracle.bias_gelu(f64(Z), f64(b)), TOL[dtype])
+    _rel("colsum", f64(db), oracle.bias_grad(f64(Z)), 1e-5)
+
+
+def test_python_binding_rejects_bad_inputs():
+    x = torch.zeros((4, 16), dtype=torch.bfloat16, device=DEV)
+    w = torch.zeros((16, 8), dtype=torch.float32, device=DEV)
+    with pytest.raises(TypeError):
+        tps.column_linear(x, w, tp_size=1)
+    w = torch.zeros((16, 12), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(RuntimeError, match="TP_ERR_ALIGNMENT"):
+        tps.column_linear(x, w, tp_size=1)
