@@ -7,19 +7,19 @@
 //
 // Tiling.  A workgroup of 4 waves (2 x 2) owns a BM x BN tile of C; each wave a
 // (BM/2) x (BN/2) sub-tile of 32 x 32 MFMA blocks whose fp32 accumulators stay in
-// the AGPR file for the whole K loop.  The K loop steps by 64: the next A and B
-// panels are fetched from HBM into registers with 16-byte loads while the matrix
-// cores work on the current panels in LDS, then written to the other LDS buffer
-// (two buffers, one barrier per step).
+// the AGPR file for the whole K loop.  The K loop steps by 64 through two LDS
+// stages: while the matrix cores work on one stage, the next A and B panels are
+// copied HBM -> LDS by buffer_load_dwordx4 ... lds (no register staging; rows and
+// columns outside the matrix read as zero through the buffer range check).  The
+// MFMA operands of the next 16-wide k slice are read from LDS while the current
+// slice's MFMAs issue (register double buffer).
 //
 // Layouts.  Each operand is kept in LDS in its memory orientation:
-//  * K-contiguous panels (rows of A, or rows of B stored as [N x K]) as
-//    [rows][64 + 8] bf16; a lane's MFMA operand (8 consecutive k of one row) is
-//    one ds_read_b128.
-//  * M/N-contiguous panels (A stored [K x M], B stored [K x N]) as
-//    [64][cols + 32] bf16; a lane's operand is gathered across 8 k-rows by two
-//    ds_read_b64_tr_b16, whose 16-lane groups transpose a 4 x 16 block.
-// The row pads put the rows a read touches in distinct LDS banks.
+//  * K-contiguous panels (rows of A, or rows of B stored as [N x K]): a lane's
+//    MFMA operand (8 consecutive k of one row) is one ds_read_b128;
+//  * M/N-contiguous panels (A stored [K x M], B stored [K x N]): a lane's operand
+//    is gathered across 8 k-rows by two ds_read_b64_tr_b16, whose 16-lane groups
+//    transpose a 4 x 16 block.
 //
 // Output.  The MFMA is issued with the B fragment as its first operand, so a
 // lane's 16 results of a block are 4 runs of 4 consecutive columns of one row
@@ -72,25 +72,49 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
   tn = in_group / gsize;
 }
 
+// Direct global -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds):
+// lane i's bytes land at lds + 16 i; lanes whose offset is outside the buffer
+// record range write zeros.
+extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(
+    i32x4 rsrc, __attribute__((address_space(3))) unsigned* lds, int size, int voffset, int soffset,
+    int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(a & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff));
+  r[2] = __builtin_amdgcn_readfirstlane((int)n);
+  r[3] = 0x00020000;
+  return r;
+}
+
+constexpr int OOB = 0x7ffffff0;  // a voffset beyond every record range: the lane reads zeros
+
+// LDS layouts (per stage, no padding; 16-byte chunks permuted by XOR so that the
+// rows a read instruction touches fall in different banks):
+//  * K-contiguous panel [rows][64]: 128-byte rows; chunk c of row r sits in slot
+//    c ^ ((r >> 1) & 7).
+//  * M/N-contiguous panel [64][cols]: rows of 2*cols bytes; chunk c of k-row r sits
+//    in slot c ^ (2 * (r & 3)) (stays inside its aligned group of 8 chunks).
 template <int BM, int BN, bool AK, bool BKC, int EPI>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_kernel(GemmArgs g) {
-  constexpr int A_LD = AK ? (KT + 8) : (BM + 32);
-  constexpr int B_LD = BKC ? (KT + 8) : (BN + 32);
-  constexpr int A_ELEMS = AK ? BM * A_LD : KT * A_LD;
-  constexpr int B_ELEMS = BKC ? BN * B_LD : KT * B_LD;
-  constexpr int STAGE = A_ELEMS + B_ELEMS;
+  constexpr int A_BYTES = BM * KT * 2;
+  constexpr int B_BYTES = BN * KT * 2;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_INS = A_BYTES / 1024 / 4;  // 1 KiB direct-load instructions per wave per stage
+  constexpr int B_INS = B_BYTES / 1024 / 4;
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int A_CH = BM * KT / 8 / NT;  // 16-byte chunks per thread
-  constexpr int B_CH = BN * KT / 8 / NT;
-  static_assert(A_CH >= 1 && B_CH >= 1, "tile too small");
+  static_assert(A_INS * 4 * 1024 == A_BYTES && B_INS * 4 * 1024 == B_BYTES, "tile must fill whole loads");
 
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1;
   const int wn = wave & 1;
 
@@ -101,84 +125,103 @@ gemm_bf16_kernel(GemmArgs g) {
   const int m0 = tm * BM;
   const int n0 = tn * BN;
 
-  const bf16* __restrict__ Ag = (const bf16*)g.A;
-  const bf16* __restrict__ Bg = (const bf16*)g.B;
+  // Tile origins in memory and the bytes from there to the end of each matrix.
+  const char* a_base = (const char*)g.A + 2 * (AK ? (int64_t)m0 * g.lda : (int64_t)m0);
+  const char* b_base = (const char*)g.B + 2 * (BKC ? (int64_t)n0 * g.ldb : (int64_t)n0);
+  const int64_t a_total = 2 * ((AK ? (int64_t)g.M : (int64_t)g.K) * g.lda - (AK ? (int64_t)m0 * g.lda : m0));
+  const int64_t b_total = 2 * ((BKC ? (int64_t)g.N : (int64_t)g.K) * g.ldb - (BKC ? (int64_t)n0 * g.ldb : n0));
+  const int64_t a_step = AK ? 2 * KT : 2 * (int64_t)KT * g.lda;
+  const int64_t b_step = BKC ? 2 * KT : 2 * (int64_t)KT * g.ldb;
 
-  // Per-thread global pointers for the first K step and their fixed bounds.
-  const bf16* a_ptr[A_CH];
-  bool a_ok[A_CH];
-  int a_k[A_CH];      // k index of the chunk at K step 0 (row for !AK, col for AK)
-  int a_lds[A_CH];
+  // Per-lane byte offsets of each direct load inside the tile at the current K step.
+  int a_off[A_INS], a_kc[A_INS];
 #pragma unroll
-  for (int p = 0; p < A_CH; ++p) {
-    const int c = tid + NT * p;
+  for (int j = 0; j < A_INS; ++j) {
+    const int q = (wave * A_INS + j) * 64 + lane;  // 16-byte chunk index in the stage's A panel
     if (AK) {
-      const int row = c >> 3, kc = c & 7;
-      const int gm = m0 + row;
-      a_ok[p] = gm < g.M;
-      a_k[p] = kc * 8;
-      a_ptr[p] = Ag + (int64_t)(a_ok[p] ? gm : 0) * g.lda + kc * 8;
-      a_lds[p] = row * A_LD + kc * 8;
+      const int r = q >> 3, s = q & 7, c = s ^ ((r >> 1) & 7);
+      a_off[j] = r * (int)g.lda * 2 + c * 16;
+      a_kc[j] = c * 8;
     } else {
       constexpr int CPR = BM / 8;
-      const int krow = c / CPR, mc = c % CPR;
-      const int gm = m0 + mc * 8;
-      a_ok[p] = gm < g.M;
-      a_k[p] = krow;
-      a_ptr[p] = Ag + (int64_t)krow * g.lda + (a_ok[p] ? gm : 0);
-      a_lds[p] = krow * A_LD + mc * 8;
+      const int r = q / CPR, s = q % CPR, c = s ^ (2 * (r & 3));
+      a_off[j] = (m0 + c * 8 < g.M) ? r * (int)g.lda * 2 + c * 16 : OOB;
+      a_kc[j] = 0;
     }
   }
-  const bf16* b_ptr[B_CH];
-  bool b_ok[B_CH];
-  int b_k[B_CH];
-  int b_lds[B_CH];
+  int b_off[B_INS], b_kc[B_INS];
 #pragma unroll
-  for (int p = 0; p < B_CH; ++p) {
-    const int c = tid + NT * p;
+  for (int j = 0; j < B_INS; ++j) {
+    const int q = (wave * B_INS + j) * 64 + lane;
     if (BKC) {
-      const int row = c >> 3, kc = c & 7;
-      const int gn = n0 + row;
-      b_ok[p] = gn < g.N;
-      b_k[p] = kc * 8;
-      b_ptr[p] = Bg + (int64_t)(b_ok[p] ? gn : 0) * g.ldb + kc * 8;
-      b_lds[p] = row * B_LD + kc * 8;
+      const int r = q >> 3, s = q & 7, c = s ^ ((r >> 1) & 7);
+      b_off[j] = r * (int)g.ldb * 2 + c * 16;
+      b_kc[j] = c * 8;
     } else {
       constexpr int CPR = BN / 8;
-      const int krow = c / CPR, nc = c % CPR;
-      const int gn = n0 + nc * 8;
-      b_ok[p] = gn < g.N;
-      b_k[p] = krow;
-      b_ptr[p] = Bg + (int64_t)krow * g.ldb + (b_ok[p] ? gn : 0);
-      b_lds[p] = krow * B_LD + nc * 8;
+      const int r = q / CPR, s = q % CPR, c = s ^ (2 * (r & 3));
+      b_off[j] = (n0 + c * 8 < g.N) ? r * (int)g.ldb * 2 + c * 16 : OOB;
+      b_kc[j] = 0;
     }
   }
 
-  bf16x8 ra[A_CH], rb[B_CH];
-  const bf16x8 zero8 = {};
-
-  auto load_global = [&](int kt) {
+  auto issue_loads = [&](int kt, int stage) {
     const int k0 = kt * KT;
+    const i32x4 ra = make_rsrc(a_base + kt * a_step, a_total - kt * a_step);
+    const i32x4 rb = make_rsrc(b_base + kt * b_step, b_total - kt * b_step);
+    char* sa = smem + stage * STAGE;
+    char* sb = sa + A_BYTES;
 #pragma unroll
-    for (int p = 0; p < A_CH; ++p) {
-      const int k = k0 + a_k[p];
-      const int64_t off = AK ? (int64_t)k0 : (int64_t)k0 * g.lda;
-      ra[p] = (a_ok[p] && k < g.K) ? *(const bf16x8*)(a_ptr[p] + off) : zero8;
+    for (int j = 0; j < A_INS; ++j) {
+      const int off = (AK && k0 + a_kc[j] >= g.K) ? OOB : a_off[j];
+      llvm_amdgcn_raw_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) unsigned*)(sa + (wave * A_INS + j) * 1024), 16, off, 0, 0, 0);
     }
 #pragma unroll
-    for (int p = 0; p < B_CH; ++p) {
-      const int k = k0 + b_k[p];
-      const int64_t off = BKC ? (int64_t)k0 : (int64_t)k0 * g.ldb;
-      rb[p] = (b_ok[p] && k < g.K) ? *(const bf16x8*)(b_ptr[p] + off) : zero8;
+    for (int j = 0; j < B_INS; ++j) {
+      const int off = (BKC && k0 + b_kc[j] >= g.K) ? OOB : b_off[j];
+      llvm_amdgcn_raw_buffer_load_lds(
+          rb, (__attribute__((address_space(3))) unsigned*)(sb + (wave * B_INS + j) * 1024), 16, off, 0, 0, 0);
     }
   };
-  auto store_lds = [&](int stage) {
-    bf16* As = smem + stage * STAGE;
-    bf16* Bs = As + A_ELEMS;
+
+  // Lane -> LDS read coordinates.
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int kswz = (l32 >> 1) & 7;             // K-contig slot swizzle of this lane's row
+  const int grp = lane >> 4, i16 = lane & 15;  // transpose read: 16-lane group, lane in it
+  const int tr_row = 8 * (grp >> 1) + (i16 >> 2);
+  const int tr_col = 16 * (grp & 1) + 4 * (i16 & 3);
+  const int tr_swz = 2 * ((i16 >> 2) & 3);
+
+  auto frag_k = [&](const char* panel, int row0, int s) -> bf16x8 {
+    const int r = row0 + l32;
+    const int slot = (2 * s + hi) ^ kswz;
+    return *(const bf16x8*)(panel + r * 128 + slot * 16);
+  };
+  auto frag_mn = [&](const char* panel, int row_bytes, int col0, int s) -> bf16x8 {
+    const int col = col0 + tr_col;
+    const int slot = (col >> 3) ^ tr_swz;
+    const char* p0 = panel + (16 * s + tr_row) * row_bytes + slot * 16 + (col & 7) * 2;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
+    const i16x4 hv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(p0 + 4 * row_bytes));
+    const bf16x4 lo_b = __builtin_bit_cast(bf16x4, lo);
+    const bf16x4 hi_b = __builtin_bit_cast(bf16x4, hv);
+    bf16x8 v;
+    v[0] = lo_b[0]; v[1] = lo_b[1]; v[2] = lo_b[2]; v[3] = lo_b[3];
+    v[4] = hi_b[0]; v[5] = hi_b[1]; v[6] = hi_b[2]; v[7] = hi_b[3];
+    return v;
+  };
+  auto load_frags = [&](int stage, int s, bf16x8* fa, bf16x8* fb) {
+    const char* sa = smem + stage * STAGE;
+    const char* sb = sa + A_BYTES;
 #pragma unroll
-    for (int p = 0; p < A_CH; ++p) *(bf16x8*)(As + a_lds[p]) = ra[p];
+    for (int i = 0; i < FM; ++i)
+      fa[i] = AK ? frag_k(sa, wm * WM + 32 * i, s) : frag_mn(sa, BM * 2, wm * WM + 32 * i, s);
 #pragma unroll
-    for (int p = 0; p < B_CH; ++p) *(bf16x8*)(Bs + b_lds[p]) = rb[p];
+    for (int j = 0; j < FN; ++j)
+      fb[j] = BKC ? frag_k(sb, wn * WN + 32 * j, s) : frag_mn(sb, BN * 2, wn * WN + 32 * j, s);
   };
 
   f32x16 acc[FM][FN];
@@ -189,75 +232,33 @@ gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // Lane -> operand coordinates inside a 32-wide MFMA block.
-  const int l32 = lane & 31;
-  const int khalf = (lane >> 5) * 8;          // K-contig: k offset of this lane's 8 values
-  const int grp = lane >> 4, i16 = lane & 15; // transpose read: 16-lane group and lane in it
-  const int tr_k = 8 * (grp >> 1) + (i16 >> 2);
-  const int tr_c = 16 * (grp & 1) + 4 * (i16 & 3);
-
-  auto read_frag_a = [&](const bf16* As, int i, int s) -> bf16x8 {
-    if (AK) {
-      return *(const bf16x8*)(As + (wm * WM + 32 * i + l32) * A_LD + 16 * s + khalf);
-    } else {
-      const bf16* p0 = As + (16 * s + tr_k) * A_LD + wm * WM + 32 * i + tr_c;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(p0 + 4 * A_LD));
-      bf16x8 v;
-      const bf16x4 lo_b = __builtin_bit_cast(bf16x4, lo);
-      const bf16x4 hi_b = __builtin_bit_cast(bf16x4, hi);
-      v[0] = lo_b[0]; v[1] = lo_b[1]; v[2] = lo_b[2]; v[3] = lo_b[3];
-      v[4] = hi_b[0]; v[5] = hi_b[1]; v[6] = hi_b[2]; v[7] = hi_b[3];
-      return v;
-    }
-  };
-  auto read_frag_b = [&](const bf16* Bs, int j, int s) -> bf16x8 {
-    if (BKC) {
-      return *(const bf16x8*)(Bs + (wn * WN + 32 * j + l32) * B_LD + 16 * s + khalf);
-    } else {
-      const bf16* p0 = Bs + (16 * s + tr_k) * B_LD + wn * WN + 32 * j + tr_c;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(p0 + 4 * B_LD));
-      bf16x8 v;
-      const bf16x4 lo_b = __builtin_bit_cast(bf16x4, lo);
-      const bf16x4 hi_b = __builtin_bit_cast(bf16x4, hi);
-      v[0] = lo_b[0]; v[1] = lo_b[1]; v[2] = lo_b[2]; v[3] = lo_b[3];
-      v[4] = hi_b[0]; v[5] = hi_b[1]; v[6] = hi_b[2]; v[7] = hi_b[3];
-      return v;
-    }
-  };
-
   const int nk = (g.K + KT - 1) / KT;
-  load_global(0);
-  store_lds(0);
+  issue_loads(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   __syncthreads();
 
+  bf16x8 fa[2][FM], fb[2][FN];
+  load_frags(0, 0, fa[0], fb[0]);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) load_global(kt + 1);
-    const bf16* As = smem + cur * STAGE;
-    const bf16* Bs = As + A_ELEMS;
+    if (kt + 1 < nk) issue_loads(kt + 1, cur ^ 1);
 #pragma unroll
     for (int s = 0; s < KT / 16; ++s) {
-      bf16x8 fa[FM], fb[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) fa[i] = read_frag_a(As, i, s);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) fb[j] = read_frag_b(Bs, j, s);
+      const int b = s & 1;
+      if (s + 1 < KT / 16) load_frags(cur, s + 1, fa[b ^ 1], fb[b ^ 1]);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[b][j], fa[b][i], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_lds(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads for the next stage landed
     __syncthreads();
+    if (kt + 1 < nk) load_frags(cur ^ 1, 0, fa[0], fb[0]);
   }
 
   // Epilogue.  Block (i, j), lane: row m = l32, columns 8q + 4*(lane/32) + 0..3.
-  const int col_lane = 4 * (lane >> 5);
+  const int col_lane = 4 * hi;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int m = m0 + wm * WM + 32 * i + l32;
@@ -333,7 +334,8 @@ struct TileChoice { int bm, bn; };
 
 TileChoice choose_tile(int M, int N) {
   static const struct { int bm, bn; double eff; } cand[] = {
-      {256, 256, 1.00}, {256, 128, 0.88}, {128, 256, 0.88}, {128, 128, 0.72}};
+      {256, 256, 1.00}, {256, 192, 0.96}, {192, 256, 0.96}, {256, 128, 0.88}, {128, 256, 0.88},
+      {128, 128, 0.72}};
   double best = 1e300;
   TileChoice pick = {256, 256};
   for (const auto& c : cand) {
@@ -349,6 +351,8 @@ template <bool AK, bool BKC, int EPI>
 hipError_t launch_shape(const GemmArgs& g, hipStream_t s, const char** name) {
   const TileChoice t = choose_tile(g.M, g.N);
   if (t.bm == 256 && t.bn == 256) return launch_tile<256, 256, AK, BKC, EPI>(g, s, name);
+  if (t.bm == 256 && t.bn == 192) return launch_tile<256, 192, AK, BKC, EPI>(g, s, name);
+  if (t.bm == 192 && t.bn == 256) return launch_tile<192, 256, AK, BKC, EPI>(g, s, name);
   if (t.bm == 256 && t.bn == 128) return launch_tile<256, 128, AK, BKC, EPI>(g, s, name);
   if (t.bm == 128 && t.bn == 256) return launch_tile<128, 256, AK, BKC, EPI>(g, s, name);
   return launch_tile<128, 128, AK, BKC, EPI>(g, s, name);
