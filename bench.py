@@ -196,6 +196,9 @@ def main():
     ap.add_argument("--cpu-frac", type=int, default=1, help="oracle sample = 1/N of the tokens")
     ap.add_argument("--part", choices=["all", "mlp", "attn"], default="all",
                     help="run only one part (for profiling runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of this many MiB, three times (a known-size "
+                         "reference for hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -211,6 +214,14 @@ def main():
         import __graft_entry__
         __graft_entry__.build()
     device = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=device)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     shard = Shard(device)
     fn = {"all": shard.step, "mlp": shard.mlp_step, "attn": shard.attn_step}[args.part]
     flops = {"all": shard.flops_mlp + shard.flops_attn, "mlp": shard.flops_mlp, "attn": shard.flops_attn}[args.part]

@@ -72,12 +72,23 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
   tn = in_group / gsize;
 }
 
-// Direct global -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds):
-// lane i's bytes land at lds + 16 i; lanes whose offset is outside the buffer
-// record range write zeros.
-extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(
-    i32x4 rsrc, __attribute__((address_space(3))) unsigned* lds, int size, int voffset, int soffset,
-    int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+// Direct global -> LDS copy of 16 bytes per lane: buffer_load_dwordx4 ... lds.
+// Lane i's 16 bytes land at LDS byte address lds_addr + 16 i (lds_addr goes to
+// M0 and must be wave-uniform); a lane whose offset is outside the buffer's
+// record range writes zeros.  Issued as inline asm so that the compiler does not
+// order every later LDS read behind the copy (it cannot tell which LDS bytes the
+// copy writes); completion is awaited explicitly with vmcnt before the barrier
+// that publishes the stage.  M0 is not used for anything else in these kernels.
+__device__ __forceinline__ void lds_dma16(const i32x4& rsrc, int voffset, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(voffset), "s"(rsrc)
+               : "m0");
+}
+
+__device__ __forceinline__ unsigned lds_address(const void* p) {
+  return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
 
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
   const uint64_t a = (uint64_t)base;
@@ -92,12 +103,20 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
 
 constexpr int OOB = 0x7ffffff0;  // a voffset beyond every record range: the lane reads zeros
 
+template <int COLS>
+__device__ __forceinline__ int mn_swz(int r) {
+  return (COLS * 2) % 256 == 0 ? 4 * (r & 3) : 2 * (r & 3);
+}
+
 // LDS layouts (per stage, no padding; 16-byte chunks permuted by XOR so that the
 // rows a read instruction touches fall in different banks):
 //  * K-contiguous panel [rows][64]: 128-byte rows; chunk c of row r sits in slot
 //    c ^ ((r >> 1) & 7).
 //  * M/N-contiguous panel [64][cols]: rows of 2*cols bytes; chunk c of k-row r sits
-//    in slot c ^ (2 * (r & 3)) (stays inside its aligned group of 8 chunks).
+//    in slot c ^ mn_swz(r): 4 * (r & 3) when a row is a multiple of 256 bytes (the
+//    four k-rows a transpose read touches would otherwise share banks), else
+//    2 * (r & 3) (384-byte rows already alternate bank halves).  Either stays
+//    inside the row.
 template <int BM, int BN, bool AK, bool BKC, int EPI>
 __global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
 gemm_bf16_kernel(GemmArgs g) {
@@ -110,7 +129,11 @@ gemm_bf16_kernel(GemmArgs g) {
   constexpr int FM = WM / 32, FN = WN / 32;
   static_assert(A_INS * 4 * 1024 == A_BYTES && B_INS * 4 * 1024 == B_BYTES, "tile must fill whole loads");
 
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  // The two stages are separate LDS objects so that the compiler can tell the
+  // direct loads into one stage from the operand reads of the other and does not
+  // make those reads wait for the loads.
+  __shared__ __attribute__((aligned(1024))) char smem0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem1[STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -144,7 +167,7 @@ gemm_bf16_kernel(GemmArgs g) {
       a_kc[j] = c * 8;
     } else {
       constexpr int CPR = BM / 8;
-      const int r = q / CPR, s = q % CPR, c = s ^ (2 * (r & 3));
+      const int r = q / CPR, s = q % CPR, c = s ^ mn_swz<BM>(r);
       a_off[j] = (m0 + c * 8 < g.M) ? r * (int)g.lda * 2 + c * 16 : OOB;
       a_kc[j] = 0;
     }
@@ -159,29 +182,29 @@ gemm_bf16_kernel(GemmArgs g) {
       b_kc[j] = c * 8;
     } else {
       constexpr int CPR = BN / 8;
-      const int r = q / CPR, s = q % CPR, c = s ^ (2 * (r & 3));
+      const int r = q / CPR, s = q % CPR, c = s ^ mn_swz<BN>(r);
       b_off[j] = (n0 + c * 8 < g.N) ? r * (int)g.ldb * 2 + c * 16 : OOB;
       b_kc[j] = 0;
     }
   }
 
-  auto issue_loads = [&](int kt, int stage) {
+  auto issue_loads = [&](int kt, char* stage) {
     const int k0 = kt * KT;
     const i32x4 ra = make_rsrc(a_base + kt * a_step, a_total - kt * a_step);
     const i32x4 rb = make_rsrc(b_base + kt * b_step, b_total - kt * b_step);
-    char* sa = smem + stage * STAGE;
+    char* sa = stage;
     char* sb = sa + A_BYTES;
+    const unsigned la = lds_address(sa) + wave * A_INS * 1024;
+    const unsigned lb = lds_address(sb) + wave * B_INS * 1024;
 #pragma unroll
     for (int j = 0; j < A_INS; ++j) {
       const int off = (AK && k0 + a_kc[j] >= g.K) ? OOB : a_off[j];
-      llvm_amdgcn_raw_buffer_load_lds(
-          ra, (__attribute__((address_space(3))) unsigned*)(sa + (wave * A_INS + j) * 1024), 16, off, 0, 0, 0);
+      lds_dma16(ra, off, la + j * 1024);
     }
 #pragma unroll
     for (int j = 0; j < B_INS; ++j) {
       const int off = (BKC && k0 + b_kc[j] >= g.K) ? OOB : b_off[j];
-      llvm_amdgcn_raw_buffer_load_lds(
-          rb, (__attribute__((address_space(3))) unsigned*)(sb + (wave * B_INS + j) * 1024), 16, off, 0, 0, 0);
+      lds_dma16(rb, off, lb + j * 1024);
     }
   };
 
@@ -192,16 +215,17 @@ gemm_bf16_kernel(GemmArgs g) {
   const int grp = lane >> 4, i16 = lane & 15;  // transpose read: 16-lane group, lane in it
   const int tr_row = 8 * (grp >> 1) + (i16 >> 2);
   const int tr_col = 16 * (grp & 1) + 4 * (i16 & 3);
-  const int tr_swz = 2 * ((i16 >> 2) & 3);
+  const int tr_swz_a = mn_swz<BM>(i16 >> 2);
+  const int tr_swz_b = mn_swz<BN>(i16 >> 2);
 
   auto frag_k = [&](const char* panel, int row0, int s) -> bf16x8 {
     const int r = row0 + l32;
     const int slot = (2 * s + hi) ^ kswz;
     return *(const bf16x8*)(panel + r * 128 + slot * 16);
   };
-  auto frag_mn = [&](const char* panel, int row_bytes, int col0, int s) -> bf16x8 {
+  auto frag_mn = [&](const char* panel, int row_bytes, int swz, int col0, int s) -> bf16x8 {
     const int col = col0 + tr_col;
-    const int slot = (col >> 3) ^ tr_swz;
+    const int slot = (col >> 3) ^ swz;
     const char* p0 = panel + (16 * s + tr_row) * row_bytes + slot * 16 + (col & 7) * 2;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
     const i16x4 hv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -213,15 +237,15 @@ gemm_bf16_kernel(GemmArgs g) {
     v[4] = hi_b[0]; v[5] = hi_b[1]; v[6] = hi_b[2]; v[7] = hi_b[3];
     return v;
   };
-  auto load_frags = [&](int stage, int s, bf16x8* fa, bf16x8* fb) {
-    const char* sa = smem + stage * STAGE;
+  auto load_frags = [&](const char* stage, int s, bf16x8* fa, bf16x8* fb) {
+    const char* sa = stage;
     const char* sb = sa + A_BYTES;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      fa[i] = AK ? frag_k(sa, wm * WM + 32 * i, s) : frag_mn(sa, BM * 2, wm * WM + 32 * i, s);
+      fa[i] = AK ? frag_k(sa, wm * WM + 32 * i, s) : frag_mn(sa, BM * 2, tr_swz_a, wm * WM + 32 * i, s);
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      fb[j] = BKC ? frag_k(sb, wn * WN + 32 * j, s) : frag_mn(sb, BN * 2, wn * WN + 32 * j, s);
+      fb[j] = BKC ? frag_k(sb, wn * WN + 32 * j, s) : frag_mn(sb, BN * 2, tr_swz_b, wn * WN + 32 * j, s);
   };
 
   f32x16 acc[FM][FN];
@@ -233,41 +257,79 @@ gemm_bf16_kernel(GemmArgs g) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int nk = (g.K + KT - 1) / KT;
-  issue_loads(0, 0);
+  issue_loads(0, smem0);
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   __syncthreads();
 
+  constexpr int NS = KT / 16;           // 16-wide k slices per stage
+  constexpr int NMF = FM * FN;          // MFMAs per slice
+  constexpr int NDS = FM * (AK ? 1 : 2) + FN * (BKC ? 1 : 2);  // LDS reads per slice
+  constexpr int NVM = A_INS + B_INS;    // direct loads per stage
+  constexpr int LB = (NS - 1) & 1;      // operand buffer of the last slice
+
+  auto mfma_rows = [&](const bf16x8* fa_, const bf16x8* fb_, int i0, int i1) {
+#pragma unroll
+    for (int i = i0; i < i1; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb_[j], fa_[i], acc[i][j], 0, 0, 0);
+  };
+
   bf16x8 fa[2][FM], fb[2][FN];
-  load_frags(0, 0, fa[0], fb[0]);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) issue_loads(kt + 1, cur ^ 1);
+
+  // One K step: MFMAs on `cur` while the next K step's panels stream into `nxt`.
+  auto k_step = [&](const char* cur, char* nxt, int kt) {
+    // Past the last step the loads read only zeros into the idle stage.
+    issue_loads(kt + 1, nxt);
 #pragma unroll
-    for (int s = 0; s < KT / 16; ++s) {
-      const int b = s & 1;
-      if (s + 1 < KT / 16) load_frags(cur, s + 1, fa[b ^ 1], fb[b ^ 1]);
+    for (int s = 0; s < NS - 1; ++s) {
+      load_frags(cur, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+      mfma_rows(fa[s & 1], fb[s & 1], 0, FM);
+      // The next slice's LDS reads go out ahead of this slice's MFMAs; in the
+      // first slice one direct load follows each MFMA.
+      __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[b][j], fa[b][i], acc[i][j], 0, 0, 0);
+      for (int u = 0; u < NMF; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (s == 0 && u < NVM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads for the next stage landed
+    // Last slice: half of its MFMAs, the barrier that publishes the next stage,
+    // then the next stage's first operands are read while the other half runs.
+    mfma_rows(fa[LB], fb[LB], 0, FM / 2);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads into `nxt` landed
     __syncthreads();
-    if (kt + 1 < nk) load_frags(cur ^ 1, 0, fa[0], fb[0]);
+    load_frags(nxt, 0, fa[LB ^ 1], fb[LB ^ 1]);
+    mfma_rows(fa[LB], fb[LB], FM / 2, FM);
+    __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NMF - (FM / 2) * FN, 0);
+  };
+
+  load_frags(smem0, 0, fa[0], fb[0]);
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool odd = kt & 1;
+    k_step(odd ? smem1 : smem0, odd ? smem0 : smem1, kt);
   }
 
   // Epilogue.  Block (i, j), lane: row m = l32, columns 8q + 4*(lane/32) + 0..3.
-  const int col_lane = 4 * hi;
+  // The coordinates are passed through empty asm so that the compiler derives the
+  // epilogue addresses here instead of hoisting them above the K loop, where they
+  // would hold registers for its whole duration.
+  int e_lane = lane, e_m0 = m0, e_n0 = n0, e_wave = wave;
+  asm volatile("" : "+v"(e_lane));
+  asm volatile("" : "+s"(e_m0), "+s"(e_n0), "+s"(e_wave));
+  const int e_l32 = e_lane & 31;
+  const int col_lane = 4 * (e_lane >> 5);
+  const int e_wm = e_wave >> 1, e_wn = e_wave & 1;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * WM + 32 * i + l32;
+    const int m = e_m0 + e_wm * WM + 32 * i + e_l32;
     if (m >= g.M) continue;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * WN + 32 * j + 8 * q + col_lane;
+        const int n = e_n0 + e_wn * WN + 32 * j + 8 * q + col_lane;
         if (n >= g.N) continue;
         float v[4] = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                       acc[i][j][4 * q + 3]};
