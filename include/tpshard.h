@@ -29,7 +29,8 @@
  *   The shard width is N/p (column) or K/p (row) and must be an integer
  *   (TP_ERR_TP_DIVISIBILITY).  T >= 1 is arbitrary; every feature dimension
  *   (K, N, and their shard widths) must be a positive multiple of 8
- *   (TP_ERR_ALIGNMENT), and every dimension must be <= 2^30 (TP_ERR_DIM).
+ *   (TP_ERR_ALIGNMENT) and at most 2^21 (TP_ERR_DIM); T must be <= 2^30
+ *   (TP_ERR_DIM).
  * Dtypes.  dtype = TP_BF16: activations, weights, biases and activation
  *   outputs are bfloat16; products accumulate in fp32 on the matrix cores
  *   and are rounded to nearest-even on store.  dtype = TP_FP32: everything is
@@ -67,7 +68,7 @@ typedef enum { TP_ACT_NONE = 0, TP_ACT_GELU = 1 } tp_act;
 enum {
   TP_OK = 0,
   TP_ERR_NULLPTR = -1,          /* a required pointer is NULL */
-  TP_ERR_DIM = -2,              /* a dimension is < 1 or > 2^30 */
+  TP_ERR_DIM = -2,              /* a dimension is < 1 or too large (T > 2^30, feature > 2^21) */
   TP_ERR_TP_DIVISIBILITY = -3,  /* tp_size < 1 or the sharded dimension not divisible by it */
   TP_ERR_ALIGNMENT = -4,        /* pointer not 16-byte aligned or feature dim not a multiple of 8 */
   TP_ERR_DTYPE = -5,            /* unknown dtype or activation code */

@@ -16,7 +16,8 @@
 namespace tps {
 namespace {
 
-constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kMaxDim = int64_t(1) << 30;      // tokens
+constexpr int64_t kMaxFeature = int64_t(1) << 21;  // in/out features (and their shards)
 constexpr int64_t kMaxElems = int64_t(1) << 36;
 constexpr size_t kAlign = 256;  // workspace sub-buffer alignment
 
@@ -51,8 +52,10 @@ int check_elems(std::initializer_list<std::pair<int64_t, int64_t>> mats) {
 }
 
 int check_feature(std::initializer_list<int64_t> dims) {
-  for (int64_t d : dims)
+  for (int64_t d : dims) {
+    if (d > kMaxFeature) return TP_ERR_DIM;
     if (d % 8 != 0) return TP_ERR_ALIGNMENT;
+  }
   return TP_OK;
 }
 

@@ -36,8 +36,7 @@
 namespace tps {
 namespace {
 
-constexpr int KT = 64;        // K step per LDS stage
-constexpr int NT = 256;       // threads per workgroup (4 waves)
+constexpr int KT = 32;        // K step per LDS stage
 constexpr int GROUP_M = 8;    // tile rows per group in the tile order
 
 __device__ __forceinline__ float gelu_f(float z) {
@@ -80,7 +79,8 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 // copy writes); completion is awaited explicitly with vmcnt before the barrier
 // that publishes the stage.  M0 is not used for anything else in these kernels.
 __device__ __forceinline__ void lds_dma16(const i32x4& rsrc, int voffset, unsigned lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  // One wait state between the M0 write and the LDS-DMA that reads it.
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(lds_addr), "v"(voffset), "s"(rsrc)
                : "m0");
@@ -92,7 +92,10 @@ __device__ __forceinline__ unsigned lds_address(const void* p) {
 
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
   const uint64_t a = (uint64_t)base;
-  const int64_t n = bytes < 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  // The record count is capped at 1 GiB: every in-range offset of one K step is
+  // below that (feature dimensions are at most 2^21), and the OOB offset above it
+  // then always fails the range check, dword by dword.
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0x40000000 ? 0x40000000 : bytes);
   i32x4 r;
   r[0] = __builtin_amdgcn_readfirstlane((int)(a & 0xffffffffu));
   r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff));
@@ -110,36 +113,66 @@ __device__ __forceinline__ int mn_swz(int r) {
 
 // LDS layouts (per stage, no padding; 16-byte chunks permuted by XOR so that the
 // rows a read instruction touches fall in different banks):
-//  * K-contiguous panel [rows][64]: 128-byte rows; chunk c of row r sits in slot
-//    c ^ ((r >> 1) & 7).
-//  * M/N-contiguous panel [64][cols]: rows of 2*cols bytes; chunk c of k-row r sits
+//  * K-contiguous panel [rows][32]: 64-byte rows of 4 chunks; chunk c of row r
+//    sits in slot c ^ ((r >> 2) & 3).
+//  * M/N-contiguous panel [32][cols]: rows of 2*cols bytes; chunk c of k-row r sits
 //    in slot c ^ mn_swz(r): 4 * (r & 3) when a row is a multiple of 256 bytes (the
 //    four k-rows a transpose read touches would otherwise share banks), else
 //    2 * (r & 3) (384-byte rows already alternate bank halves).  Either stays
 //    inside the row.
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int waitcnt_vm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+
+template <int BM, int BN>
+struct StageCfg {
+  static constexpr int BYTES = (BM + BN) * KT * 2;
+  static constexpr int N = (163840 / BYTES) < 5 ? (163840 / BYTES) : 5;  // LDS stages (<= 160 KiB)
+};
+
+// Wave roles.  A workgroup has 12 waves, 3 per SIMD: 8 consumer waves that read
+// operands from LDS and issue the MFMAs (2 per SIMD, so one covers the other's
+// LDS waits), and 4 producer waves that only issue the HBM -> LDS copies.  A
+// copy instruction holds up its wave's instruction issue for tens of cycles;
+// keeping them off the MFMA waves keeps the matrix pipe fed.
+constexpr int N_CONS = 8;
+constexpr int N_PROD = 4;
+constexpr int NT_WS = 64 * (N_CONS + N_PROD);
+
+// Consumer grid over the tile: CM x CN waves of (BM/CM) x (BN/CN) outputs.
+template <int BM, int BN>
+struct ConsCfg {
+  static constexpr int CM = BM >= 256 ? 4 : 2;
+  static constexpr int CN = N_CONS / CM;
+  static constexpr int WM = BM / CM, WN = BN / CN;
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "consumer tile must be whole 32x32 blocks");
+};
+
 template <int BM, int BN, bool AK, bool BKC, int EPI>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(NT_WS, NT_WS), amdgpu_waves_per_eu(3, 3)))
 gemm_bf16_kernel(GemmArgs g) {
   constexpr int A_BYTES = BM * KT * 2;
   constexpr int B_BYTES = BN * KT * 2;
   constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int A_INS = A_BYTES / 1024 / 4;  // 1 KiB direct-load instructions per wave per stage
-  constexpr int B_INS = B_BYTES / 1024 / 4;
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int NSTAGE = StageCfg<BM, BN>::N;
+  constexpr int A_INS = A_BYTES / 1024 / N_PROD;  // 1 KiB copies per producer wave per stage
+  constexpr int B_INS = B_BYTES / 1024 / N_PROD;
+  constexpr int NVM = A_INS + B_INS;
+  constexpr int WM = ConsCfg<BM, BN>::WM, WN = ConsCfg<BM, BN>::WN, CN = ConsCfg<BM, BN>::CN;
   constexpr int FM = WM / 32, FN = WN / 32;
-  static_assert(A_INS * 4 * 1024 == A_BYTES && B_INS * 4 * 1024 == B_BYTES, "tile must fill whole loads");
+  constexpr int KROW = KT * 2;               // bytes per row of a K-contiguous panel
+  constexpr int KCH = KT / 8;                // 16-byte chunks per such row
+  constexpr int PREF = NSTAGE - 1;           // K steps in flight ahead of the one computed
+  static_assert(A_INS * N_PROD * 1024 == A_BYTES && B_INS * N_PROD * 1024 == B_BYTES, "whole copies");
+  static_assert(NSTAGE >= 3, "need at least three stages");
+  static_assert((PREF - 1) * NVM <= 63, "vmcnt range");
 
-  // The two stages are separate LDS objects so that the compiler can tell the
-  // direct loads into one stage from the operand reads of the other and does not
-  // make those reads wait for the loads.
-  __shared__ __attribute__((aligned(1024))) char smem0[STAGE];
-  __shared__ __attribute__((aligned(1024))) char smem1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
 
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = (g.N + BN - 1) / BN;
@@ -147,71 +180,83 @@ gemm_bf16_kernel(GemmArgs g) {
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM;
   const int n0 = tn * BN;
+  const int nk = (g.K + KT - 1) / KT;
 
-  // Tile origins in memory and the bytes from there to the end of each matrix.
-  const char* a_base = (const char*)g.A + 2 * (AK ? (int64_t)m0 * g.lda : (int64_t)m0);
-  const char* b_base = (const char*)g.B + 2 * (BKC ? (int64_t)n0 * g.ldb : (int64_t)n0);
-  const int64_t a_total = 2 * ((AK ? (int64_t)g.M : (int64_t)g.K) * g.lda - (AK ? (int64_t)m0 * g.lda : m0));
-  const int64_t b_total = 2 * ((BKC ? (int64_t)g.N : (int64_t)g.K) * g.ldb - (BKC ? (int64_t)n0 * g.ldb : n0));
-  const int64_t a_step = AK ? 2 * KT : 2 * (int64_t)KT * g.lda;
-  const int64_t b_step = BKC ? 2 * KT : 2 * (int64_t)KT * g.ldb;
+  if (wave >= N_CONS) {
+    // ------------------------------------------------------------ producer
+    const int pw = wave - N_CONS;
+    const char* a_base = (const char*)g.A + 2 * (AK ? (int64_t)m0 * g.lda : (int64_t)m0);
+    const char* b_base = (const char*)g.B + 2 * (BKC ? (int64_t)n0 * g.ldb : (int64_t)n0);
+    const int64_t a_total = 2 * ((AK ? (int64_t)g.M : (int64_t)g.K) * g.lda - (AK ? (int64_t)m0 * g.lda : m0));
+    const int64_t b_total = 2 * ((BKC ? (int64_t)g.N : (int64_t)g.K) * g.ldb - (BKC ? (int64_t)n0 * g.ldb : n0));
+    const int64_t a_step = AK ? 2 * KT : 2 * (int64_t)KT * g.lda;
+    const int64_t b_step = BKC ? 2 * KT : 2 * (int64_t)KT * g.ldb;
 
-  // Per-lane byte offsets of each direct load inside the tile at the current K step.
-  int a_off[A_INS], a_kc[A_INS];
-#pragma unroll
-  for (int j = 0; j < A_INS; ++j) {
-    const int q = (wave * A_INS + j) * 64 + lane;  // 16-byte chunk index in the stage's A panel
-    if (AK) {
-      const int r = q >> 3, s = q & 7, c = s ^ ((r >> 1) & 7);
-      a_off[j] = r * (int)g.lda * 2 + c * 16;
-      a_kc[j] = c * 8;
-    } else {
-      constexpr int CPR = BM / 8;
-      const int r = q / CPR, s = q % CPR, c = s ^ mn_swz<BM>(r);
-      a_off[j] = (m0 + c * 8 < g.M) ? r * (int)g.lda * 2 + c * 16 : OOB;
-      a_kc[j] = 0;
-    }
-  }
-  int b_off[B_INS], b_kc[B_INS];
-#pragma unroll
-  for (int j = 0; j < B_INS; ++j) {
-    const int q = (wave * B_INS + j) * 64 + lane;
-    if (BKC) {
-      const int r = q >> 3, s = q & 7, c = s ^ ((r >> 1) & 7);
-      b_off[j] = r * (int)g.ldb * 2 + c * 16;
-      b_kc[j] = c * 8;
-    } else {
-      constexpr int CPR = BN / 8;
-      const int r = q / CPR, s = q % CPR, c = s ^ mn_swz<BN>(r);
-      b_off[j] = (n0 + c * 8 < g.N) ? r * (int)g.ldb * 2 + c * 16 : OOB;
-      b_kc[j] = 0;
-    }
-  }
-
-  auto issue_loads = [&](int kt, char* stage) {
-    const int k0 = kt * KT;
-    const i32x4 ra = make_rsrc(a_base + kt * a_step, a_total - kt * a_step);
-    const i32x4 rb = make_rsrc(b_base + kt * b_step, b_total - kt * b_step);
-    char* sa = stage;
-    char* sb = sa + A_BYTES;
-    const unsigned la = lds_address(sa) + wave * A_INS * 1024;
-    const unsigned lb = lds_address(sb) + wave * B_INS * 1024;
+    // Per-lane byte offsets of each copy inside the tile at the current K step.
+    int a_off[A_INS], a_kc[A_INS];
 #pragma unroll
     for (int j = 0; j < A_INS; ++j) {
-      const int off = (AK && k0 + a_kc[j] >= g.K) ? OOB : a_off[j];
-      lds_dma16(ra, off, la + j * 1024);
+      const int q = (pw * A_INS + j) * 64 + lane;  // 16-byte chunk index in the stage's A panel
+      if (AK) {
+        const int r = q / KCH, sl = q % KCH, c = sl ^ ((r >> 2) & 3);
+        a_off[j] = r * (int)g.lda * 2 + c * 16;
+        a_kc[j] = c * 8;
+      } else {
+        constexpr int CPR = BM / 8;
+        const int r = q / CPR, sl = q % CPR, c = sl ^ mn_swz<BM>(r);
+        a_off[j] = (m0 + c * 8 < g.M) ? r * (int)g.lda * 2 + c * 16 : OOB;
+        a_kc[j] = 0;
+      }
     }
+    int b_off[B_INS], b_kc[B_INS];
 #pragma unroll
     for (int j = 0; j < B_INS; ++j) {
-      const int off = (BKC && k0 + b_kc[j] >= g.K) ? OOB : b_off[j];
-      lds_dma16(rb, off, lb + j * 1024);
+      const int q = (pw * B_INS + j) * 64 + lane;
+      if (BKC) {
+        const int r = q / KCH, sl = q % KCH, c = sl ^ ((r >> 2) & 3);
+        b_off[j] = r * (int)g.ldb * 2 + c * 16;
+        b_kc[j] = c * 8;
+      } else {
+        constexpr int CPR = BN / 8;
+        const int r = q / CPR, sl = q % CPR, c = sl ^ mn_swz<BN>(r);
+        b_off[j] = (n0 + c * 8 < g.N) ? r * (int)g.ldb * 2 + c * 16 : OOB;
+        b_kc[j] = 0;
+      }
     }
-  };
+    const unsigned smem_addr = lds_address(smem);
+    // All copies of K step kt into LDS stage kt % NSTAGE (past the last step the
+    // copies read only zeros into a stage that is not used again).
+    auto issue_step = [&](int kt) {
+      const int k0 = kt * KT;
+      const unsigned st = smem_addr + (unsigned)((kt % NSTAGE) * STAGE);
+      const i32x4 ra = make_rsrc(a_base + kt * a_step, a_total - kt * a_step);
+      const i32x4 rb = make_rsrc(b_base + kt * b_step, b_total - kt * b_step);
+#pragma unroll
+      for (int j = 0; j < A_INS; ++j)
+        lds_dma16(ra, (AK && k0 + a_kc[j] >= g.K) ? OOB : a_off[j], st + (pw * A_INS + j) * 1024);
+#pragma unroll
+      for (int j = 0; j < B_INS; ++j)
+        lds_dma16(rb, (BKC && k0 + b_kc[j] >= g.K) ? OOB : b_off[j], st + A_BYTES + (pw * B_INS + j) * 1024);
+    };
+#pragma unroll
+    for (int p = 0; p < PREF; ++p) issue_step(p);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step 0 landed
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      issue_step(kt + PREF);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step kt+1 landed
+      __syncthreads();
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no copy into this workgroup's LDS outlives it
+    return;
+  }
 
-  // Lane -> LDS read coordinates.
+  // -------------------------------------------------------------- consumer
+  const int wm = wave / CN;
+  const int wn = wave % CN;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int kswz = (l32 >> 1) & 7;             // K-contig slot swizzle of this lane's row
+  const int kswz = (l32 >> 2) & 3;             // K-contig slot swizzle of this lane's row
   const int grp = lane >> 4, i16 = lane & 15;  // transpose read: 16-lane group, lane in it
   const int tr_row = 8 * (grp >> 1) + (i16 >> 2);
   const int tr_col = 16 * (grp & 1) + 4 * (i16 & 3);
@@ -221,7 +266,7 @@ gemm_bf16_kernel(GemmArgs g) {
   auto frag_k = [&](const char* panel, int row0, int s) -> bf16x8 {
     const int r = row0 + l32;
     const int slot = (2 * s + hi) ^ kswz;
-    return *(const bf16x8*)(panel + r * 128 + slot * 16);
+    return *(const bf16x8*)(panel + r * KROW + slot * 16);
   };
   auto frag_mn = [&](const char* panel, int row_bytes, int swz, int col0, int s) -> bf16x8 {
     const int col = col0 + tr_col;
@@ -237,8 +282,8 @@ gemm_bf16_kernel(GemmArgs g) {
     v[4] = hi_b[0]; v[5] = hi_b[1]; v[6] = hi_b[2]; v[7] = hi_b[3];
     return v;
   };
-  auto load_frags = [&](const char* stage, int s, bf16x8* fa, bf16x8* fb) {
-    const char* sa = stage;
+  auto load_frags = [&](int kt, int s, bf16x8* fa, bf16x8* fb) {
+    const char* sa = smem + (kt % NSTAGE) * STAGE;
     const char* sb = sa + A_BYTES;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -256,17 +301,9 @@ gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = (g.K + KT - 1) / KT;
-  issue_loads(0, smem0);
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-  __syncthreads();
-
   constexpr int NS = KT / 16;           // 16-wide k slices per stage
-  constexpr int NMF = FM * FN;          // MFMAs per slice
-  constexpr int NDS = FM * (AK ? 1 : 2) + FN * (BKC ? 1 : 2);  // LDS reads per slice
-  constexpr int NVM = A_INS + B_INS;    // direct loads per stage
   constexpr int LB = (NS - 1) & 1;      // operand buffer of the last slice
-
+  constexpr int FM_HALF = FM / 2 > 0 ? FM / 2 : 1;
   auto mfma_rows = [&](const bf16x8* fa_, const bf16x8* fb_, int i0, int i1) {
 #pragma unroll
     for (int i = i0; i < i1; ++i)
@@ -275,40 +312,22 @@ gemm_bf16_kernel(GemmArgs g) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb_[j], fa_[i], acc[i][j], 0, 0, 0);
   };
 
+  __syncthreads();  // step 0 is in LDS
   bf16x8 fa[2][FM], fb[2][FN];
-
-  // One K step: MFMAs on `cur` while the next K step's panels stream into `nxt`.
-  auto k_step = [&](const char* cur, char* nxt, int kt) {
-    // Past the last step the loads read only zeros into the idle stage.
-    issue_loads(kt + 1, nxt);
+  load_frags(0, 0, fa[0], fb[0]);
+  for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s) {
-      load_frags(cur, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+      load_frags(kt, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
       mfma_rows(fa[s & 1], fb[s & 1], 0, FM);
-      // The next slice's LDS reads go out ahead of this slice's MFMAs; in the
-      // first slice one direct load follows each MFMA.
-      __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
-#pragma unroll
-      for (int u = 0; u < NMF; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (s == 0 && u < NVM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
     }
-    // Last slice: half of its MFMAs, the barrier that publishes the next stage,
-    // then the next stage's first operands are read while the other half runs.
-    mfma_rows(fa[LB], fb[LB], 0, FM / 2);
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads into `nxt` landed
+    // Last slice: part of its MFMAs, the barrier that publishes step kt+1 (and
+    // releases step kt's stage to the producers), then step kt+1's first
+    // operands are read while the rest run.
+    mfma_rows(fa[LB], fb[LB], 0, FM_HALF);
     __syncthreads();
-    load_frags(nxt, 0, fa[LB ^ 1], fb[LB ^ 1]);
-    mfma_rows(fa[LB], fb[LB], FM / 2, FM);
-    __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, NMF - (FM / 2) * FN, 0);
-  };
-
-  load_frags(smem0, 0, fa[0], fb[0]);
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool odd = kt & 1;
-    k_step(odd ? smem1 : smem0, odd ? smem0 : smem1, kt);
+    load_frags(kt + 1, 0, fa[LB ^ 1], fb[LB ^ 1]);
+    mfma_rows(fa[LB], fb[LB], FM_HALF, FM);
   }
 
   // Epilogue.  Block (i, j), lane: row m = l32, columns 8q + 4*(lane/32) + 0..3.
@@ -320,7 +339,7 @@ gemm_bf16_kernel(GemmArgs g) {
   asm volatile("" : "+s"(e_m0), "+s"(e_n0), "+s"(e_wave));
   const int e_l32 = e_lane & 31;
   const int col_lane = 4 * (e_lane >> 5);
-  const int e_wm = e_wave >> 1, e_wn = e_wave & 1;
+  const int e_wm = e_wave / CN, e_wn = e_wave % CN;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int m = e_m0 + e_wm * WM + 32 * i + e_l32;
@@ -385,7 +404,7 @@ template <int BM, int BN, bool AK, bool BKC, int EPI>
 hipError_t launch_tile(const GemmArgs& g, hipStream_t s, const char** name) {
   *name = kname<BM, BN, AK, BKC, EPI>();
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, AK, BKC, EPI>), dim3(tiles), dim3(NT), 0, s, g);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, AK, BKC, EPI>), dim3(tiles), dim3(NT_WS), 0, s, g);
   return hipGetLastError();
 }
 
@@ -396,10 +415,9 @@ struct TileChoice { int bm, bn; };
 
 TileChoice choose_tile(int M, int N) {
   static const struct { int bm, bn; double eff; } cand[] = {
-      {256, 256, 1.00}, {256, 192, 0.96}, {192, 256, 0.96}, {256, 128, 0.88}, {128, 256, 0.88},
-      {128, 128, 0.72}};
+      {256, 192, 1.00}, {192, 256, 1.00}, {256, 128, 0.92}, {128, 256, 0.92}, {128, 128, 0.75}};
   double best = 1e300;
-  TileChoice pick = {256, 256};
+  TileChoice pick = {256, 192};
   for (const auto& c : cand) {
     const long tiles = (long)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
     const long waves = (tiles + 255) / 256;
@@ -412,7 +430,6 @@ TileChoice choose_tile(int M, int N) {
 template <bool AK, bool BKC, int EPI>
 hipError_t launch_shape(const GemmArgs& g, hipStream_t s, const char** name) {
   const TileChoice t = choose_tile(g.M, g.N);
-  if (t.bm == 256 && t.bn == 256) return launch_tile<256, 256, AK, BKC, EPI>(g, s, name);
   if (t.bm == 256 && t.bn == 192) return launch_tile<256, 192, AK, BKC, EPI>(g, s, name);
   if (t.bm == 192 && t.bn == 256) return launch_tile<192, 256, AK, BKC, EPI>(g, s, name);
   if (t.bm == 256 && t.bn == 128) return launch_tile<256, 128, AK, BKC, EPI>(g, s, name);

@@ -69,6 +69,7 @@ def test_column_linear_validation(lib):
     assert f(A0, A1, None, A2, None, 0, 256, 1024, 2, 0, 0, S) == -2
     assert f(A0, A1, None, A2, None, 128, -8, 1024, 2, 0, 0, S) == -2
     assert f(A0, A1, None, A2, None, 1 << 31, 256, 1024, 2, 0, 0, S) == -2
+    assert f(A0, A1, None, A2, None, 128, 1 << 22, 1024, 2, 0, 0, S) == -2     # feature dim > 2^21
     # TP divisibility
     assert f(A0, A1, None, A2, None, 128, 256, 1000, 3, 0, 0, S) == -3
     assert f(A0, A1, None, A2, None, 128, 256, 1024, 0, 0, 0, S) == -3
