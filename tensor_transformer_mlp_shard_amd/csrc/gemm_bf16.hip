@@ -5,14 +5,23 @@
 // registers before the only store (bias, bias + exact-erf GeLU with the
 // pre-activation saved, GeLU' for the backward, or fp32 store / accumulate).
 //
-// Tiling.  A workgroup of 4 waves (2 x 2) owns a BM x BN tile of C; each wave a
-// (BM/2) x (BN/2) sub-tile of 32 x 32 MFMA blocks whose fp32 accumulators stay in
-// the AGPR file for the whole K loop.  The K loop steps by 64 through two LDS
-// stages: while the matrix cores work on one stage, the next A and B panels are
-// copied HBM -> LDS by buffer_load_dwordx4 ... lds (no register staging; rows and
-// columns outside the matrix read as zero through the buffer range check).  The
-// MFMA operands of the next 16-wide k slice are read from LDS while the current
-// slice's MFMAs issue (register double buffer).
+// Data path.  A workgroup owns a BM x BN tile of C.  The K loop walks K in steps
+// of 32 through a ring of up to five LDS stages: each step's A and B panels are
+// copied HBM -> LDS by buffer_load_dwordx4 ... lds (no register staging; rows
+// and columns outside the matrix read as zero through the buffer range check)
+// several steps ahead of the step the matrix cores work on.  Consumer waves
+// read their MFMA operands from LDS and keep their fp32 accumulators in
+// registers for the whole K loop.
+//
+// Wave organisation.  A copy instruction holds up its wave's instruction issue
+// for tens of cycles, so a SIMD needs a second wave to keep the matrix pipe fed:
+//  * "split" kernels (tiles up to 256 x 192): 8 consumer waves (2 per SIMD) and
+//    4 producer waves that only issue the copies;
+//  * "shared" kernels (256 x 384 and 384 x 256): 8 waves, each a consumer of a
+//    128 x 96 (or 96 x 128) sub-tile that also issues 1/8 of the copies; the
+//    bigger tile moves 29% fewer bytes per FLOP from L2 and reads 31% fewer
+//    operand bytes from LDS, which matters because the chip runs at its power
+//    limit and data movement lowers the clock.
 //
 // Layouts.  Each operand is kept in LDS in its memory orientation:
 //  * K-contiguous panels (rows of A, or rows of B stored as [N x K]): a lane's
@@ -125,150 +134,119 @@ __device__ __forceinline__ int mn_swz(int r) {
 // outstanding (expcnt and lgkmcnt left at their maxima).
 constexpr int waitcnt_vm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
 
-template <int BM, int BN>
-struct StageCfg {
-  static constexpr int BYTES = (BM + BN) * KT * 2;
-  static constexpr int N = (163840 / BYTES) < 5 ? (163840 / BYTES) : 5;  // LDS stages (<= 160 KiB)
-};
-
-// Wave roles.  A workgroup has 12 waves, 3 per SIMD: 8 consumer waves that read
-// operands from LDS and issue the MFMAs (2 per SIMD, so one covers the other's
-// LDS waits), and 4 producer waves that only issue the HBM -> LDS copies.  A
-// copy instruction holds up its wave's instruction issue for tens of cycles;
-// keeping them off the MFMA waves keeps the matrix pipe fed.
-constexpr int N_CONS = 8;
-constexpr int N_PROD = 4;
-constexpr int NT_WS = 64 * (N_CONS + N_PROD);
-
-// Consumer grid over the tile: CM x CN waves of (BM/CM) x (BN/CN) outputs.
-template <int BM, int BN>
-struct ConsCfg {
-  static constexpr int CM = BM >= 256 ? 4 : 2;
-  static constexpr int CN = N_CONS / CM;
+// Kernel shape: tile, waves and their roles, LDS ring.
+template <int BM_, int BN_, int NPROD_, int CM_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int NCONS = 8, NPROD = NPROD_, NW = NCONS + NPROD, NT = 64 * NW;
+  static constexpr int CM = CM_, CN = NCONS / CM_;
   static constexpr int WM = BM / CM, WN = BN / CN;
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int A_BYTES = BM * KT * 2, B_BYTES = BN * KT * 2, STAGE = A_BYTES + B_BYTES;
+  static constexpr int NSTAGE = (163840 / STAGE) < 5 ? (163840 / STAGE) : 5;  // <= 160 KiB of LDS
+  static constexpr int PREF = NSTAGE - 1;       // K steps in flight ahead of the one computed
+  static constexpr int NCOPY = NPROD > 0 ? NPROD : NCONS;  // waves that issue the copies
+  static constexpr int A_INS = A_BYTES / 1024 / NCOPY, B_INS = B_BYTES / 1024 / NCOPY;
+  static constexpr int NVM = A_INS + B_INS;    // 1 KiB copies per copying wave per step
+  static constexpr int WAVES_PER_EU = (NW + 3) / 4;
+  static constexpr bool DBUF = NPROD > 0;       // double-buffered operands (register budget)
   static_assert(WM % 32 == 0 && WN % 32 == 0, "consumer tile must be whole 32x32 blocks");
-};
-
-template <int BM, int BN, bool AK, bool BKC, int EPI>
-__global__ void __attribute__((amdgpu_flat_work_group_size(NT_WS, NT_WS), amdgpu_waves_per_eu(3, 3)))
-gemm_bf16_kernel(GemmArgs g) {
-  constexpr int A_BYTES = BM * KT * 2;
-  constexpr int B_BYTES = BN * KT * 2;
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int NSTAGE = StageCfg<BM, BN>::N;
-  constexpr int A_INS = A_BYTES / 1024 / N_PROD;  // 1 KiB copies per producer wave per stage
-  constexpr int B_INS = B_BYTES / 1024 / N_PROD;
-  constexpr int NVM = A_INS + B_INS;
-  constexpr int WM = ConsCfg<BM, BN>::WM, WN = ConsCfg<BM, BN>::WN, CN = ConsCfg<BM, BN>::CN;
-  constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int KROW = KT * 2;               // bytes per row of a K-contiguous panel
-  constexpr int KCH = KT / 8;                // 16-byte chunks per such row
-  constexpr int PREF = NSTAGE - 1;           // K steps in flight ahead of the one computed
-  static_assert(A_INS * N_PROD * 1024 == A_BYTES && B_INS * N_PROD * 1024 == B_BYTES, "whole copies");
+  static_assert(A_INS * NCOPY * 1024 == A_BYTES && B_INS * NCOPY * 1024 == B_BYTES, "whole copies");
   static_assert(NSTAGE >= 3, "need at least three stages");
   static_assert((PREF - 1) * NVM <= 63, "vmcnt range");
+};
 
-  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+// One copying wave's share of every K step's copies.
+template <class C, bool AK, bool BKC>
+struct Copier {
+  const char* a_base;
+  const char* b_base;
+  int64_t a_total, b_total, a_step, b_step;
+  int a_off[C::A_INS], a_kc[C::A_INS], b_off[C::B_INS], b_kc[C::B_INS];
+  unsigned smem_addr;
+  int cw, K;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-  const int tiles_m = (g.M + BM - 1) / BM;
-  const int tiles_n = (g.N + BN - 1) / BN;
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM;
-  const int n0 = tn * BN;
-  const int nk = (g.K + KT - 1) / KT;
-
-  if (wave >= N_CONS) {
-    // ------------------------------------------------------------ producer
-    const int pw = wave - N_CONS;
-    const char* a_base = (const char*)g.A + 2 * (AK ? (int64_t)m0 * g.lda : (int64_t)m0);
-    const char* b_base = (const char*)g.B + 2 * (BKC ? (int64_t)n0 * g.ldb : (int64_t)n0);
-    const int64_t a_total = 2 * ((AK ? (int64_t)g.M : (int64_t)g.K) * g.lda - (AK ? (int64_t)m0 * g.lda : m0));
-    const int64_t b_total = 2 * ((BKC ? (int64_t)g.N : (int64_t)g.K) * g.ldb - (BKC ? (int64_t)n0 * g.ldb : n0));
-    const int64_t a_step = AK ? 2 * KT : 2 * (int64_t)KT * g.lda;
-    const int64_t b_step = BKC ? 2 * KT : 2 * (int64_t)KT * g.ldb;
-
-    // Per-lane byte offsets of each copy inside the tile at the current K step.
-    int a_off[A_INS], a_kc[A_INS];
+  __device__ __forceinline__ void init(const GemmArgs& g, int m0, int n0, int cw_, int lane, const char* smem) {
+    constexpr int KCH = KT / 8;  // 16-byte chunks per row of a K-contiguous panel
+    cw = cw_;
+    K = g.K;
+    a_base = (const char*)g.A + 2 * (AK ? (int64_t)m0 * g.lda : (int64_t)m0);
+    b_base = (const char*)g.B + 2 * (BKC ? (int64_t)n0 * g.ldb : (int64_t)n0);
+    a_total = 2 * ((AK ? (int64_t)g.M : (int64_t)g.K) * g.lda - (AK ? (int64_t)m0 * g.lda : m0));
+    b_total = 2 * ((BKC ? (int64_t)g.N : (int64_t)g.K) * g.ldb - (BKC ? (int64_t)n0 * g.ldb : n0));
+    a_step = AK ? 2 * KT : 2 * (int64_t)KT * g.lda;
+    b_step = BKC ? 2 * KT : 2 * (int64_t)KT * g.ldb;
 #pragma unroll
-    for (int j = 0; j < A_INS; ++j) {
-      const int q = (pw * A_INS + j) * 64 + lane;  // 16-byte chunk index in the stage's A panel
+    for (int j = 0; j < C::A_INS; ++j) {
+      const int q = (cw * C::A_INS + j) * 64 + lane;  // 16-byte chunk index in the stage's A panel
       if (AK) {
         const int r = q / KCH, sl = q % KCH, c = sl ^ ((r >> 2) & 3);
         a_off[j] = r * (int)g.lda * 2 + c * 16;
         a_kc[j] = c * 8;
       } else {
-        constexpr int CPR = BM / 8;
-        const int r = q / CPR, sl = q % CPR, c = sl ^ mn_swz<BM>(r);
+        constexpr int CPR = C::BM / 8;
+        const int r = q / CPR, sl = q % CPR, c = sl ^ mn_swz<C::BM>(r);
         a_off[j] = (m0 + c * 8 < g.M) ? r * (int)g.lda * 2 + c * 16 : OOB;
         a_kc[j] = 0;
       }
     }
-    int b_off[B_INS], b_kc[B_INS];
 #pragma unroll
-    for (int j = 0; j < B_INS; ++j) {
-      const int q = (pw * B_INS + j) * 64 + lane;
+    for (int j = 0; j < C::B_INS; ++j) {
+      const int q = (cw * C::B_INS + j) * 64 + lane;
       if (BKC) {
         const int r = q / KCH, sl = q % KCH, c = sl ^ ((r >> 2) & 3);
         b_off[j] = r * (int)g.ldb * 2 + c * 16;
         b_kc[j] = c * 8;
       } else {
-        constexpr int CPR = BN / 8;
-        const int r = q / CPR, sl = q % CPR, c = sl ^ mn_swz<BN>(r);
+        constexpr int CPR = C::BN / 8;
+        const int r = q / CPR, sl = q % CPR, c = sl ^ mn_swz<C::BN>(r);
         b_off[j] = (n0 + c * 8 < g.N) ? r * (int)g.ldb * 2 + c * 16 : OOB;
         b_kc[j] = 0;
       }
     }
-    const unsigned smem_addr = lds_address(smem);
-    // All copies of K step kt into LDS stage kt % NSTAGE (past the last step the
-    // copies read only zeros into a stage that is not used again).
-    auto issue_step = [&](int kt) {
-      const int k0 = kt * KT;
-      const unsigned st = smem_addr + (unsigned)((kt % NSTAGE) * STAGE);
-      const i32x4 ra = make_rsrc(a_base + kt * a_step, a_total - kt * a_step);
-      const i32x4 rb = make_rsrc(b_base + kt * b_step, b_total - kt * b_step);
-#pragma unroll
-      for (int j = 0; j < A_INS; ++j)
-        lds_dma16(ra, (AK && k0 + a_kc[j] >= g.K) ? OOB : a_off[j], st + (pw * A_INS + j) * 1024);
-#pragma unroll
-      for (int j = 0; j < B_INS; ++j)
-        lds_dma16(rb, (BKC && k0 + b_kc[j] >= g.K) ? OOB : b_off[j], st + A_BYTES + (pw * B_INS + j) * 1024);
-    };
-#pragma unroll
-    for (int p = 0; p < PREF; ++p) issue_step(p);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step 0 landed
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      issue_step(kt + PREF);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step kt+1 landed
-      __syncthreads();
-    }
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no copy into this workgroup's LDS outlives it
-    return;
+    smem_addr = lds_address(smem);
   }
 
-  // -------------------------------------------------------------- consumer
-  const int wm = wave / CN;
-  const int wn = wave % CN;
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
-  const int kswz = (l32 >> 2) & 3;             // K-contig slot swizzle of this lane's row
-  const int grp = lane >> 4, i16 = lane & 15;  // transpose read: 16-lane group, lane in it
-  const int tr_row = 8 * (grp >> 1) + (i16 >> 2);
-  const int tr_col = 16 * (grp & 1) + 4 * (i16 & 3);
-  const int tr_swz_a = mn_swz<BM>(i16 >> 2);
-  const int tr_swz_b = mn_swz<BN>(i16 >> 2);
+  // Copy u (0 <= u < NVM) of K step kt into LDS stage kt % NSTAGE.  Past the last
+  // step the copies read only zeros into a stage that is not used again.
+  __device__ __forceinline__ void issue(int kt, int u) const {
+    const int k0 = kt * KT;
+    const unsigned st = smem_addr + (unsigned)((kt % C::NSTAGE) * C::STAGE);
+    if (u < C::A_INS) {
+      const int j = u;
+      const i32x4 r = make_rsrc(a_base + kt * a_step, a_total - kt * a_step);
+      lds_dma16(r, (AK && k0 + a_kc[j] >= K) ? OOB : a_off[j], st + (cw * C::A_INS + j) * 1024);
+    } else {
+      const int j = u - C::A_INS;
+      const i32x4 r = make_rsrc(b_base + kt * b_step, b_total - kt * b_step);
+      lds_dma16(r, (BKC && k0 + b_kc[j] >= K) ? OOB : b_off[j], st + C::A_BYTES + (cw * C::B_INS + j) * 1024);
+    }
+  }
+};
 
-  auto frag_k = [&](const char* panel, int row0, int s) -> bf16x8 {
+// A consumer wave's MFMA operand reads from an LDS stage.
+template <class C, bool AK, bool BKC>
+struct Reader {
+  int wm, wn, l32, hi, kswz, tr_row, tr_col, tr_swz_a, tr_swz_b;
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+    wm = wave / C::CN;
+    wn = wave % C::CN;
+    l32 = lane & 31;
+    hi = lane >> 5;
+    kswz = (l32 >> 2) & 3;                      // K-contig slot swizzle of this lane's row
+    const int grp = lane >> 4, i16 = lane & 15; // transpose read: 16-lane group, lane in it
+    tr_row = 8 * (grp >> 1) + (i16 >> 2);
+    tr_col = 16 * (grp & 1) + 4 * (i16 & 3);
+    tr_swz_a = mn_swz<C::BM>(i16 >> 2);
+    tr_swz_b = mn_swz<C::BN>(i16 >> 2);
+  }
+  __device__ __forceinline__ bf16x8 frag_k(const char* panel, int row0, int s) const {
     const int r = row0 + l32;
     const int slot = (2 * s + hi) ^ kswz;
-    return *(const bf16x8*)(panel + r * KROW + slot * 16);
-  };
-  auto frag_mn = [&](const char* panel, int row_bytes, int swz, int col0, int s) -> bf16x8 {
+    return *(const bf16x8*)(panel + r * (KT * 2) + slot * 16);
+  }
+  __device__ __forceinline__ bf16x8 frag_mn(const char* panel, int row_bytes, int swz, int col0, int s) const {
     const int col = col0 + tr_col;
     const int slot = (col >> 3) ^ swz;
     const char* p0 = panel + (16 * s + tr_row) * row_bytes + slot * 16 + (col & 7) * 2;
@@ -281,74 +259,42 @@ gemm_bf16_kernel(GemmArgs g) {
     v[0] = lo_b[0]; v[1] = lo_b[1]; v[2] = lo_b[2]; v[3] = lo_b[3];
     v[4] = hi_b[0]; v[5] = hi_b[1]; v[6] = hi_b[2]; v[7] = hi_b[3];
     return v;
-  };
-  auto load_frags = [&](int kt, int s, bf16x8* fa, bf16x8* fb) {
-    const char* sa = smem + (kt % NSTAGE) * STAGE;
-    const char* sb = sa + A_BYTES;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-      fa[i] = AK ? frag_k(sa, wm * WM + 32 * i, s) : frag_mn(sa, BM * 2, tr_swz_a, wm * WM + 32 * i, s);
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-      fb[j] = BKC ? frag_k(sb, wn * WN + 32 * j, s) : frag_mn(sb, BN * 2, tr_swz_b, wn * WN + 32 * j, s);
-  };
-
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  constexpr int NS = KT / 16;           // 16-wide k slices per stage
-  constexpr int LB = (NS - 1) & 1;      // operand buffer of the last slice
-  constexpr int FM_HALF = FM / 2 > 0 ? FM / 2 : 1;
-  auto mfma_rows = [&](const bf16x8* fa_, const bf16x8* fb_, int i0, int i1) {
-#pragma unroll
-    for (int i = i0; i < i1; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb_[j], fa_[i], acc[i][j], 0, 0, 0);
-  };
-
-  __syncthreads();  // step 0 is in LDS
-  bf16x8 fa[2][FM], fb[2][FN];
-  load_frags(0, 0, fa[0], fb[0]);
-  for (int kt = 0; kt < nk; ++kt) {
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s) {
-      load_frags(kt, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-      mfma_rows(fa[s & 1], fb[s & 1], 0, FM);
-    }
-    // Last slice: part of its MFMAs, the barrier that publishes step kt+1 (and
-    // releases step kt's stage to the producers), then step kt+1's first
-    // operands are read while the rest run.
-    mfma_rows(fa[LB], fb[LB], 0, FM_HALF);
-    __syncthreads();
-    load_frags(kt + 1, 0, fa[LB ^ 1], fb[LB ^ 1]);
-    mfma_rows(fa[LB], fb[LB], FM_HALF, FM);
   }
+  // Operands of 16-wide k slice s of K step kt.
+  __device__ __forceinline__ void load(const char* smem, int kt, int s, bf16x8* fa, bf16x8* fb) const {
+    const char* sa = smem + (kt % C::NSTAGE) * C::STAGE;
+    const char* sb = sa + C::A_BYTES;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+      fa[i] = AK ? frag_k(sa, wm * C::WM + 32 * i, s) : frag_mn(sa, C::BM * 2, tr_swz_a, wm * C::WM + 32 * i, s);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+      fb[j] = BKC ? frag_k(sb, wn * C::WN + 32 * j, s) : frag_mn(sb, C::BN * 2, tr_swz_b, wn * C::WN + 32 * j, s);
+  }
+};
 
-  // Epilogue.  Block (i, j), lane: row m = l32, columns 8q + 4*(lane/32) + 0..3.
+// Epilogue of one consumer wave.  Block (i, j), lane: row m = l32, columns
+// 8q + 4*(lane/32) + 0..3.
+template <class C, int EPI>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::FM][C::FN], int m0, int n0,
+                                         int wave, int lane) {
   // The coordinates are passed through empty asm so that the compiler derives the
   // epilogue addresses here instead of hoisting them above the K loop, where they
   // would hold registers for its whole duration.
-  int e_lane = lane, e_m0 = m0, e_n0 = n0, e_wave = wave;
-  asm volatile("" : "+v"(e_lane));
-  asm volatile("" : "+s"(e_m0), "+s"(e_n0), "+s"(e_wave));
-  const int e_l32 = e_lane & 31;
-  const int col_lane = 4 * (e_lane >> 5);
-  const int e_wm = e_wave / CN, e_wn = e_wave % CN;
+  asm volatile("" : "+v"(lane));
+  asm volatile("" : "+s"(m0), "+s"(n0), "+s"(wave));
+  const int l32 = lane & 31;
+  const int col_lane = 4 * (lane >> 5);
+  const int wm = wave / C::CN, wn = wave % C::CN;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = e_m0 + e_wm * WM + 32 * i + e_l32;
+  for (int i = 0; i < C::FM; ++i) {
+    const int m = m0 + wm * C::WM + 32 * i + l32;
     if (m >= g.M) continue;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
+    for (int j = 0; j < C::FN; ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = e_n0 + e_wn * WN + 32 * j + 8 * q + col_lane;
+        const int n = n0 + wn * C::WN + 32 * j + 8 * q + col_lane;
         if (n >= g.N) continue;
         float v[4] = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                       acc[i][j][4 * q + 3]};
@@ -391,31 +337,172 @@ gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
-template <int BM, int BN, bool AK, bool BKC, int EPI>
+template <class C, bool AK, bool BKC, int EPI>
+__global__ void __attribute__((amdgpu_flat_work_group_size(C::NT, C::NT),
+                               amdgpu_waves_per_eu(C::WAVES_PER_EU, C::WAVES_PER_EU)))
+gemm_bf16_kernel(GemmArgs g) {
+  constexpr int FM = C::FM, FN = C::FN, NVM = C::NVM, PREF = C::PREF;
+  constexpr int NS = KT / 16;             // 16-wide k slices per step
+  constexpr int LB = (NS - 1) & 1;        // operand buffer of the last slice (double buffering)
+  constexpr int FM_HALF = FM / 2 > 0 ? FM / 2 : 1;
+
+  __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  const int tiles_m = (g.M + C::BM - 1) / C::BM;
+  const int tiles_n = (g.N + C::BN - 1) / C::BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * C::BM;
+  const int n0 = tn * C::BN;
+  const int nk = (g.K + KT - 1) / KT;
+
+  if constexpr (C::NPROD > 0) {
+    if (wave >= C::NCONS) {
+      // -------------------------------------------------------- producer wave
+      Copier<C, AK, BKC> cp;
+      cp.init(g, m0, n0, wave - C::NCONS, lane, smem);
+#pragma unroll
+      for (int p = 0; p < PREF; ++p)
+#pragma unroll
+        for (int u = 0; u < NVM; ++u) cp.issue(p, u);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step 0 landed
+      __syncthreads();
+      for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+        for (int u = 0; u < NVM; ++u) cp.issue(kt + PREF, u);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step kt+1 landed
+        __syncthreads();
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no copy into this workgroup's LDS outlives it
+      return;
+    }
+  }
+
+  // ------------------------------------------------------------ consumer wave
+  Reader<C, AK, BKC> rd;
+  rd.init(wave, lane);
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto mfma = [&](const bf16x8* fa_, const bf16x8* fb_, int i, int j) {
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb_[j], fa_[i], acc[i][j], 0, 0, 0);
+  };
+
+  if constexpr (C::NPROD > 0) {
+    __syncthreads();  // step 0 is in LDS
+    bf16x8 fa[2][FM], fb[2][FN];
+    rd.load(smem, 0, 0, fa[0], fb[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+      for (int s = 0; s < NS - 1; ++s) {
+        rd.load(smem, kt, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) mfma(fa[s & 1], fb[s & 1], i, j);
+      }
+      // Last slice: part of its MFMAs, the barrier that publishes step kt+1 (and
+      // releases step kt's stage to the producers), then step kt+1's first
+      // operands are read while the rest run.
+#pragma unroll
+      for (int i = 0; i < FM_HALF; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mfma(fa[LB], fb[LB], i, j);
+      __syncthreads();
+      rd.load(smem, kt + 1, 0, fa[LB ^ 1], fb[LB ^ 1]);
+#pragma unroll
+      for (int i = FM_HALF; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mfma(fa[LB], fb[LB], i, j);
+    }
+  } else {
+    // Every wave also issues 1/8 of the copies, spread over the MFMAs that
+    // precede each step's barrier (the other wave on the SIMD keeps the matrix
+    // pipe busy while a copy holds this one up).
+    Copier<C, AK, BKC> cp;
+    cp.init(g, m0, n0, wave, lane, smem);
+#pragma unroll
+    for (int p = 0; p < PREF; ++p)
+#pragma unroll
+      for (int u = 0; u < NVM; ++u) cp.issue(p, u);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step 0 landed
+    __syncthreads();
+    constexpr int PRE_MF = FM * FN * (NS - 1) + FM_HALF * FN;   // MFMAs before the barrier
+    static_assert(PRE_MF >= NVM, "not enough MFMAs to spread the copies over");
+    bf16x8 fa[FM], fb[FN];
+    for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        rd.load(smem, kt, s, fa, fb);
+        const int i_end = (s == NS - 1) ? FM_HALF : FM;
+#pragma unroll
+        for (int i = 0; i < i_end; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            mfma(fa, fb, i, j);
+            const int t = s * FM * FN + i * FN + j;
+#pragma unroll
+            for (int u = 0; u < NVM; ++u)
+              if ((u * PRE_MF) / NVM == t) cp.issue(kt + PREF, u);
+          }
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step kt+1 landed
+      __syncthreads();
+#pragma unroll
+      for (int i = FM_HALF; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mfma(fa, fb, i, j);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no copy into this workgroup's LDS outlives it
+  }
+
+  epilogue<C, EPI>(g, acc, m0, n0, wave, lane);
+}
+
+// Tile menu: split kernels (8 consumer + 4 producer waves) and shared kernels
+// (8 waves that copy and compute).
+using T256x192 = Cfg<256, 192, 4, 4>;
+using T192x256 = Cfg<192, 256, 4, 2>;
+using T256x128 = Cfg<256, 128, 4, 4>;
+using T128x256 = Cfg<128, 256, 4, 2>;
+using T128x128 = Cfg<128, 128, 4, 2>;
+using T256x384 = Cfg<256, 384, 0, 2>;
+using T384x256 = Cfg<384, 256, 0, 4>;
+
+template <class C, bool AK, bool BKC, int EPI>
 const char* kname() {
   static const std::string s = std::string("gemm_bf16_") + (AK ? "n" : "t") + (BKC ? "t" : "n") + "_" +
                                (EPI == EPI_STORE ? "store" : EPI == EPI_BIAS_GELU ? "bias_gelu"
                                 : EPI == EPI_DGELU ? "dgelu" : "f32") +
-                               "_" + std::to_string(BM) + "x" + std::to_string(BN);
+                               "_" + std::to_string(C::BM) + "x" + std::to_string(C::BN);
   return s.c_str();
 }
 
-template <int BM, int BN, bool AK, bool BKC, int EPI>
+template <class C, bool AK, bool BKC, int EPI>
 hipError_t launch_tile(const GemmArgs& g, hipStream_t s, const char** name) {
-  *name = kname<BM, BN, AK, BKC, EPI>();
-  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, AK, BKC, EPI>), dim3(tiles), dim3(NT_WS), 0, s, g);
+  *name = kname<C, AK, BKC, EPI>();
+  const int tiles = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN);
+  hipLaunchKernelGGL((gemm_bf16_kernel<C, AK, BKC, EPI>), dim3(tiles), dim3(C::NT), 0, s, g);
   return hipGetLastError();
 }
 
 // Tile shape: the one with the least estimated time, counting whole waves of
-// tiles over the 256 CUs (one workgroup per CU) and the lower MFMA efficiency
-// of smaller tiles.
+// tiles over the 256 CUs (one workgroup per CU) and a per-tile efficiency that
+// grows with the tile (fewer bytes moved per FLOP).
 struct TileChoice { int bm, bn; };
 
 TileChoice choose_tile(int M, int N) {
   static const struct { int bm, bn; double eff; } cand[] = {
-      {256, 192, 1.00}, {192, 256, 1.00}, {256, 128, 0.92}, {128, 256, 0.92}, {128, 128, 0.75}};
+      {256, 384, 1.12}, {384, 256, 1.12}, {256, 192, 1.00}, {192, 256, 1.00},
+      {256, 128, 0.92}, {128, 256, 0.92}, {128, 128, 0.75}};
   double best = 1e300;
   TileChoice pick = {256, 192};
   for (const auto& c : cand) {
@@ -430,11 +517,13 @@ TileChoice choose_tile(int M, int N) {
 template <bool AK, bool BKC, int EPI>
 hipError_t launch_shape(const GemmArgs& g, hipStream_t s, const char** name) {
   const TileChoice t = choose_tile(g.M, g.N);
-  if (t.bm == 256 && t.bn == 192) return launch_tile<256, 192, AK, BKC, EPI>(g, s, name);
-  if (t.bm == 192 && t.bn == 256) return launch_tile<192, 256, AK, BKC, EPI>(g, s, name);
-  if (t.bm == 256 && t.bn == 128) return launch_tile<256, 128, AK, BKC, EPI>(g, s, name);
-  if (t.bm == 128 && t.bn == 256) return launch_tile<128, 256, AK, BKC, EPI>(g, s, name);
-  return launch_tile<128, 128, AK, BKC, EPI>(g, s, name);
+  if (t.bm == 256 && t.bn == 384) return launch_tile<T256x384, AK, BKC, EPI>(g, s, name);
+  if (t.bm == 384 && t.bn == 256) return launch_tile<T384x256, AK, BKC, EPI>(g, s, name);
+  if (t.bm == 256 && t.bn == 192) return launch_tile<T256x192, AK, BKC, EPI>(g, s, name);
+  if (t.bm == 192 && t.bn == 256) return launch_tile<T192x256, AK, BKC, EPI>(g, s, name);
+  if (t.bm == 256 && t.bn == 128) return launch_tile<T256x128, AK, BKC, EPI>(g, s, name);
+  if (t.bm == 128 && t.bn == 256) return launch_tile<T128x256, AK, BKC, EPI>(g, s, name);
+  return launch_tile<T128x128, AK, BKC, EPI>(g, s, name);
 }
 
 }  // namespace
