@@ -6,7 +6,7 @@
 // columns, so each wave reads one contiguous 1 KiB (bf16) run of a row) and a
 // chunk of rows; wave w sums rows w, w+4, ... of the chunk in fp32, the four
 // wave sums are added in a fixed order through LDS and written as one partial
-// row.  Pass 2 adds the partial rows of every column in chunk order.  There
+// row.  Pass 2 adds the partial rows of every column in a fixed order.  There
 // are no atomics, so the result is bitwise reproducible.
 //
 // Bias + GeLU.  H = GeLU(Z + b) with 8 elements per lane (16-byte bf16 loads).
@@ -60,14 +60,23 @@ __global__ void __launch_bounds__(CS_THREADS) colsum_partial_kernel(const void* 
   }
 }
 
+// Pass 2: a workgroup owns 64 columns (one per lane); wave w adds the partial
+// rows w, w+4, ... and the four wave sums are added in a fixed order.
 __global__ void __launch_bounds__(256) colsum_finalize_kernel(const float* part, float* out, int64_t N,
                                                               int chunks, int accumulate) {
-  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
-  float s = accumulate ? out[n] : 0.0f;
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n = (int64_t)blockIdx.x * 64 + lane;
   float t = 0.0f;
-  for (int c = 0; c < chunks; ++c) t += part[(int64_t)c * N + n];
-  out[n] = s + t;
+  if (n < N) {
+    for (int c = wave; c < chunks; c += 4) t += part[(int64_t)c * N + n];
+  }
+  red[wave][lane] = t;
+  __syncthreads();
+  if (wave == 0 && n < N) {
+    const float s = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    out[n] = accumulate ? out[n] + s : s;
+  }
 }
 
 template <bool IS_BF16>
@@ -127,7 +136,7 @@ hipError_t colsum(const void* in, bool in_bf16, float* out, float* ws, int accum
   if (e != hipSuccess) return e;
   LaunchInfo info2{"colsum_finalize", 0.0, 4.0 * chunks * (double)N + 4.0 * (accumulate ? 2 : 1) * N};
   trace_begin(s);
-  hipLaunchKernelGGL(colsum_finalize_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s,
+  hipLaunchKernelGGL(colsum_finalize_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, s,
                      (const float*)ws, out, N, chunks, accumulate);
   trace_end(s, info2);
   return hipGetLastError();
