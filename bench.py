@@ -190,8 +190,8 @@ def cpu_baseline(shard, frac_tokens=1):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frac", type=int, default=1, help="oracle sample = 1/N of the tokens")
     ap.add_argument("--part", choices=["all", "mlp", "attn"], default="all",

@@ -40,6 +40,7 @@ struct GemmArgs {
   const void* aux;    // [M x N] read by EPI_DGELU
   int64_t ldaux;
   int accumulate;     // EPI_F32 only
+  int group_m;        // tile rows per group in the tile order (set by the launcher)
 };
 
 // Kernel launch record for the optional event trace.

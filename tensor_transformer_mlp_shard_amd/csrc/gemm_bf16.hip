@@ -46,7 +46,6 @@ namespace tps {
 namespace {
 
 constexpr int KT = 32;        // K step per LDS stage
-constexpr int GROUP_M = 8;    // tile rows per group in the tile order
 
 __device__ __forceinline__ float gelu_f(float z) {
   return 0.5f * z * (1.0f + erff(z * 0.7071067811865475f));
@@ -62,19 +61,19 @@ __device__ __forceinline__ float bf2f(bf16 v) { return (float)v; }
 
 // Workgroup -> output tile.  Workgroups are handed to the 8 XCDs round-robin,
 // so consecutive ids are remapped to one XCD's contiguous range of logical
-// tiles; logical tiles are ordered in groups of GROUP_M tile rows so that an
+// tiles; logical tiles are ordered in groups of group_m tile rows so that an
 // XCD's workgroups share A and B panels in its L2.
-__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
   const int xcd = bid & 7;
   const int local = bid >> 3;
   const int base = total >> 3;
   const int rem = total & 7;
   const int logical = xcd * base + (xcd < rem ? xcd : rem) + local;
-  const int per_group = GROUP_M * tiles_n;
+  const int per_group = group_m * tiles_n;
   const int group = logical / per_group;
-  const int first_m = group * GROUP_M;
-  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int first_m = group * group_m;
+  const int gsize = min(tiles_m - first_m, group_m);
   const int in_group = logical - group * per_group;
   tm = first_m + in_group % gsize;
   tn = in_group / gsize;
@@ -354,7 +353,7 @@ gemm_bf16_kernel(GemmArgs g) {
   const int tiles_m = (g.M + C::BM - 1) / C::BM;
   const int tiles_n = (g.N + C::BN - 1) / C::BN;
   int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  tile_coords(blockIdx.x, tiles_m, tiles_n, g.group_m, tm, tn);
   const int m0 = tm * C::BM;
   const int n0 = tn * C::BN;
   const int nk = (g.K + KT - 1) / KT;
@@ -486,11 +485,28 @@ const char* kname() {
   return s.c_str();
 }
 
+// Rows of tiles per group in the tile order.  The 32 workgroups an XCD runs at
+// once cover about g tile rows x 32/g tile columns; their L2 fetches g row
+// panels of A (BM x K each) and 32/g column panels of B (K x BN each), so g is
+// chosen to minimise g * BM + (32 / g) * BN.
+int choose_group_m(int tiles_m, int bm, int bn) {
+  int best = 1;
+  double best_cost = 1e300;
+  for (int gm = 1; gm <= 32; gm *= 2) {
+    if (gm > tiles_m) break;
+    const double cost = (double)gm * bm + 32.0 / gm * bn;
+    if (cost < best_cost * 0.999) { best_cost = cost; best = gm; }
+  }
+  return best;
+}
+
 template <class C, bool AK, bool BKC, int EPI>
-hipError_t launch_tile(const GemmArgs& g, hipStream_t s, const char** name) {
+hipError_t launch_tile(const GemmArgs& g_in, hipStream_t s, const char** name) {
   *name = kname<C, AK, BKC, EPI>();
-  const int tiles = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<C, AK, BKC, EPI>), dim3(tiles), dim3(C::NT), 0, s, g);
+  GemmArgs g = g_in;
+  const int tiles_m = (g.M + C::BM - 1) / C::BM, tiles_n = (g.N + C::BN - 1) / C::BN;
+  g.group_m = choose_group_m(tiles_m, C::BM, C::BN);
+  hipLaunchKernelGGL((gemm_bf16_kernel<C, AK, BKC, EPI>), dim3(tiles_m * tiles_n), dim3(C::NT), 0, s, g);
   return hipGetLastError();
 }
 
