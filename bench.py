@@ -249,6 +249,11 @@ def main():
     roof["kernel"] = dom["name"]
     roof["launches_per_step"] = dom["launches"] // args.steps
     roof["avg_launch_ms"] = round(avg_ms, 5)
+    # what the matrix cores sustain with no memory traffic under the same power limit
+    shard.tps.mfma_probe(iters=20000)
+    probe = shard.tps.mfma_probe(iters=100000)
+    if roof["bound"] == "mfma":
+        roof["frac_of_mfma_probe"] = round(achieved / probe["tflops"], 4)
     kern = [{"name": k["name"], "launches_per_step": k["launches"] // args.steps,
              "ms_per_step": round(k["total_ms"] / args.steps, 4),
              "tflops": round(k["flops"] / (k["total_ms"] * 1e-3) / 1e12, 1) if k["flops"] else None,
@@ -278,6 +283,9 @@ def main():
         "wall_ms_per_step": round(wall_ms, 4),
         "parts": parts,
         "roofline": roof,
+        "mfma_probe": {"tflops": round(probe["tflops"], 1), "clock_ghz": round(probe["clock_ghz_mean"], 3),
+                       "mfma_busy": round(probe["mfma_busy"], 3), "compute_units": probe["compute_units"],
+                       "note": "register-only bf16 MFMA stream on random operands, no memory traffic"},
         "kernels": kern,
     }
     if not args.no_cpu_baseline and args.part == "all":

@@ -217,6 +217,26 @@ int tp_trace_num_kernels(void);
 int tp_trace_kernel(int32_t idx, char* name, size_t name_len, int64_t* launches,
                     double* total_ms, double* flops, double* bytes);
 
+/*
+ * Matrix-core probe (measurement only; no layer arithmetic).  Launches
+ * `blocks` workgroups of 4 waves; every wave issues 16 * `iters` bf16 MFMAs
+ * (32x32x16, fp32 accumulate, 32768 FLOP each) on register operands with
+ * random bits and no memory traffic, so the run shows what the matrix cores
+ * sustain under the board's power limit.  Outputs (device memory, caller
+ * owned): sink[blocks * 256] floats (one accumulator sum per thread, written
+ * only so the work is kept); ticks[2 * blocks] as unsigned 64-bit integers,
+ * per workgroup: shader-clock cycles, then constant-rate-clock ticks (rate
+ * from tp_wall_clock_rate_khz) spent in its MFMA loop.  Asynchronous on
+ * `stream`.  Limits: 1 <= blocks <= 65536, 1 <= iters <= 2^24, else
+ * TP_ERR_ARG; null outputs TP_ERR_NULLPTR; ticks not 8-byte aligned
+ * TP_ERR_ALIGNMENT; launch failure TP_ERR_HIP.
+ */
+int tp_mfma_probe(int32_t blocks, int32_t iters, float* sink, unsigned long long* ticks, void* stream);
+/* Rate of the constant-rate clock read by tp_mfma_probe (kHz) on the current
+ * device, written to *khz.  TP_ERR_NULLPTR for a null khz, TP_ERR_HIP when
+ * the runtime cannot report it. */
+int tp_wall_clock_rate_khz(int32_t* khz);
+
 #ifdef __cplusplus
 }
 #endif

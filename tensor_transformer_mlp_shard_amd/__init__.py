@@ -24,7 +24,7 @@ from ._native import NativeLibraryMissing  # noqa: F401
 __all__ = [
     "column_linear", "row_linear", "mlp_shard_fwd", "mlp_shard_bwd", "column_linear_bwd",
     "row_linear_bwd", "bias_grad", "bias_gelu", "workspace_size", "trace_start", "trace_stop",
-    "library_path", "NativeLibraryMissing",
+    "mfma_probe", "library_path", "NativeLibraryMissing",
 ]
 
 _DT = {torch.bfloat16: _native.TP_BF16, torch.float32: _native.TP_FP32}
@@ -278,3 +278,40 @@ def trace_stop():
         out.append({"name": buf.value.decode(), "launches": n.value, "total_ms": ms.value, "flops": fl.value,
                     "bytes": by.value})
     return out
+
+
+MFMA_FLOP = 2 * 32 * 32 * 16   # one bf16 32x32x16 MFMA
+FLOP_PER_CU_CLK = 4096         # dense bf16 matrix-core rate of one compute unit
+
+
+def mfma_probe(iters: int = 100000, blocks: int | None = None, device=None) -> dict:
+    """Run the register-only MFMA probe once and return what it sustained:
+    TFLOP/s over the kernel's event time, the mean and minimum shader clock
+    (GHz) over the workgroups, and the matrix-pipe busy fraction implied by
+    the cycle counts (1.0 when every SIMD issues one MFMA per 32 cycles).
+    ``blocks`` defaults to two 4-wave workgroups per compute unit."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = 2 * cus if blocks is None else blocks
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    ticks = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
+    L = _native.lib()
+    khz = ctypes.c_int32()
+    with torch.cuda.device(dev):
+        _native.check(L.tp_wall_clock_rate_khz(ctypes.byref(khz)), "tp_wall_clock_rate_khz")
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        _native.check(L.tp_mfma_probe(blocks, iters, _ptr(sink), _ptr(ticks), _stream(dev)), "tp_mfma_probe")
+        stop.record()
+        stop.synchronize()
+    ms = start.elapsed_time(stop)
+    t = ticks.view(blocks, 2).cpu().double()
+    cycles, wall_s = t[:, 0], t[:, 1] / (khz.value * 1e3)
+    ghz = cycles / wall_s / 1e9
+    flops = float(blocks) * 4 * 16 * iters * MFMA_FLOP
+    # MFMAs each SIMD issued, over the cycles the slowest workgroup took
+    waves_per_simd = blocks * 4 / (4 * cus)
+    busy = waves_per_simd * 16 * iters * 32 / float(cycles.max())
+    return {"tflops": flops / (ms * 1e-3) / 1e12, "ms": ms, "clock_ghz_mean": float(ghz.mean()),
+            "clock_ghz_min": float(ghz.min()), "mfma_busy": busy, "blocks": blocks, "iters": iters,
+            "compute_units": cus, "finite": bool(torch.isfinite(sink).all().item())}

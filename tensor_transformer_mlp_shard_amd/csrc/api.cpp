@@ -403,6 +403,24 @@ int tp_bias_gelu(const void* Z, const void* b, void* H, int64_t T, int64_t N, in
   return TP_OK;
 }
 
+// ---------------------------------------------------------------- probe
+int tp_mfma_probe(int32_t blocks, int32_t iters, float* sink, unsigned long long* ticks, void* stream) {
+  if (blocks < 1 || blocks > 65536 || iters < 1 || iters > (1 << 24)) return TP_ERR_ARG;
+  if (!sink || !ticks) return TP_ERR_NULLPTR;
+  if ((uintptr_t)ticks % 8 != 0 || (uintptr_t)sink % 4 != 0) return TP_ERR_ALIGNMENT;
+  HIP_TRY(mfma_probe(blocks, iters, sink, ticks, (hipStream_t)stream));
+  return TP_OK;
+}
+
+int tp_wall_clock_rate_khz(int32_t* khz) {
+  if (!khz) return TP_ERR_NULLPTR;
+  int dev = 0, rate = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TP_ERR_HIP;
+  if (hipDeviceGetAttribute(&rate, hipDeviceAttributeWallClockRate, dev) != hipSuccess || rate <= 0) return TP_ERR_HIP;
+  *khz = rate;
+  return TP_OK;
+}
+
 // ---------------------------------------------------------------- trace
 int tp_trace_start(int32_t max_launches) {
   Trace& t = trace();

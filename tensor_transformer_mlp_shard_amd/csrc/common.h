@@ -69,4 +69,7 @@ hipError_t colsum(const void* in, bool in_bf16, float* out, float* ws, int accum
 hipError_t bias_gelu(const void* Z, const void* b, void* H, bool is_bf16, int64_t T, int64_t N,
                      hipStream_t s);
 
+// Register-only MFMA throughput probe (probe.hip).
+hipError_t mfma_probe(int blocks, int iters, float* sink, unsigned long long* ticks, hipStream_t s);
+
 }  // namespace tps

@@ -143,3 +143,15 @@ def test_workspace_size(lib):
     assert ws(_native.TP_OP_MLP_SHARD_BWD, 2048, 12288, 49152, 8, 1) > a   # fp32 dZ
     assert ws(_native.TP_OP_BIAS_GRAD, 4096, 1024, 0, 1, 0) >= 1024 * 4
     assert ws(_native.TP_OP_COLUMN_LINEAR_BWD, 8192, 12288, 36864, 8, 0) >= 4608 * 4
+
+
+def test_probe_validation(lib):
+    # every call fails its argument checks before any HIP call
+    assert lib.tp_mfma_probe(0, 10, A0, A1, S) == -9
+    assert lib.tp_mfma_probe(65537, 10, A0, A1, S) == -9
+    assert lib.tp_mfma_probe(4, 0, A0, A1, S) == -9
+    assert lib.tp_mfma_probe(4, (1 << 24) + 1, A0, A1, S) == -9
+    assert lib.tp_mfma_probe(4, 10, None, A1, S) == -1
+    assert lib.tp_mfma_probe(4, 10, A0, None, S) == -1
+    assert lib.tp_mfma_probe(4, 10, A0, P(0x10004), S) == -4
+    assert lib.tp_wall_clock_rate_khz(None) == -1

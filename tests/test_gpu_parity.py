@@ -294,3 +294,19 @@ def test_python_binding_rejects_bad_inputs():
     w = torch.zeros((16, 12), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(RuntimeError, match="TP_ERR_ALIGNMENT"):
         tps.column_linear(x, w, tp_size=1)
+
+
+@pytest.mark.gpu
+def test_mfma_probe_reports_plausible_rates():
+    """The matrix-core probe runs, keeps finite accumulators, and its cycle and
+    clock readings agree with its own event time."""
+    import tensor_transformer_mlp_shard_amd as tps
+    tps.mfma_probe(iters=2000)  # warm-up
+    r = tps.mfma_probe(iters=20000)
+    print("probe", r)
+    assert r["finite"]
+    assert 0.3 < r["clock_ghz_min"] <= r["clock_ghz_mean"] < 3.0
+    assert 0.5 < r["mfma_busy"] <= 1.05
+    # the rate is bounded by the compute units at the measured clock
+    ceiling = r["compute_units"] * tps.FLOP_PER_CU_CLK * r["clock_ghz_mean"] / 1e3
+    assert 0.3 * ceiling < r["tflops"] < 1.1 * ceiling
