@@ -11,7 +11,8 @@
 #include <string>
 #include <vector>
 
-#include "common.h"
+#include "gemm.h"
+#include "side.h"
 
 namespace tps {
 namespace {

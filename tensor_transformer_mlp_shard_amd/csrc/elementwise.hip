@@ -10,7 +10,7 @@
 // are no atomics, so the result is bitwise reproducible.
 //
 // Bias + GeLU.  H = GeLU(Z + b) with 8 elements per lane (16-byte bf16 loads).
-#include "common.h"
+#include "side.h"
 
 namespace tps {
 namespace {

@@ -1,0 +1,40 @@
+// GEMM launch arguments and launchers (gemm_bf16.hip, gemm_f32.hip).
+#pragma once
+
+#include "common.h"
+
+namespace tps {
+
+// Epilogue applied to the fp32 accumulators of a GEMM tile.
+enum Epi : int {
+  EPI_STORE = 0,      // C (dtype) = acc (+ bias[n])
+  EPI_BIAS_GELU = 1,  // z = acc (+ bias[n]); C2 (dtype, optional) = z; C (dtype) = GeLU(z)
+  EPI_DGELU = 2,      // C (dtype) = acc * GeLU'(aux[m, n])
+  EPI_F32 = 3         // C (fp32) = acc, or C += acc when accumulate
+};
+
+// One C = op(A)[M x K] * op(B)[K x N] launch plus its epilogue operands.
+// A is [M x K] row-major when a_kcontig, else [K x M] row-major (A^T stored);
+// B is [N x K] row-major when b_kcontig, else [K x N] row-major.
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  int64_t lda, ldb;
+  int M, N, K;
+  void* C;            // main output
+  int64_t ldc;
+  void* C2;           // second output (pre-activation for EPI_BIAS_GELU), nullable
+  int64_t ldc2;
+  const void* bias;   // [N], dtype of the path, nullable
+  const void* aux;    // [M x N] read by EPI_DGELU
+  int64_t ldaux;
+  int accumulate;     // EPI_F32 only
+  int group_m;        // tile rows per group in the tile order (set by the launcher)
+};
+
+// GEMM launchers (gemm_bf16.hip / gemm_f32.hip). Return hipSuccess or the
+// launch error.  a_kcontig / b_kcontig select the operand layouts.
+hipError_t gemm_bf16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s);
+hipError_t gemm_f32(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s);
+
+}  // namespace tps

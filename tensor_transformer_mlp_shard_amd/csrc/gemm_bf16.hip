@@ -38,7 +38,7 @@
 // outside the matrix read zero and stores outside it are skipped.  Feature
 // dimensions are multiples of 8, so a 16-byte vector is entirely inside or
 // entirely outside.
-#include "common.h"
+#include "gemm.h"
 
 #include <string>
 

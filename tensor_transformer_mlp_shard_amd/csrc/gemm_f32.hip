@@ -3,7 +3,7 @@
 // Plain LDS-tiled FMA kernel (64 x 64 output tile, K step 16, 256 threads with
 // 4 x 4 outputs each).  It exists to run the whole shard in true fp32
 // arithmetic, not for speed; the bf16 matrix-core kernel is the product path.
-#include "common.h"
+#include "gemm.h"
 
 namespace tps {
 namespace {

@@ -8,7 +8,7 @@
 // Together they give the throughput the matrix cores reach under the board's
 // power limit, the ceiling a GEMM's rate is best compared against beside the
 // datasheet peak.
-#include "common.h"
+#include "side.h"
 
 namespace tps {
 namespace {

@@ -1,0 +1,22 @@
+// Memory-bound side kernels (elementwise.hip) and the matrix-core probe
+// (probe.hip).
+#pragma once
+
+#include "common.h"
+
+namespace tps {
+
+// Column sum over rows (elementwise.hip): out[n] (+)= sum_t in[t, n].
+// Uses `chunks * N` floats of workspace.
+int colsum_chunks(int64_t T, int64_t N);
+hipError_t colsum(const void* in, bool in_bf16, float* out, float* ws, int accumulate,
+                  int64_t T, int64_t N, hipStream_t s);
+
+// H = GeLU(Z + b) elementwise (elementwise.hip).
+hipError_t bias_gelu(const void* Z, const void* b, void* H, bool is_bf16, int64_t T, int64_t N,
+                     hipStream_t s);
+
+// Register-only MFMA throughput probe (probe.hip).
+hipError_t mfma_probe(int blocks, int iters, float* sink, unsigned long long* ticks, hipStream_t s);
+
+}  // namespace tps
