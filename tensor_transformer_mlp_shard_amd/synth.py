@@ -15,13 +15,14 @@ from dataclasses import dataclass, field
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "seeded", "randn", "mlp_inputs", "attn_inputs", "inputs_for"]
+__all__ = ["Workload", "WORKLOADS", "seeded", "randn", "mlp_inputs", "attn_inputs", "core_attn_inputs",
+           "inputs_for"]
 
 
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "mlp" or "attn"
+    kind: str            # "mlp", "attn" (attention linears) or "core_attn"
     T: int               # tokens (micro-batch x sequence, flattened)
     h: int               # hidden size
     F: int               # full FFN width (mlp) or full QKV width (attn)
@@ -31,10 +32,20 @@ class Workload:
     seed: int
     full: bool           # draw unsharded weights (then slice) or the rank's shard only
     note: str = field(default="", compare=False)
+    seq: int = 0         # core_attn: sequence length (T = micro-batch x seq)
+    heads: int = 0       # core_attn: attention heads of the whole layer
 
     @property
     def f(self) -> int:
         return self.F // self.tp
+
+    @property
+    def heads_local(self) -> int:
+        return self.heads // self.tp
+
+    @property
+    def head_dim(self) -> int:
+        return self.h // self.heads
 
 
 # Sizes follow the pages' workloads: the GPT launch example of the tutorial
@@ -54,6 +65,17 @@ WORKLOADS = {
     "gpt175b_attn_tp8": Workload("gpt175b_attn_tp8", "attn", 8192, 12288, 36864, 8, "bf16", 0.006, 1239, False,
                                  "175B attention linears at TP=8: QKV 12288->4608 column shard, "
                                  "out-proj 1536->12288 row shard"),
+    # Core attention on a rank's local heads.  Head counts: 16 for the tutorial's
+    # GPT (head dim 64); 96 for the 175B case (head dim 128, so the 4608-wide
+    # QKV shard holds 12 heads).  The 175B token count is 4 sequences of 2048.
+    # QKV activations are drawn N(0, 1), which puts the scaled scores at unit
+    # spread.
+    "gpt_h1024_core_attn_tp2": Workload("gpt_h1024_core_attn_tp2", "core_attn", 4096, 1024, 3072, 2, "bf16", 1.0,
+                                        1240, False, "GPT h=1024 TP=2: 8 local heads of 64, 4 x 1024 tokens",
+                                        seq=1024, heads=16),
+    "gpt175b_core_attn_tp8": Workload("gpt175b_core_attn_tp8", "core_attn", 8192, 12288, 36864, 8, "bf16", 1.0,
+                                      1241, False, "175B TP=8: 12 local heads of 128, 4 x 2048 tokens",
+                                      seq=2048, heads=96),
 }
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}
@@ -119,7 +141,20 @@ def attn_inputs(T: int, h: int, qkv_width: int, tp: int, dtype: str, sigma_w: fl
     return out
 
 
+def core_attn_inputs(T: int, heads_local: int, head_dim: int, dtype: str, sigma: float, seed: int) -> dict:
+    """Inputs of core attention on one rank's heads.
+
+    Draw order: QKV[T x 3*Hl*d] (columns [Q | K | V], head-major in each),
+    dO[T x Hl*d].  QKV entries are N(0, sigma^2), dO entries N(0, 1).
+    """
+    g = seeded(seed)
+    w = heads_local * head_dim
+    return {"QKV": randn(g, (T, 3 * w), sigma, dtype), "dO": randn(g, (T, w), 1.0, dtype)}
+
+
 def inputs_for(w: Workload) -> dict:
+    if w.kind == "core_attn":
+        return core_attn_inputs(w.T, w.heads_local, w.head_dim, w.dtype, w.sigma_w, w.seed)
     if w.kind == "mlp":
         return mlp_inputs(w.T, w.h, w.F, w.tp, w.dtype, w.sigma_w, w.seed, full=w.full)
     return attn_inputs(w.T, w.h, w.F, w.tp, w.dtype, w.sigma_w, w.seed)

@@ -39,3 +39,15 @@ def test_sigma_scaling():
     d = synth.mlp_inputs(256, 512, 512, 1, "fp32", 0.02, seed=3)
     assert abs(float(d["A"].std()) - 0.02) < 0.001
     assert abs(float(d["X"].std()) - 1.0) < 0.02
+
+
+def test_core_attention_workloads():
+    w = synth.WORKLOADS["gpt175b_core_attn_tp8"]
+    assert (w.heads_local, w.head_dim, w.T // w.seq) == (12, 128, 4)
+    assert 3 * w.heads_local * w.head_dim == w.F // w.tp == 4608
+    v = synth.WORKLOADS["gpt_h1024_core_attn_tp2"]
+    assert (v.heads_local, v.head_dim, v.T // v.seq) == (8, 64, 4)
+    x = synth.core_attn_inputs(32, 2, 8, "bf16", 1.0, seed=4)
+    assert x["QKV"].shape == (32, 48) and x["dO"].shape == (32, 16) and x["QKV"].dtype == torch.bfloat16
+    y = synth.core_attn_inputs(32, 2, 8, "bf16", 1.0, seed=4)
+    assert torch.equal(x["QKV"].view(torch.int16), y["QKV"].view(torch.int16))
