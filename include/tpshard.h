@@ -189,6 +189,32 @@ int tp_bias_gelu(const void* Z, const void* b, void* H, int64_t T, int64_t N, in
                  void* stream);
 
 /*
+ * Core attention on the rank's local heads.  [TUT] "Megatron-LM 核心架构 /
+ * 张量并行原理": with the Q, K, V projections column-parallel and the output
+ * projection row-parallel, each rank owns whole heads and runs their attention
+ * locally between the two shards; [INTRO] "课程导入" 1.3.1: multi-head
+ * self-attention; [TUT] "最佳实践与调优建议": an IO-aware exact attention kernel
+ * (the score matrix never reaches HBM).
+ *
+ *   Hl = heads / tp_size local heads of width head_dim (64 or 128);
+ *   QKV_i [T x 3*Hl*head_dim] bf16: columns [Q | K | V], each block head-major
+ *         ([head][head_dim]) -- the QKV column shard's output;
+ *   T = B * seq tokens: B sequences of length seq packed back to back;
+ *   O_i [T x Hl*head_dim] bf16, head-major -- the out-projection row shard's input;
+ *   per head and sequence O = softmax(Q K^T / sqrt(head_dim) + M) V, M the causal
+ *   mask (key > query excluded) when causal = 1, none when causal = 0; scores and
+ *   softmax in fp32; no dropout;
+ *   lse [Hl x T] fp32 (nullable, e.g. for inference): natural-log log-sum-exp of
+ *   each query's scaled scores over its allowed keys (what the backward reads).
+ * dtype must be TP_BF16 (TP_ERR_DTYPE otherwise).  Errors: head_dim not 64/128,
+ * T not a multiple of seq, or 3*Hl*head_dim > 2^21 -> TP_ERR_DIM; heads not
+ * divisible by tp_size -> TP_ERR_TP_DIVISIBILITY; causal not 0/1 -> TP_ERR_ARG;
+ * outputs overlapping the input or each other -> TP_ERR_ALIAS.
+ */
+int tp_attention_fwd(const void* QKV_i, void* O_i, float* lse, int64_t T, int64_t seq, int64_t heads,
+                     int64_t head_dim, int32_t tp_size, int32_t causal, int32_t dtype, void* stream);
+
+/*
  * Workspace bytes needed by `op` (TP_OP_*).  Arguments are those of the
  * matching call: T, d_in, d_out = (T, K, N) for the linears, (T, h, F) for the
  * MLP, (T, N, unused) for the bias gradient.  Returns 0 for invalid arguments.

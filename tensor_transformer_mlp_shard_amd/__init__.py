@@ -24,7 +24,7 @@ from ._native import NativeLibraryMissing  # noqa: F401
 __all__ = [
     "column_linear", "row_linear", "mlp_shard_fwd", "mlp_shard_bwd", "column_linear_bwd",
     "row_linear_bwd", "bias_grad", "bias_gelu", "workspace_size", "trace_start", "trace_stop",
-    "mfma_probe", "library_path", "NativeLibraryMissing",
+    "attention_fwd", "mfma_probe", "library_path", "NativeLibraryMissing",
 ]
 
 _DT = {torch.bfloat16: _native.TP_BF16, torch.float32: _native.TP_FP32}
@@ -258,6 +258,22 @@ def bias_gelu(z, b=None):
     st = _native.lib().tp_bias_gelu(_ptr(z), _ptr(b), _ptr(hh), T, N, _dtype_code(z), _stream(z.device))
     _native.check(st, "tp_bias_gelu")
     return hh
+
+
+def attention_fwd(qkv, *, seq: int, heads: int, head_dim: int, tp_size: int, causal: bool = True,
+                  save_lse: bool = True, out=None):
+    """Core attention on the rank's heads: qkv [T x 3*Hl*d] -> (O [T x Hl*d], lse [Hl x T] or None)."""
+    T, W = qkv.shape
+    hl = heads // tp_size if tp_size > 0 else 0
+    dev = qkv.device
+    _check("qkv", qkv, (T, 3 * hl * head_dim), torch.bfloat16, dev)
+    o = out if out is not None else torch.empty((T, hl * head_dim), dtype=torch.bfloat16, device=dev)
+    _check("out", o, (T, hl * head_dim), torch.bfloat16, dev)
+    lse = torch.empty((hl, T), dtype=torch.float32, device=dev) if save_lse else None
+    st = _native.lib().tp_attention_fwd(_ptr(qkv), _ptr(o), _ptr(lse), T, seq, heads, head_dim, tp_size,
+                                        int(causal), _native.TP_BF16, _stream(dev))
+    _native.check(st, "tp_attention_fwd")
+    return o, lse
 
 
 def trace_start(max_launches: int = 4096) -> None:

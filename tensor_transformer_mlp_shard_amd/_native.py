@@ -35,6 +35,7 @@ PROTOTYPES = {
     "tp_bias_gelu": (_i32, [_p, _p, _p, _i64, _i64, _i32, _p]),
     "tp_workspace_size": (_sz, [_i32, _i64, _i64, _i64, _i32, _i32]),
     "tp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "tp_attention_fwd": (_i32, [_p, _p, _fp, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _p]),
     "tp_mfma_probe": (_i32, [_i32, _i32, _p, _p, _p]),
     "tp_wall_clock_rate_khz": (_i32, [ctypes.POINTER(_i32)]),
     "tp_trace_start": (_i32, [_i32]),

@@ -11,6 +11,7 @@
 #include <string>
 #include <vector>
 
+#include "attention.h"
 #include "gemm.h"
 #include "side.h"
 
@@ -117,6 +118,27 @@ GemmArgs make_args(const void* A, int64_t lda, const void* B, int64_t ldb, int64
 }
 
 size_t colsum_ws_bytes(int64_t T, int64_t N) { return round_up((size_t)colsum_chunks(T, N) * (size_t)N * 4); }
+
+// Shape checks shared by the attention entry points; fills p on success.
+int check_attention(int64_t T, int64_t seq, int64_t heads, int64_t head_dim, int32_t tp_size, int32_t causal,
+                    int32_t dtype, AttnProblem& p) {
+  if (dtype != TP_BF16) return TP_ERR_DTYPE;  // bf16 only: the attention kernels are MFMA kernels
+  if (causal != 0 && causal != 1) return TP_ERR_ARG;
+  TP_TRY(check_dims({T, seq, heads}));
+  if (head_dim != 64 && head_dim != 128) return TP_ERR_DIM;
+  if (T % seq != 0) return TP_ERR_DIM;
+  if (tp_size < 1 || heads % tp_size != 0) return TP_ERR_TP_DIVISIBILITY;
+  const int64_t hl = heads / tp_size;
+  if (3 * hl * head_dim > kMaxFeature) return TP_ERR_DIM;
+  const int64_t workgroups = (seq + 127) / 128 * (T / seq) * hl;  // one per 128 queries of a (sequence, head)
+  if (workgroups > 0x7fffffff) return TP_ERR_DIM;
+  p.T = T;
+  p.S = (int)seq;
+  p.Hl = (int)hl;
+  p.D = (int)head_dim;
+  p.causal = causal != 0;
+  return TP_OK;
+}
 
 // ---------------------------------------------------------------- trace
 struct TraceAgg {
@@ -401,6 +423,19 @@ int tp_bias_gelu(const void* Z, const void* b, void* H, int64_t T, int64_t N, in
   const int64_t es = elsize(dtype);
   TP_TRY(check_alias({{Z, T * N * es}, {b, N * es}}, {{H, T * N * es}}));
   HIP_TRY(bias_gelu(Z, b, H, dtype == TP_BF16, T, N, (hipStream_t)stream));
+  return TP_OK;
+}
+
+// ---------------------------------------------------------------- core attention
+int tp_attention_fwd(const void* QKV_i, void* O_i, float* lse, int64_t T, int64_t seq, int64_t heads,
+                     int64_t head_dim, int32_t tp_size, int32_t causal, int32_t dtype, void* stream) {
+  AttnProblem p;
+  TP_TRY(check_attention(T, seq, heads, head_dim, tp_size, causal, dtype, p));
+  TP_TRY(check_nonnull({QKV_i, O_i}));
+  TP_TRY(check_ptrs_aligned({QKV_i, O_i, lse}));
+  const int64_t w = (int64_t)p.Hl * p.D;
+  TP_TRY(check_alias({{QKV_i, T * 3 * w * 2}}, {{O_i, T * w * 2}, {lse, lse ? T * p.Hl * 4 : 0}}));
+  HIP_TRY(attention_fwd((const bf16*)QKV_i, (bf16*)O_i, lse, p, (hipStream_t)stream));
   return TP_OK;
 }
 

@@ -155,3 +155,24 @@ def test_probe_validation(lib):
     assert lib.tp_mfma_probe(4, 10, A0, None, S) == -1
     assert lib.tp_mfma_probe(4, 10, A0, P(0x10004), S) == -4
     assert lib.tp_wall_clock_rate_khz(None) == -1
+
+
+def test_attention_fwd_validation(lib):
+    f = lib.tp_attention_fwd
+    A0, A1, A2 = P(0x1000000), P(0x2000000), P(0x3000000)   # disjoint at these sizes
+    # (QKV, O, lse, T, seq, heads, head_dim, tp, causal, dtype, stream); 2 local heads of 64 -> QKV 384 wide
+    assert f(A0, A1, A2, 256, 128, 4, 64, 2, 1, 1, S) == -5          # fp32: MFMA kernels are bf16 only
+    assert f(A0, A1, A2, 256, 128, 4, 64, 2, 1, 7, S) == -5
+    assert f(A0, A1, A2, 256, 128, 4, 96, 2, 1, 0, S) == -2          # head_dim not 64/128
+    assert f(A0, A1, A2, 250, 128, 4, 64, 2, 1, 0, S) == -2          # T not whole sequences
+    assert f(A0, A1, A2, 0, 128, 4, 64, 2, 1, 0, S) == -2
+    assert f(A0, A1, A2, 256, 0, 4, 64, 2, 1, 0, S) == -2
+    assert f(A0, A1, A2, 256, 128, 4, 64, 3, 1, 0, S) == -3          # heads % tp
+    assert f(A0, A1, A2, 256, 128, 4, 64, 0, 1, 0, S) == -3
+    assert f(A0, A1, A2, 256, 128, 4, 64, 2, 2, 0, S) == -9          # causal flag
+    assert f(None, A1, A2, 256, 128, 4, 64, 2, 1, 0, S) == -1
+    assert f(A0, None, A2, 256, 128, 4, 64, 2, 1, 0, S) == -1
+    assert f(P(0x10008), A1, A2, 256, 128, 4, 64, 2, 1, 0, S) == -4
+    assert f(A0, A0, A2, 256, 128, 4, 64, 2, 1, 0, S) == -6          # O aliases QKV
+    assert f(A0, A1, P(A1.value + 256), 256, 128, 4, 64, 2, 1, 0, S) == -6   # lse inside O
+    assert f(A0, A1, A2, 1 << 20, 1 << 20, 3 * 4096, 128, 1, 1, 0, S) == -2  # QKV wider than 2^21

@@ -1,0 +1,107 @@
+"""GPU parity of core attention on the local heads (tp_attention_*) against the
+fp64 oracle, by relative Frobenius error (bf16 storage, fp32 scores and
+softmax: <= 5e-3) and absolute error of the log-sum-exp (<= 2e-3: fp32
+accumulation of exact bf16 products).
+
+Small problems are compared whole; they cover sequences shorter than one key
+block, ragged key and query blocks, one-token sequences, several sequences and
+heads, both head widths and both masks.  The 175B-shaped and GPT h=1024
+problems run at full size and are compared on sampled (sequence, head) pairs,
+each of which the oracle evaluates whole."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tensor_transformer_mlp_shard_amd as tps
+from tensor_transformer_mlp_shard_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-3
+LSE_TOL = 2e-3
+DEV = "cuda:0"
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def _rel(name, got, ref, tol=TOL):
+    e = oracle.rel_fro(got, ref)
+    print(f"  {name:6s} rel_fro={e:.3e} (tol {tol:g})", flush=True)
+    assert e <= tol, f"{name}: rel_fro {e:.3e} > {tol:g}"
+
+
+def _lse(got, ref):
+    e = float(np.max(np.abs(got - ref)))
+    print(f"  lse    max_abs={e:.3e} (tol {LSE_TOL:g})", flush=True)
+    assert e <= LSE_TOL
+
+
+CASES = [  # (T, seq, heads, head_dim, tp, causal, sigma)
+    (1, 1, 1, 64, 1, True, 1.0),
+    (7, 7, 2, 64, 1, True, 1.0),
+    (64, 64, 1, 128, 1, True, 1.0),
+    (130, 65, 2, 128, 2, True, 1.0),
+    (257, 257, 3, 64, 1, True, 1.0),
+    (300, 100, 2, 128, 1, False, 1.0),
+    (384, 128, 4, 128, 2, True, 2.0),
+    (520, 260, 2, 64, 1, False, 1.5),
+    (1024, 512, 2, 128, 1, True, 1.0),
+]
+
+
+@pytest.mark.parametrize("T,seq,heads,d,tp,causal,sigma", CASES,
+                         ids=[f"T{c[0]}_S{c[1]}_H{c[2]}_d{c[3]}_p{c[4]}_{'causal' if c[5] else 'full'}" for c in CASES])
+def test_attention_fwd_small(T, seq, heads, d, tp, causal, sigma):
+    hl = heads // tp
+    x = synth.core_attn_inputs(T, hl, d, "bf16", sigma, seed=T * 7 + d + heads)
+    print(f"case T={T} S={seq} Hl={hl} d={d} causal={causal}", flush=True)
+    O, lse = tps.attention_fwd(x["QKV"].to(DEV), seq=seq, heads=heads, head_dim=d, tp_size=tp, causal=causal)
+    torch.cuda.synchronize()
+    O_ref, lse_ref = oracle.core_attention_fwd(f64(x["QKV"]), seq, hl, d, causal)
+    _rel("O", f64(O), O_ref)
+    _lse(f64(lse), lse_ref)
+
+
+def _sampled_pairs(w, n):
+    rng = np.random.default_rng(w.seed)
+    B = w.T // w.seq
+    pairs = {(B - 1, w.heads_local - 1), (0, 0)}
+    while len(pairs) < n:
+        pairs.add((int(rng.integers(B)), int(rng.integers(w.heads_local))))
+    return sorted(pairs)
+
+
+@pytest.mark.parametrize("name", ["gpt175b_core_attn_tp8", "gpt_h1024_core_attn_tp2"])
+def test_attention_fwd_full_size_sampled(name):
+    w = synth.WORKLOADS[name]
+    x = synth.inputs_for(w)
+    hl, d, S = w.heads_local, w.head_dim, w.seq
+    print(f"case {name}: T={w.T} S={S} Hl={hl} d={d}", flush=True)
+    O, lse = tps.attention_fwd(x["QKV"].to(DEV), seq=S, heads=w.heads, head_dim=d, tp_size=w.tp)
+    torch.cuda.synchronize()
+    O, lse = f64(O), f64(lse)
+    Q, K, V = oracle.split_qkv(f64(x["QKV"]), hl, d)
+    for b, h in _sampled_pairs(w, 4):
+        rows = slice(b * S, (b + 1) * S)
+        Oh, lseh, _ = oracle.attention_head_fwd(Q[h, rows], K[h, rows], V[h, rows], causal=True)
+        print(f" sequence {b} head {h}", flush=True)
+        _rel("O", O[rows, h * d:(h + 1) * d], Oh)
+        _lse(lse[h, rows], lseh)
+
+
+def test_attention_fwd_deterministic_and_inference_mode():
+    w = synth.WORKLOADS["gpt_h1024_core_attn_tp2"]
+    x = synth.inputs_for(w)
+    q = x["QKV"].to(DEV)
+    kw = dict(seq=w.seq, heads=w.heads, head_dim=w.head_dim, tp_size=w.tp)
+    O1, l1 = tps.attention_fwd(q, **kw)
+    O2, l2 = tps.attention_fwd(q, **kw)
+    O3, l3 = tps.attention_fwd(q, save_lse=False, **kw)
+    torch.cuda.synchronize()
+    assert l3 is None
+    assert torch.equal(O1.view(torch.int16), O2.view(torch.int16))
+    assert torch.equal(l1, l2)
+    assert torch.equal(O1.view(torch.int16), O3.view(torch.int16))
