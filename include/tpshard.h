@@ -83,7 +83,8 @@ enum {
   TP_OP_COLUMN_LINEAR_BWD = 1,
   TP_OP_ROW_LINEAR_BWD = 2,
   TP_OP_MLP_SHARD_BWD = 3,
-  TP_OP_BIAS_GRAD = 4
+  TP_OP_BIAS_GRAD = 4,
+  TP_OP_ATTENTION_BWD = 5
 };
 
 /*
@@ -215,9 +216,24 @@ int tp_attention_fwd(const void* QKV_i, void* O_i, float* lse, int64_t T, int64_
                      int64_t head_dim, int32_t tp_size, int32_t causal, int32_t dtype, void* stream);
 
 /*
+ * Backward of tp_attention_fwd (the chain rule of the same definition; the
+ * pages give no backward formulas).  Inputs: QKV_i, O_i and lse as written by
+ * the forward with the same arguments, dO_i [T x Hl*head_dim] bf16.  Output:
+ * dQKV_i [T x 3*Hl*head_dim] bf16 in the same [Q | K | V] layout, which is
+ * the dY_i the QKV column shard's backward (tp_column_linear_bwd) takes.
+ * Computed without atomics (bitwise reproducible).  workspace: >=
+ * tp_workspace_size(TP_OP_ATTENTION_BWD, T, heads, head_dim, tp_size, TP_BF16)
+ * bytes (TP_ERR_WORKSPACE).  Errors as tp_attention_fwd; lse is required here.
+ */
+int tp_attention_bwd(const void* QKV_i, const void* O_i, const float* lse, const void* dO_i, void* dQKV_i,
+                     void* workspace, size_t workspace_bytes, int64_t T, int64_t seq, int64_t heads,
+                     int64_t head_dim, int32_t tp_size, int32_t causal, int32_t dtype, void* stream);
+
+/*
  * Workspace bytes needed by `op` (TP_OP_*).  Arguments are those of the
  * matching call: T, d_in, d_out = (T, K, N) for the linears, (T, h, F) for the
- * MLP, (T, N, unused) for the bias gradient.  Returns 0 for invalid arguments.
+ * MLP, (T, N, unused) for the bias gradient, (T, heads, head_dim) for the
+ * attention backward (dtype TP_BF16).  Returns 0 for invalid arguments.
  */
 size_t tp_workspace_size(int32_t op, int64_t T, int64_t d_in, int64_t d_out, int32_t tp_size,
                          int32_t dtype);

@@ -24,7 +24,7 @@ from ._native import NativeLibraryMissing  # noqa: F401
 __all__ = [
     "column_linear", "row_linear", "mlp_shard_fwd", "mlp_shard_bwd", "column_linear_bwd",
     "row_linear_bwd", "bias_grad", "bias_gelu", "workspace_size", "trace_start", "trace_stop",
-    "attention_fwd", "mfma_probe", "library_path", "NativeLibraryMissing",
+    "attention_fwd", "attention_bwd", "mfma_probe", "library_path", "NativeLibraryMissing",
 ]
 
 _DT = {torch.bfloat16: _native.TP_BF16, torch.float32: _native.TP_FP32}
@@ -274,6 +274,34 @@ def attention_fwd(qkv, *, seq: int, heads: int, head_dim: int, tp_size: int, cau
                                         int(causal), _native.TP_BF16, _stream(dev))
     _native.check(st, "tp_attention_fwd")
     return o, lse
+
+
+def attention_bwd(qkv, o, lse, dout, *, seq: int, heads: int, head_dim: int, tp_size: int, causal: bool = True,
+                  out=None, workspace=None):
+    """Backward of attention_fwd: -> dQKV [T x 3*Hl*d] (same [Q | K | V] layout as qkv)."""
+    T = qkv.shape[0]
+    hl = heads // tp_size if tp_size > 0 else 0
+    dev = qkv.device
+    w = hl * head_dim
+    _check("qkv", qkv, (T, 3 * w), torch.bfloat16, dev)
+    _check("o", o, (T, w), torch.bfloat16, dev)
+    _check("lse", lse, (hl, T), torch.float32, dev)
+    _check("dout", dout, (T, w), torch.bfloat16, dev)
+    dq = out if out is not None else torch.empty((T, 3 * w), dtype=torch.bfloat16, device=dev)
+    _check("out", dq, (T, 3 * w), torch.bfloat16, dev)
+    need = int(_native.lib().tp_workspace_size(_native.TP_OP_ATTENTION_BWD, T, heads, head_dim, tp_size,
+                                               _native.TP_BF16))
+    if workspace is not None:
+        if workspace.device != dev or workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace needs {need} bytes on {dev}")
+        ws = workspace
+    else:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    st = _native.lib().tp_attention_bwd(_ptr(qkv), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(ws),
+                                        ws.numel() * ws.element_size(), T, seq, heads, head_dim, tp_size,
+                                        int(causal), _native.TP_BF16, _stream(dev))
+    _native.check(st, "tp_attention_bwd")
+    return dq
 
 
 def trace_start(max_launches: int = 4096) -> None:

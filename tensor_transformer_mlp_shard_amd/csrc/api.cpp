@@ -220,6 +220,12 @@ size_t tp_workspace_size(int32_t op, int64_t T, int64_t d_in, int64_t d_out, int
                                                                           : colsum_ws_bytes(T, d_in);
       return dz + cs;
     }
+    case TP_OP_ATTENTION_BWD: {
+      // d_in = heads, d_out = head_dim: the row-dot Dt [Hl x T] fp32
+      if (dtype != TP_BF16 || tp_size < 1 || d_in < 1 || d_in > kMaxDim || d_in % tp_size) return 0;
+      if (d_out != 64 && d_out != 128) return 0;
+      return round_up((size_t)(d_in / tp_size) * (size_t)T * 4);
+    }
     default:
       return 0;
   }
@@ -436,6 +442,23 @@ int tp_attention_fwd(const void* QKV_i, void* O_i, float* lse, int64_t T, int64_
   const int64_t w = (int64_t)p.Hl * p.D;
   TP_TRY(check_alias({{QKV_i, T * 3 * w * 2}}, {{O_i, T * w * 2}, {lse, lse ? T * p.Hl * 4 : 0}}));
   HIP_TRY(attention_fwd((const bf16*)QKV_i, (bf16*)O_i, lse, p, (hipStream_t)stream));
+  return TP_OK;
+}
+
+int tp_attention_bwd(const void* QKV_i, const void* O_i, const float* lse, const void* dO_i, void* dQKV_i,
+                     void* workspace, size_t workspace_bytes, int64_t T, int64_t seq, int64_t heads,
+                     int64_t head_dim, int32_t tp_size, int32_t causal, int32_t dtype, void* stream) {
+  AttnProblem p;
+  TP_TRY(check_attention(T, seq, heads, head_dim, tp_size, causal, dtype, p));
+  TP_TRY(check_nonnull({QKV_i, O_i, lse, dO_i, dQKV_i}));
+  TP_TRY(check_ptrs_aligned({QKV_i, O_i, lse, dO_i, dQKV_i, workspace}));
+  const size_t need = tp_workspace_size(TP_OP_ATTENTION_BWD, T, heads, head_dim, tp_size, dtype);
+  if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
+  const int64_t w = (int64_t)p.Hl * p.D;
+  TP_TRY(check_alias({{QKV_i, T * 3 * w * 2}, {O_i, T * w * 2}, {lse, T * p.Hl * 4}, {dO_i, T * w * 2}},
+                     {{dQKV_i, T * 3 * w * 2}, {workspace, (int64_t)need}}));
+  HIP_TRY(attention_bwd((const bf16*)QKV_i, (const bf16*)O_i, lse, (const bf16*)dO_i, (bf16*)dQKV_i,
+                        (float*)workspace, p, (hipStream_t)stream));
   return TP_OK;
 }
 

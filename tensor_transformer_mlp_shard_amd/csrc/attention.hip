@@ -245,6 +245,333 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- backward
+//
+// With P the forward's probabilities (recomputed from the saved log-sum-exp),
+// dP = dO V^T and Dt = rowsum(dO * O) = rowsum(P * dP):
+//   dV = P^T dO,  dS = P * (dP - Dt),  dK = dS^T Q / sqrt(D),  dQ = dS K / sqrt(D).
+// Three kernels, no atomics (bitwise reproducible):
+//  * attn_bwd_dot: Dt for every (token, head);
+//  * attn_bwd_dkdv: a workgroup owns 128 keys (32 per wave, one per lane
+//    column); K and V of its keys stay in registers; queries stream through
+//    LDS in blocks of 64.  Scores are computed as S[query][key] so each lane
+//    holds one key's column, and P and dS feed dV^T += dO^T P and
+//    dK^T += Q^T dS from registers (queries in the accumulator order, dO^T and
+//    Q^T read from LDS with transposing reads in that order);
+//  * attn_bwd_dq: a workgroup owns 128 queries (32 per wave, one per lane
+//    column) as in the forward; keys and values stream through LDS in blocks
+//    of 64; S^T and dP^T = V dO^T give dS^T, which feeds dQ^T += K^T dS^T.
+
+struct BwdArgs {
+  const bf16* qkv;
+  const bf16* o;
+  const bf16* dout;
+  const float* lse;
+  float* dt;        // [Hl x T]
+  bf16* dqkv;
+  int64_t T;
+  int S, Hl, B, nb, causal;  // nb: 128-row blocks per sequence
+  float scale_log2;           // log2(e) / sqrt(D)
+  float scale;                // 1 / sqrt(D)
+};
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+// Dt[h, t] = sum_d dO[t, h, d] * O[t, h, d]; D/8 lanes per (token, head) row.
+template <int D>
+__global__ void __launch_bounds__(NT) attn_bwd_dot_kernel(BwdArgs a) {
+  constexpr int LPR = D / 8;  // lanes per row
+  const int64_t row = ((int64_t)blockIdx.x * NT + threadIdx.x) / LPR;   // token * Hl + head
+  const int part = threadIdx.x % LPR;
+  float s = 0.0f;
+  if (row < a.T * a.Hl) {
+    const bf16x8 o = *(const bf16x8*)(a.o + row * D + part * 8);
+    const bf16x8 g = *(const bf16x8*)(a.dout + row * D + part * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += (float)o[e] * (float)g[e];
+  }
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) s += __shfl_xor(s, m);
+  if (row < a.T * a.Hl && part == 0) {
+    const int64_t t = row / a.Hl;
+    const int h = (int)(row % a.Hl);
+    a.dt[(int64_t)h * a.T + t] = s;
+  }
+}
+
+// 16-byte operand of an MFMA from a k_slot-swizzled LDS block: row r, 16-wide
+// slice s, lane half hh (elements 16 s + 8 hh .. + 7).
+template <int D>
+__device__ __forceinline__ bf16x8 lds_row_frag(const char* blk, int r, int s, int hh) {
+  return *(const bf16x8*)(blk + r * Shape<D>::ROW_BYTES + k_slot<D>(2 * s + hh, r) * 16);
+}
+
+// Transposed operand from a k_slot-swizzled LDS block: columns 32 t + (0..31)
+// of rows 16 s + {4 hh + 0..3, 8 + 4 hh + 0..3} (the accumulator order).
+template <int D>
+__device__ __forceinline__ bf16x8 lds_tr_frag(const char* blk, int t, int s, int tr_r, int tr_c) {
+  const int col = 32 * t + tr_c;
+  const int ra = 16 * s + tr_r, rb = ra + 8;
+  const bf16x4 lo = read_tr(blk + ra * Shape<D>::ROW_BYTES + k_slot<D>(col >> 3, ra) * 16 + (col & 7) * 2);
+  const bf16x4 hi = read_tr(blk + rb * Shape<D>::ROW_BYTES + k_slot<D>(col >> 3, rb) * 16 + (col & 7) * 2);
+  bf16x8 v;
+  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+  return v;
+}
+
+// Two 64-row blocks (rows r0.. of the sequence; base / row stride of each) into
+// registers, zero past the sequence end, then into k_slot-swizzled LDS.
+template <int D>
+struct PairStager {
+  static constexpr int L = Shape<D>::LOADS;  // 16-byte loads per thread (both blocks)
+  bf16x8 st[L];
+  __device__ __forceinline__ void load(const bf16* base0, int64_t ld0, const bf16* base1, int64_t ld1, int r0, int S,
+                                       int tid) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int c = tid + NT * (i % (L / 2));
+      const int r = c / Shape<D>::CH, ch = c % Shape<D>::CH;
+      const bf16* src = i < L / 2 ? base0 + (int64_t)(r0 + r) * ld0 + ch * 8 : base1 + (int64_t)(r0 + r) * ld1 + ch * 8;
+      st[i] = (r0 + r < S) ? *(const bf16x8*)src : bf16x8{};
+    }
+  }
+  __device__ __forceinline__ void store(char* blk0, char* blk1, int tid) const {
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int c = tid + NT * (i % (L / 2));
+      const int r = c / Shape<D>::CH, ch = c % Shape<D>::CH;
+      *(bf16x8*)((i < L / 2 ? blk0 : blk1) + r * Shape<D>::ROW_BYTES + k_slot<D>(ch, r) * 16) = st[i];
+    }
+  }
+};
+
+template <int D>
+__global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
+  using SH = Shape<D>;
+  constexpr int QB = 64;  // queries per LDS block
+  __shared__ __attribute__((aligned(16))) char smem[2][2][SH::BLOCK_BYTES];  // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) float stat[2][2][QB];              // [buffer][lse2, Dt]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int bh = a.B * a.Hl;
+  const int kb = (int)(blockIdx.x / bh);           // causal: low key blocks have the most queries
+  const int b = (int)(blockIdx.x % bh) / a.Hl, h = (int)(blockIdx.x % bh) % a.Hl;
+  const int64_t ld = 3LL * a.Hl * D;
+  const int64_t row0 = (int64_t)b * a.S;
+  const bf16* qbase = a.qkv + row0 * ld + (int64_t)h * D;
+  const bf16* kbase = qbase + (int64_t)a.Hl * D;
+  const bf16* vbase = qbase + 2LL * a.Hl * D;
+  const bf16* dobase = a.dout + row0 * (int64_t)a.Hl * D + (int64_t)h * D;
+  const int64_t ldo = (int64_t)a.Hl * D;
+  const int kj = kb * 128 + wave * 32 + l32;      // this lane's key
+  const bool kvalid = kj < a.S;
+
+  // K and V of this lane's key as the B operand (k = d) of S and dP.
+  bf16x8 kf[SH::KS], vf[SH::KS];
+#pragma unroll
+  for (int s = 0; s < SH::KS; ++s) {
+    kf[s] = kvalid ? *(const bf16x8*)(kbase + (int64_t)kj * ld + 16 * s + 8 * hh) : bf16x8{};
+    vf[s] = kvalid ? *(const bf16x8*)(vbase + (int64_t)kj * ld + 16 * s + 8 * hh) : bf16x8{};
+  }
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int tr_r = 4 * (g16 >> 1) + (i16 >> 2);
+  const int tr_c = 16 * (g16 & 1) + 4 * (i16 & 3);
+
+  f32x16 dk[SH::DT], dv[SH::DT];
+#pragma unroll
+  for (int t = 0; t < SH::DT; ++t) { dk[t] = f32x16{}; dv[t] = f32x16{}; }
+
+  const int qstart = a.causal ? kb * 128 : 0;      // earlier queries see none of these keys
+  const int nqblk = (a.S - qstart + QB - 1) / QB;
+  PairStager<D> stg;
+  auto load_stats = [&](int buf, int q0) {
+    if (tid < QB) {
+      const int q = q0 + tid;
+      stat[buf][0][tid] = q < a.S ? a.lse[(int64_t)h * a.T + row0 + q] * LOG2E : INFINITY;
+      stat[buf][1][tid] = q < a.S ? a.dt[(int64_t)h * a.T + row0 + q] : 0.0f;
+    }
+  };
+  stg.load(qbase, ld, dobase, ldo, qstart, a.S, tid);
+  stg.store(smem[0][0], smem[0][1], tid);
+  load_stats(0, qstart);
+  __syncthreads();
+  for (int j = 0; j < nqblk; ++j) {
+    const int buf = j & 1;
+    const int q0 = qstart + j * QB;
+    if (j + 1 < nqblk) stg.load(qbase, ld, dobase, ldo, q0 + QB, a.S, tid);
+    const char* Qs = smem[buf][0];
+    const char* Gs = smem[buf][1];
+
+    // S[query][key] and dP[query][key] for queries 32 t + (0..31) of the block.
+    f32x16 sc[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < SH::KS; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sc[t] = mfma(lds_row_frag<D>(Qs, 32 * t + l32, s, hh), kf[s], sc[t]);
+        dp[t] = mfma(lds_row_frag<D>(Gs, 32 * t + l32, s, hh), vf[s], dp[t]);
+      }
+    // P and dS; this lane's entries are queries 32 t + 8 g + 4 hh + e.
+    const bool masked = a.causal && q0 < kb * 128 + wave * 32 + 31;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qo = 32 * t + 8 * g + 4 * hh;
+        const f32x4 l2 = *(const f32x4*)&stat[buf][0][qo];
+        const f32x4 dd = *(const f32x4*)&stat[buf][1][qo];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = 4 * g + e;
+          float p = __builtin_amdgcn_exp2f(sc[t][v] * a.scale_log2 - l2[e]);
+          if (masked && kj > q0 + qo + e) p = 0.0f;
+          sc[t][v] = p;
+          dp[t][v] = p * (dp[t][v] - dd[e]);
+        }
+      }
+    bf16x8 pf[4], sf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        pf[s][m] = (bf16)sc[s >> 1][8 * (s & 1) + m];
+        sf[s][m] = (bf16)dp[s >> 1][8 * (s & 1) + m];
+      }
+    // dV^T += dO^T P, dK^T += Q^T dS (k = the block's queries in accumulator order).
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int t = 0; t < SH::DT; ++t) {
+        dv[t] = mfma(lds_tr_frag<D>(Gs, t, s, tr_r, tr_c), pf[s], dv[t]);
+        dk[t] = mfma(lds_tr_frag<D>(Qs, t, s, tr_r, tr_c), sf[s], dk[t]);
+      }
+    if (j + 1 < nqblk) {
+      stg.store(smem[buf ^ 1][0], smem[buf ^ 1][1], tid);
+      load_stats(buf ^ 1, q0 + QB);
+    }
+    __syncthreads();
+  }
+
+  if (kvalid) {
+    bf16* krow = a.dqkv + (row0 + kj) * ld + (int64_t)a.Hl * D + (int64_t)h * D;
+    bf16* vrow = krow + (int64_t)a.Hl * D;
+#pragma unroll
+    for (int t = 0; t < SH::DT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 k4, v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          k4[e] = (bf16)(dk[t][4 * g + e] * a.scale);
+          v4[e] = (bf16)dv[t][4 * g + e];
+        }
+        *(bf16x4*)(krow + 32 * t + 8 * g + 4 * hh) = k4;
+        *(bf16x4*)(vrow + 32 * t + 8 * g + 4 * hh) = v4;
+      }
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(NT, 1) attn_bwd_dq_kernel(BwdArgs a) {
+  using SH = Shape<D>;
+  __shared__ __attribute__((aligned(16))) char smem[2][2][SH::BLOCK_BYTES];  // [buffer][K, V]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int bh = a.B * a.Hl;
+  const int qb = a.nb - 1 - (int)(blockIdx.x / bh);  // longest causal query blocks first
+  const int b = (int)(blockIdx.x % bh) / a.Hl, h = (int)(blockIdx.x % bh) % a.Hl;
+  const int64_t ld = 3LL * a.Hl * D;
+  const int64_t row0 = (int64_t)b * a.S;
+  const bf16* qbase = a.qkv + row0 * ld + (int64_t)h * D;
+  const bf16* kbase = qbase + (int64_t)a.Hl * D;
+  const bf16* vbase = qbase + 2LL * a.Hl * D;
+  const int64_t ldo = (int64_t)a.Hl * D;
+  const bf16* dobase = a.dout + row0 * ldo + (int64_t)h * D;
+  const int q0 = qb * BQ;
+  const int wq0 = q0 + wave * QW;
+  const int qi = wq0 + l32;
+  const bool qvalid = qi < a.S;
+  const int kend = a.causal ? min(a.S, q0 + BQ) : a.S;
+  const int nkb = (kend + BKEYS - 1) / BKEYS;
+
+  // Q and dO of this lane's query as the B operand (k = d) of S^T and dP^T.
+  bf16x8 qf[SH::KS], gf[SH::KS];
+#pragma unroll
+  for (int s = 0; s < SH::KS; ++s) {
+    qf[s] = qvalid ? *(const bf16x8*)(qbase + (int64_t)qi * ld + 16 * s + 8 * hh) : bf16x8{};
+    gf[s] = qvalid ? *(const bf16x8*)(dobase + (int64_t)qi * ldo + 16 * s + 8 * hh) : bf16x8{};
+  }
+  const float lse2 = qvalid ? a.lse[(int64_t)h * a.T + row0 + qi] * LOG2E : INFINITY;
+  const float dti = qvalid ? a.dt[(int64_t)h * a.T + row0 + qi] : 0.0f;
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int tr_r = 4 * (g16 >> 1) + (i16 >> 2);
+  const int tr_c = 16 * (g16 & 1) + 4 * (i16 & 3);
+
+  f32x16 dq[SH::DT];
+#pragma unroll
+  for (int t = 0; t < SH::DT; ++t) dq[t] = f32x16{};
+
+  PairStager<D> stg;
+  stg.load(kbase, ld, vbase, ld, 0, a.S, tid);
+  stg.store(smem[0][0], smem[0][1], tid);
+  __syncthreads();
+  for (int j = 0; j < nkb; ++j) {
+    const int buf = j & 1;
+    const int k0 = j * BKEYS;
+    if (j + 1 < nkb) stg.load(kbase, ld, vbase, ld, k0 + BKEYS, a.S, tid);
+    const char* Ks = smem[buf][0];
+    const char* Vs = smem[buf][1];
+
+    // S^T[key][query] and dP^T[key][query] = (V dO^T) for keys 32 t + (0..31).
+    f32x16 sc[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < SH::KS; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sc[t] = mfma(lds_row_frag<D>(Ks, 32 * t + l32, s, hh), qf[s], sc[t]);
+        dp[t] = mfma(lds_row_frag<D>(Vs, 32 * t + l32, s, hh), gf[s], dp[t]);
+      }
+    const bool masked = (k0 + BKEYS > a.S) || (a.causal && k0 + BKEYS - 1 > wq0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float p = __builtin_amdgcn_exp2f(sc[t][v] * a.scale_log2 - lse2);
+        if (masked) {
+          const int key = k0 + 32 * t + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (key >= a.S || (a.causal && key > qi)) p = 0.0f;
+        }
+        dp[t][v] = p * (dp[t][v] - dti);
+      }
+    bf16x8 sf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) sf[s][m] = (bf16)dp[s >> 1][8 * (s & 1) + m];
+    // dQ^T += K^T dS^T (k = the block's keys in accumulator order).
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int t = 0; t < SH::DT; ++t) dq[t] = mfma(lds_tr_frag<D>(Ks, t, s, tr_r, tr_c), sf[s], dq[t]);
+    if (j + 1 < nkb) stg.store(smem[buf ^ 1][0], smem[buf ^ 1][1], tid);
+    __syncthreads();
+  }
+
+  if (qvalid) {
+    bf16* qrow = a.dqkv + (row0 + qi) * ld + (int64_t)h * D;
+#pragma unroll
+    for (int t = 0; t < SH::DT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 q4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q4[e] = (bf16)(dq[t][4 * g + e] * a.scale);
+        *(bf16x4*)(qrow + 32 * t + 8 * g + 4 * hh) = q4;
+      }
+  }
+}
+
 }  // namespace
 
 double attention_fwd_flops(const AttnProblem& p) {
@@ -276,9 +603,50 @@ hipError_t attention_fwd(const bf16* qkv, bf16* o, float* lse, const AttnProblem
   return hipGetLastError();
 }
 
-hipError_t attention_bwd(const bf16*, const bf16*, const float*, const bf16*, bf16*, float*, const AttnProblem&,
-                         hipStream_t) {
-  return hipErrorNotSupported;
+
+hipError_t attention_bwd(const bf16* qkv, const bf16* o, const float* lse, const bf16* dout, bf16* dqkv,
+                         float* ws, const AttnProblem& p, hipStream_t s) {
+  BwdArgs a;
+  a.qkv = qkv;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dt = ws;
+  a.dqkv = dqkv;
+  a.T = p.T;
+  a.S = p.S;
+  a.Hl = p.Hl;
+  a.B = (int)(p.T / p.S);
+  a.nb = (p.S + 127) / 128;
+  a.causal = p.causal ? 1 : 0;
+  a.scale = (float)(1.0 / std::sqrt((double)p.D));
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p.D));
+  const double el = 2.0 * p.T * p.Hl * p.D;   // bytes of one [T x Hl*D] bf16 tensor
+  const bool d128 = p.D == 128;
+  const dim3 grid_dot((unsigned)((p.T * p.Hl * (p.D / 8) + NT - 1) / NT));
+  LaunchInfo i0{d128 ? "attn_bwd_dot_d128" : "attn_bwd_dot_d64", 0.0, 2.0 * el + 4.0 * p.T * p.Hl};
+  trace_begin(s);
+  if (d128) hipLaunchKernelGGL(attn_bwd_dot_kernel<128>, grid_dot, dim3(NT), 0, s, a);
+  else hipLaunchKernelGGL(attn_bwd_dot_kernel<64>, grid_dot, dim3(NT), 0, s, a);
+  trace_end(s, i0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const double f = attention_fwd_flops(p);   // 2 products per allowed pair
+  const dim3 grid((unsigned)((int64_t)a.nb * a.B * a.Hl));
+  // dK, dV: S, dP, dV, dK (4 products); dQ: S^T, dP^T, dQ (3 products)
+  LaunchInfo i1{d128 ? "attn_bwd_dkdv_d128" : "attn_bwd_dkdv_d64", 2.0 * f, 3.0 * el + 4.0 * 2 * p.T * p.Hl + 2.0 * el};
+  trace_begin(s);
+  if (d128) hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, grid, dim3(NT), 0, s, a);
+  else hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, grid, dim3(NT), 0, s, a);
+  trace_end(s, i1);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  LaunchInfo i2{d128 ? "attn_bwd_dq_d128" : "attn_bwd_dq_d64", 1.5 * f, 3.0 * el + 4.0 * 2 * p.T * p.Hl + el};
+  trace_begin(s);
+  if (d128) hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, grid, dim3(NT), 0, s, a);
+  else hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, grid, dim3(NT), 0, s, a);
+  trace_end(s, i2);
+  return hipGetLastError();
 }
 
 }  // namespace tps

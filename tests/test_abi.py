@@ -176,3 +176,22 @@ def test_attention_fwd_validation(lib):
     assert f(A0, A0, A2, 256, 128, 4, 64, 2, 1, 0, S) == -6          # O aliases QKV
     assert f(A0, A1, P(A1.value + 256), 256, 128, 4, 64, 2, 1, 0, S) == -6   # lse inside O
     assert f(A0, A1, A2, 1 << 20, 1 << 20, 3 * 4096, 128, 1, 1, 0, S) == -2  # QKV wider than 2^21
+
+
+def test_attention_bwd_validation(lib):
+    f = lib.tp_attention_bwd
+    QKV, O, L, G, DQ, WS = (P(0x1000000 * (i + 1)) for i in range(6))
+    need = lib.tp_workspace_size(_native.TP_OP_ATTENTION_BWD, 256, 4, 64, 2, 0)
+    assert need >= 2 * 256 * 4
+    assert lib.tp_workspace_size(_native.TP_OP_ATTENTION_BWD, 256, 4, 64, 2, 1) == 0      # fp32
+    assert lib.tp_workspace_size(_native.TP_OP_ATTENTION_BWD, 256, 4, 96, 2, 0) == 0      # head_dim
+    assert lib.tp_workspace_size(_native.TP_OP_ATTENTION_BWD, 256, 5, 64, 2, 0) == 0      # heads % tp
+    args = (256, 128, 4, 64, 2, 1, 0, S)
+    assert f(QKV, O, L, G, DQ, WS, need - 1, *args) == -7
+    assert f(QKV, O, L, G, DQ, None, need, *args) == -7
+    assert f(QKV, O, None, G, DQ, WS, need, *args) == -1                                  # lse required
+    assert f(QKV, O, L, None, DQ, WS, need, *args) == -1
+    assert f(QKV, O, L, G, QKV, WS, need, *args) == -6                                    # dQKV aliases QKV
+    assert f(QKV, O, L, G, DQ, P(DQ.value + 4096), need, *args) == -6                     # workspace inside dQKV
+    assert f(QKV, O, L, G, DQ, WS, need, 256, 128, 4, 64, 2, 1, 1, S) == -5
+    assert f(QKV, O, L, G, DQ, WS, need, 256, 100, 4, 64, 2, 1, 0, S) == -2
