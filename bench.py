@@ -14,8 +14,10 @@ peak (2.5 PFLOP/s).
 
 Prints one JSON line.  Extra fields: per-part times, a roofline entry for the
 kernel with the most time in the step (timed with HIP events around its
-launches by the library's trace), and the fp64 CPU oracle timed on a bounded
-sample of the same workload.
+launches by the library's trace), the register-only matrix-core probe, the
+fp64 CPU oracle timed on a bounded sample of the same workload, and, outside
+the step, core attention on the rank's local heads (175B shape: 4 sequences of
+2048 tokens, 12 heads of 128, causal) forward and backward.
 """
 from __future__ import annotations
 
@@ -99,6 +101,65 @@ class Shard:
     def step(self):
         self.mlp_step()
         self.attn_step()
+
+
+class CoreAttention:
+    """Core attention on the rank's local heads, 175B shape at TP=8: 4 sequences
+    of 2048 tokens, 12 local heads of 128, causal; forward and backward."""
+
+    def __init__(self, device):
+        import torch
+
+        import tensor_transformer_mlp_shard_amd as tps
+        from tensor_transformer_mlp_shard_amd import _native, synth
+
+        self.tps = tps
+        w = synth.WORKLOADS["gpt175b_core_attn_tp8"]
+        self.w = w
+        x = synth.inputs_for(w)
+        self.qkv, self.dO = x["QKV"].to(device), x["dO"].to(device)
+        W = w.heads_local * w.head_dim
+        self.O = torch.empty((w.T, W), dtype=torch.bfloat16, device=device)
+        self.dqkv = torch.empty((w.T, 3 * W), dtype=torch.bfloat16, device=device)
+        self.ws = torch.empty((tps.workspace_size(_native.TP_OP_ATTENTION_BWD, w.T, w.heads, w.head_dim, w.tp,
+                                                  torch.bfloat16),), dtype=torch.uint8, device=device)
+        self.kw = dict(seq=w.seq, heads=w.heads, head_dim=w.head_dim, tp_size=w.tp, causal=True)
+        pairs = w.seq * (w.seq + 1) / 2 * (w.T // w.seq) * w.heads_local
+        self.flops_fwd = 4.0 * w.head_dim * pairs            # Q K^T and P V
+        self.flops_bwd = 2.5 * self.flops_fwd                # dV, dP, dQ, dK (+ S recomputed: not counted)
+        self.lse = None
+        self.fwd()
+
+    def fwd(self):
+        _, self.lse = self.tps.attention_fwd(self.qkv, out=self.O, **self.kw)
+
+    def bwd(self):
+        self.tps.attention_bwd(self.qkv, self.O, self.lse, self.dO, out=self.dqkv, workspace=self.ws, **self.kw)
+
+    def step(self):
+        self.fwd()
+        self.bwd()
+
+
+def measure_core_attention(torch, device, steps, warmup):
+    ca = CoreAttention(device)
+    out = {"workload": "175B TP=8 core attention: 4 x 2048 tokens, 12 local heads of 128, causal, bf16",
+           "flop_fwd": ca.flops_fwd, "flop_bwd": ca.flops_bwd}
+    for name, fn, fl in (("fwd", ca.fwd, ca.flops_fwd), ("bwd", ca.bwd, ca.flops_bwd),
+                         ("fwd_bwd", ca.step, ca.flops_fwd + ca.flops_bwd)):
+        ms, _ = time_steps(torch, fn, steps, warmup)
+        out[name] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                     "pct_peak": round(100 * fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2)}
+    ca.tps.trace_start(4096)
+    for _ in range(steps):
+        ca.step()
+    torch.cuda.synchronize()
+    out["kernels"] = [{"name": k["name"], "launches_per_step": k["launches"] // steps,
+                       "ms_per_step": round(k["total_ms"] / steps, 4),
+                       "tflops": round(k["flops"] / (k["total_ms"] * 1e-3) / 1e12, 1) if k["flops"] else None,
+                       "gbs": round(k["bytes"] / (k["total_ms"] * 1e-3) / 1e9, 1)}
+                      for k in ca.tps.trace_stop()]
+    return out
 
 
 def time_steps(torch, fn, steps, warmup):
@@ -194,7 +255,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frac", type=int, default=1, help="oracle sample = 1/N of the tokens")
-    ap.add_argument("--part", choices=["all", "mlp", "attn"], default="all",
+    ap.add_argument("--part", choices=["all", "mlp", "attn", "core_attn"], default="all",
                     help="run only one part (for profiling runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of this many MiB, three times (a known-size "
@@ -222,6 +283,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.part == "core_attn":
+        print(json.dumps({"core_attention": measure_core_attention(torch, device, args.steps, args.warmup)}),
+              flush=True)
+        return
     shard = Shard(device)
     fn = {"all": shard.step, "mlp": shard.mlp_step, "attn": shard.attn_step}[args.part]
     flops = {"all": shard.flops_mlp + shard.flops_attn, "mlp": shard.flops_mlp, "attn": shard.flops_attn}[args.part]
@@ -288,6 +353,8 @@ def main():
                        "note": "register-only bf16 MFMA stream on random operands, no memory traffic"},
         "kernels": kern,
     }
+    if args.part == "all":
+        out["core_attention"] = measure_core_attention(torch, device, min(args.steps, 50), min(args.warmup, 10))
     if not args.no_cpu_baseline and args.part == "all":
         out["cpu_baseline"] = cpu_baseline(shard, args.cpu_frac)
     print(json.dumps(out), flush=True)
