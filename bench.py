@@ -162,6 +162,37 @@ def measure_core_attention(torch, device, steps, warmup):
     return out
 
 
+def measure_recompute(torch, shard, steps, warmup):
+    """MLP shard fwd+bwd with all activations saved against the two selective
+    recompute forms: Z kept (H recomputed by an elementwise GeLU) and nothing
+    kept (Z and H recomputed by the fc1 GEMM).  Reports the time overhead and
+    the activation bytes each form keeps between forward and backward."""
+    tps = shard.tps
+    wm = shard.wm
+    p = wm.tp
+    o = shard.fwd_out
+    ws = torch.empty((tps.workspace_size(tps._native.TP_OP_MLP_SHARD_BWD_RECOMPUTE, wm.T, wm.h, wm.F, p,
+                                         torch.bfloat16),), dtype=torch.uint8, device=shard.X.device)
+
+    def keep_z():
+        tps.mlp_shard_fwd(shard.X, shard.A, shard.b1, shard.B, tp_size=p, out=o)
+        tps.mlp_shard_bwd(shard.X, shard.A, shard.B, o["Z"], None, shard.dY, tp_size=p, want_db2=True,
+                          out=shard.bwd_out, workspace=ws, recompute=True)
+
+    def keep_none():
+        tps.mlp_shard_fwd(shard.X, shard.A, shard.b1, shard.B, tp_size=p, save_z=False, out=o)
+        tps.mlp_shard_bwd(shard.X, shard.A, shard.B, None, None, shard.dY, tp_size=p, want_db2=True,
+                          out=shard.bwd_out, workspace=ws, recompute=True, b1_i=shard.b1)
+
+    act = wm.T * wm.f * 2
+    base, _ = time_steps(torch, shard.mlp_step, steps, warmup)
+    out = {"saved_Z_and_H": {"ms": round(base, 4), "kept_bytes": 2 * act}}
+    for name, fn, kept in (("saved_Z_recompute_H", keep_z, act), ("saved_none_recompute_fc1", keep_none, 0)):
+        ms, _ = time_steps(torch, fn, steps, warmup)
+        out[name] = {"ms": round(ms, 4), "kept_bytes": kept, "overhead_pct": round(100 * (ms / base - 1), 2)}
+    return out
+
+
 def time_steps(torch, fn, steps, warmup):
     for _ in range(warmup):
         fn()
@@ -354,6 +385,7 @@ def main():
         "kernels": kern,
     }
     if args.part == "all":
+        out["selective_recompute"] = measure_recompute(torch, shard, min(args.steps, 50), min(args.warmup, 10))
         out["core_attention"] = measure_core_attention(torch, device, min(args.steps, 50), min(args.warmup, 10))
     if not args.no_cpu_baseline and args.part == "all":
         out["cpu_baseline"] = cpu_baseline(shard, args.cpu_frac)

@@ -84,7 +84,8 @@ enum {
   TP_OP_ROW_LINEAR_BWD = 2,
   TP_OP_MLP_SHARD_BWD = 3,
   TP_OP_BIAS_GRAD = 4,
-  TP_OP_ATTENTION_BWD = 5
+  TP_OP_ATTENTION_BWD = 5,
+  TP_OP_MLP_SHARD_BWD_RECOMPUTE = 6
 };
 
 /*
@@ -148,6 +149,26 @@ int tp_mlp_shard_bwd(const void* X, const void* A_i, const void* B_i, const void
                      float* dB_i, float* db2, void* workspace, size_t workspace_bytes,
                      int32_t accumulate, int64_t T, int64_t h, int64_t F, int32_t tp_size,
                      int32_t dtype, void* stream);
+
+/*
+ * MLP shard backward with selective activation recompute ([TUT] "融合优化技术"
+ * and "高级特性 / 选择性激活重计算": keep fewer activations from the forward
+ * and recompute the rest in the backward, trading compute for memory).
+ * Same outputs and conventions as tp_mlp_shard_bwd; the forward's saved
+ * activations are replaced by:
+ *   Z_i non-NULL: only the pre-activation was kept; H_i = GeLU(Z_i) is
+ *                 recomputed by one elementwise pass (H_i need not be kept);
+ *   Z_i NULL:     nothing was kept; Z_i and H_i are recomputed by the
+ *                 forward's fused fc1 GEMM (X A_i + b1_i, then GeLU), which
+ *                 needs b1_i (NULL = no bias) -- bitwise the forward's values.
+ * The recomputed tensors live in the workspace: >= tp_workspace_size(
+ * TP_OP_MLP_SHARD_BWD_RECOMPUTE, T, h, F, p, dtype) bytes.
+ */
+int tp_mlp_shard_bwd_recompute(const void* X, const void* A_i, const void* b1_i, const void* B_i,
+                               const void* Z_i, const void* dY, void* dX_i, float* dA_i, float* db1_i,
+                               float* dB_i, float* db2, void* workspace, size_t workspace_bytes,
+                               int32_t accumulate, int64_t T, int64_t h, int64_t F, int32_t tp_size,
+                               int32_t dtype, void* stream);
 
 /*
  * Column-parallel linear, backward (no activation; for the GeLU layer use
@@ -232,7 +253,7 @@ int tp_attention_bwd(const void* QKV_i, const void* O_i, const float* lse, const
 /*
  * Workspace bytes needed by `op` (TP_OP_*).  Arguments are those of the
  * matching call: T, d_in, d_out = (T, K, N) for the linears, (T, h, F) for the
- * MLP, (T, N, unused) for the bias gradient, (T, heads, head_dim) for the
+ * MLP and its recompute form, (T, N, unused) for the bias gradient, (T, heads, head_dim) for the
  * attention backward (dtype TP_BF16).  Returns 0 for invalid arguments.
  */
 size_t tp_workspace_size(int32_t op, int64_t T, int64_t d_in, int64_t d_out, int32_t tp_size,

@@ -145,16 +145,30 @@ def mlp_shard_fwd(x, a_i, b1_i, b_i, *, tp_size: int, save_z: bool = True, out=N
 
 
 def mlp_shard_bwd(x, a_i, b_i, z_i, h_i, dy, *, tp_size: int, want_db1: bool = True, want_db2: bool = False,
-                  accumulate: bool = False, out=None, workspace=None):
+                  accumulate: bool = False, out=None, workspace=None, recompute: bool = False, b1_i=None):
     """MLP shard backward.  Returns dict(dX, dA, db1, dB, db2) (db1 / db2 None
     unless wanted).  With ``accumulate`` the fp32 parameter gradients in ``out``
-    ("dA", "dB", "db1", "db2") are added to instead of overwritten."""
+    ("dA", "dB", "db1", "db2") are added to instead of overwritten.
+
+    ``recompute=True`` selects the selective-recompute form
+    (tp_mlp_shard_bwd_recompute): ``h_i`` must be None; with ``z_i`` given, H is
+    recomputed from it; with ``z_i`` None too, Z and H are recomputed from
+    ``x`` by the fc1 GEMM with bias ``b1_i``."""
     T, h = x.shape
     f = a_i.shape[1]
     dt = x.dtype
     dev = x.device
-    for name, t, shp in (("x", x, (T, h)), ("a_i", a_i, (h, f)), ("b_i", b_i, (f, h)), ("z_i", z_i, (T, f)),
-                         ("h_i", h_i, (T, f)), ("dy", dy, (T, h))):
+    checks = [("x", x, (T, h)), ("a_i", a_i, (h, f)), ("b_i", b_i, (f, h)), ("dy", dy, (T, h))]
+    if recompute:
+        if h_i is not None:
+            raise ValueError("recompute=True takes no saved h_i")
+        if z_i is not None:
+            checks.append(("z_i", z_i, (T, f)))
+        if b1_i is not None:
+            checks.append(("b1_i", b1_i, (f,)))
+    else:
+        checks += [("z_i", z_i, (T, f)), ("h_i", h_i, (T, f))]
+    for name, t, shp in checks:
         _check(name, t, shp, dt, dev)
     out = dict(out or {})
     if accumulate:
@@ -174,11 +188,20 @@ def mlp_shard_bwd(x, a_i, b_i, z_i, h_i, dy, *, tp_size: int, want_db1: bool = T
     dB = get("dB", (f, h), torch.float32)
     db1 = get("db1", (f,), torch.float32) if want_db1 else None
     db2 = get("db2", (h,), torch.float32) if want_db2 else None
-    ws = _workspace(_native.TP_OP_MLP_SHARD_BWD, T, h, f * tp_size, tp_size, dt, dev, workspace)
-    st = _native.lib().tp_mlp_shard_bwd(
-        _ptr(x), _ptr(a_i), _ptr(b_i), _ptr(z_i), _ptr(h_i), _ptr(dy), _ptr(dX), _ptr(dA), _ptr(db1), _ptr(dB),
-        _ptr(db2), _ptr(ws), ws.numel(), int(accumulate), T, h, f * tp_size, tp_size, _dtype_code(x), _stream(dev))
-    _native.check(st, "tp_mlp_shard_bwd")
+    if recompute:
+        ws = _workspace(_native.TP_OP_MLP_SHARD_BWD_RECOMPUTE, T, h, f * tp_size, tp_size, dt, dev, workspace)
+        st = _native.lib().tp_mlp_shard_bwd_recompute(
+            _ptr(x), _ptr(a_i), _ptr(b1_i), _ptr(b_i), _ptr(z_i), _ptr(dy), _ptr(dX), _ptr(dA), _ptr(db1),
+            _ptr(dB), _ptr(db2), _ptr(ws), ws.numel(), int(accumulate), T, h, f * tp_size, tp_size,
+            _dtype_code(x), _stream(dev))
+        _native.check(st, "tp_mlp_shard_bwd_recompute")
+    else:
+        ws = _workspace(_native.TP_OP_MLP_SHARD_BWD, T, h, f * tp_size, tp_size, dt, dev, workspace)
+        st = _native.lib().tp_mlp_shard_bwd(
+            _ptr(x), _ptr(a_i), _ptr(b_i), _ptr(z_i), _ptr(h_i), _ptr(dy), _ptr(dX), _ptr(dA), _ptr(db1),
+            _ptr(dB), _ptr(db2), _ptr(ws), ws.numel(), int(accumulate), T, h, f * tp_size, tp_size,
+            _dtype_code(x), _stream(dev))
+        _native.check(st, "tp_mlp_shard_bwd")
     return {"dX": dX, "dA": dA, "db1": db1, "dB": dB, "db2": db2}
 
 

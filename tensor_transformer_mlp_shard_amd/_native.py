@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpshard.
 TP_BF16, TP_FP32 = 0, 1
 TP_ACT_NONE, TP_ACT_GELU = 0, 1
 TP_OP_COLUMN_LINEAR_BWD, TP_OP_ROW_LINEAR_BWD, TP_OP_MLP_SHARD_BWD, TP_OP_BIAS_GRAD = 1, 2, 3, 4
-TP_OP_ATTENTION_BWD = 5
+TP_OP_ATTENTION_BWD, TP_OP_MLP_SHARD_BWD_RECOMPUTE = 5, 6
 STATUS = {
     0: "TP_OK", -1: "TP_ERR_NULLPTR", -2: "TP_ERR_DIM", -3: "TP_ERR_TP_DIVISIBILITY",
     -4: "TP_ERR_ALIGNMENT", -5: "TP_ERR_DTYPE", -6: "TP_ERR_ALIAS", -7: "TP_ERR_WORKSPACE",
@@ -30,6 +30,8 @@ PROTOTYPES = {
     "tp_mlp_shard_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i32, _i32, _p]),
     "tp_mlp_shard_bwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _fp, _fp, _fp, _fp, _p, _sz, _i32,
                                 _i64, _i64, _i64, _i32, _i32, _p]),
+    "tp_mlp_shard_bwd_recompute": (_i32, [_p, _p, _p, _p, _p, _p, _p, _fp, _fp, _fp, _fp, _p, _sz, _i32,
+                                          _i64, _i64, _i64, _i32, _i32, _p]),
     "tp_column_linear_bwd": (_i32, [_p, _p, _p, _p, _fp, _fp, _p, _sz, _i32, _i64, _i64, _i64, _i32, _i32, _p]),
     "tp_row_linear_bwd": (_i32, [_p, _p, _p, _p, _fp, _fp, _p, _sz, _i32, _i64, _i64, _i64, _i32, _i32, _p]),
     "tp_bias_grad": (_i32, [_p, _fp, _p, _sz, _i32, _i64, _i64, _i32, _p]),

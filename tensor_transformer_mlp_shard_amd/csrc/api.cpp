@@ -220,6 +220,15 @@ size_t tp_workspace_size(int32_t op, int64_t T, int64_t d_in, int64_t d_out, int
                                                                           : colsum_ws_bytes(T, d_in);
       return dz + cs;
     }
+    case TP_OP_MLP_SHARD_BWD_RECOMPUTE: {
+      // dZ, H and (when Z is not saved) Z [T x f], then the column-sum partials
+      if (tp_size < 1 || d_in < 1 || d_out < 1 || d_in > kMaxDim || d_out > kMaxDim || d_out % tp_size) return 0;
+      const int64_t f = d_out / tp_size;
+      const size_t act = round_up((size_t)T * (size_t)f * elsize(dtype));
+      const size_t cs = colsum_ws_bytes(T, f) > colsum_ws_bytes(T, d_in) ? colsum_ws_bytes(T, f)
+                                                                          : colsum_ws_bytes(T, d_in);
+      return 3 * act + cs;
+    }
     case TP_OP_ATTENTION_BWD: {
       // d_in = heads, d_out = head_dim: the row-dot Dt [Hl x T] fp32
       if (dtype != TP_BF16 || tp_size < 1 || d_in < 1 || d_in > kMaxDim || d_in % tp_size) return 0;
@@ -297,31 +306,10 @@ int tp_mlp_shard_fwd(const void* X, const void* A_i, const void* b1_i, const voi
   return TP_OK;
 }
 
-int tp_mlp_shard_bwd(const void* X, const void* A_i, const void* B_i, const void* Z_i, const void* H_i,
-                     const void* dY, void* dX_i, float* dA_i, float* db1_i, float* dB_i, float* db2,
-                     void* workspace, size_t workspace_bytes, int32_t accumulate, int64_t T, int64_t h, int64_t F,
-                     int32_t tp_size, int32_t dtype, void* stream) {
-  TP_TRY(check_dtype(dtype));
-  if (accumulate != 0 && accumulate != 1) return TP_ERR_ARG;
-  TP_TRY(check_nonnull({X, A_i, B_i, Z_i, H_i, dY, dX_i, dA_i, dB_i}));
-  TP_TRY(check_dims({T, h, F}));
-  if (tp_size < 1 || F % tp_size) return TP_ERR_TP_DIVISIBILITY;
-  const int64_t f = F / tp_size;
-  TP_TRY(check_feature({h, f}));
-  TP_TRY(check_elems({{T, h}, {h, f}, {T, f}}));
-  TP_TRY(check_ptrs_aligned({X, A_i, B_i, Z_i, H_i, dY, dX_i, dA_i, db1_i, dB_i, db2, workspace}));
-  const size_t need = tp_workspace_size(TP_OP_MLP_SHARD_BWD, T, h, F, tp_size, dtype);
-  if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
-  const int64_t es = elsize(dtype);
-  TP_TRY(check_alias({{X, T * h * es}, {A_i, h * f * es}, {B_i, f * h * es}, {Z_i, T * f * es},
-                      {H_i, T * f * es}, {dY, T * h * es}},
-                     {{dX_i, T * h * es}, {dA_i, h * f * 4}, {db1_i, db1_i ? f * 4 : 0}, {dB_i, f * h * 4},
-                      {db2, db2 ? h * 4 : 0}, {workspace, (int64_t)need}}));
-  hipStream_t s = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  void* dZ = ws;
-  float* part = (float*)(ws + round_up((size_t)T * (size_t)f * es));
-
+// The backward GEMM sequence shared by tp_mlp_shard_bwd and its recompute form.
+static int mlp_bwd_gemms(const void* X, const void* A_i, const void* B_i, const void* Z_i, const void* H_i, const void* dY,
+                  void* dX_i, float* dA_i, float* db1_i, float* dB_i, float* db2, void* dZ, float* part,
+                  int32_t accumulate, int64_t T, int64_t h, int64_t f, int32_t dtype, hipStream_t s) {
   // dZ = (dY B_i^T) * GeLU'(Z_i)          [T x f], contraction over h
   GemmArgs g1 = make_args(dY, h, B_i, h, T, f, h, dZ, f);
   g1.aux = Z_i;
@@ -342,6 +330,76 @@ int tp_mlp_shard_bwd(const void* X, const void* A_i, const void* B_i, const void
   if (db1_i) HIP_TRY(colsum(dZ, dtype == TP_BF16, db1_i, part, accumulate, T, f, s));
   if (db2) HIP_TRY(colsum(dY, dtype == TP_BF16, db2, part, accumulate, T, h, s));
   return TP_OK;
+}
+
+int tp_mlp_shard_bwd(const void* X, const void* A_i, const void* B_i, const void* Z_i, const void* H_i,
+                     const void* dY, void* dX_i, float* dA_i, float* db1_i, float* dB_i, float* db2,
+                     void* workspace, size_t workspace_bytes, int32_t accumulate, int64_t T, int64_t h, int64_t F,
+                     int32_t tp_size, int32_t dtype, void* stream) {
+  TP_TRY(check_dtype(dtype));
+  if (accumulate != 0 && accumulate != 1) return TP_ERR_ARG;
+  TP_TRY(check_nonnull({X, A_i, B_i, Z_i, H_i, dY, dX_i, dA_i, dB_i}));
+  TP_TRY(check_dims({T, h, F}));
+  if (tp_size < 1 || F % tp_size) return TP_ERR_TP_DIVISIBILITY;
+  const int64_t f = F / tp_size;
+  TP_TRY(check_feature({h, f}));
+  TP_TRY(check_elems({{T, h}, {h, f}, {T, f}}));
+  TP_TRY(check_ptrs_aligned({X, A_i, B_i, Z_i, H_i, dY, dX_i, dA_i, db1_i, dB_i, db2, workspace}));
+  const size_t need = tp_workspace_size(TP_OP_MLP_SHARD_BWD, T, h, F, tp_size, dtype);
+  if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
+  const int64_t es = elsize(dtype);
+  TP_TRY(check_alias({{X, T * h * es}, {A_i, h * f * es}, {B_i, f * h * es}, {Z_i, T * f * es},
+                      {H_i, T * f * es}, {dY, T * h * es}},
+                     {{dX_i, T * h * es}, {dA_i, h * f * 4}, {db1_i, db1_i ? f * 4 : 0}, {dB_i, f * h * 4},
+                      {db2, db2 ? h * 4 : 0}, {workspace, (int64_t)need}}));
+  char* ws = (char*)workspace;
+  float* part = (float*)(ws + round_up((size_t)T * (size_t)f * es));
+  return mlp_bwd_gemms(X, A_i, B_i, Z_i, H_i, dY, dX_i, dA_i, db1_i, dB_i, db2, ws, part, accumulate, T, h, f,
+                       dtype, (hipStream_t)stream);
+}
+
+int tp_mlp_shard_bwd_recompute(const void* X, const void* A_i, const void* b1_i, const void* B_i, const void* Z_i,
+                               const void* dY, void* dX_i, float* dA_i, float* db1_i, float* dB_i, float* db2,
+                               void* workspace, size_t workspace_bytes, int32_t accumulate, int64_t T, int64_t h,
+                               int64_t F, int32_t tp_size, int32_t dtype, void* stream) {
+  TP_TRY(check_dtype(dtype));
+  if (accumulate != 0 && accumulate != 1) return TP_ERR_ARG;
+  TP_TRY(check_nonnull({X, A_i, B_i, dY, dX_i, dA_i, dB_i}));
+  TP_TRY(check_dims({T, h, F}));
+  if (tp_size < 1 || F % tp_size) return TP_ERR_TP_DIVISIBILITY;
+  const int64_t f = F / tp_size;
+  TP_TRY(check_feature({h, f}));
+  TP_TRY(check_elems({{T, h}, {h, f}, {T, f}}));
+  TP_TRY(check_ptrs_aligned({X, A_i, b1_i, B_i, Z_i, dY, dX_i, dA_i, db1_i, dB_i, db2, workspace}));
+  const size_t need = tp_workspace_size(TP_OP_MLP_SHARD_BWD_RECOMPUTE, T, h, F, tp_size, dtype);
+  if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
+  const int64_t es = elsize(dtype);
+  TP_TRY(check_alias({{X, T * h * es}, {A_i, h * f * es}, {b1_i, b1_i ? f * es : 0}, {B_i, f * h * es},
+                      {Z_i, Z_i ? T * f * es : 0}, {dY, T * h * es}},
+                     {{dX_i, T * h * es}, {dA_i, h * f * 4}, {db1_i, db1_i ? f * 4 : 0}, {dB_i, f * h * 4},
+                      {db2, db2 ? h * 4 : 0}, {workspace, (int64_t)need}}));
+  hipStream_t s = (hipStream_t)stream;
+  const size_t act = round_up((size_t)T * (size_t)f * es);
+  char* ws = (char*)workspace;
+  void* dZ = ws;
+  void* H = ws + act;
+  const void* Z = Z_i;
+  if (Z_i == nullptr) {
+    // nothing saved: Z and H again from the forward's fused GEMM (same kernel, same inputs)
+    void* Zw = ws + 2 * act;
+    GemmArgs g = make_args(X, h, A_i, f, T, f, h, H, f);
+    g.bias = b1_i;
+    g.C2 = Zw;
+    g.ldc2 = f;
+    HIP_TRY(gemm(dtype, g, true, false, EPI_BIAS_GELU, s));
+    Z = Zw;
+  } else {
+    // Z saved (it already holds the bias): H = GeLU(Z)
+    HIP_TRY(bias_gelu(Z_i, nullptr, H, dtype == TP_BF16, T, f, s));
+  }
+  float* part = (float*)(ws + 3 * act);
+  return mlp_bwd_gemms(X, A_i, B_i, Z, H, dY, dX_i, dA_i, db1_i, dB_i, db2, dZ, part, accumulate, T, h, f, dtype,
+                       s);
 }
 
 int tp_column_linear_bwd(const void* X, const void* W_i, const void* dY_i, void* dX_partial, float* dW_i,

@@ -195,3 +195,17 @@ def test_attention_bwd_validation(lib):
     assert f(QKV, O, L, G, DQ, P(DQ.value + 4096), need, *args) == -6                     # workspace inside dQKV
     assert f(QKV, O, L, G, DQ, WS, need, 256, 128, 4, 64, 2, 1, 1, S) == -5
     assert f(QKV, O, L, G, DQ, WS, need, 256, 100, 4, 64, 2, 1, 0, S) == -2
+
+
+def test_mlp_bwd_recompute_validation(lib):
+    f = lib.tp_mlp_shard_bwd_recompute
+    need = lib.tp_workspace_size(_native.TP_OP_MLP_SHARD_BWD_RECOMPUTE, 128, 256, 1024, 2, 0)
+    assert need >= 3 * 128 * 512 * 2 > lib.tp_workspace_size(_native.TP_OP_MLP_SHARD_BWD, 128, 256, 1024, 2, 0)
+    X, Ai, b1, Bi, Z, dY, dX, dA, db1, dB, db2, WS = (P(0x1000000 * (i + 1)) for i in range(12))
+    args = (0, 128, 256, 1024, 2, 0, S)
+    assert f(X, Ai, b1, Bi, Z, dY, dX, dA, db1, dB, db2, WS, need - 1, *args) == -7
+    assert f(None, Ai, b1, Bi, Z, dY, dX, dA, db1, dB, db2, WS, need, *args) == -1
+    assert f(X, Ai, b1, Bi, Z, dY, Z, dA, db1, dB, db2, WS, need, *args) == -6       # dX aliases Z
+    assert f(X, Ai, b1, Bi, None, dY, dX, dA, db1, dB, db2, P(dA.value + 64), need, *args) == -6
+    assert f(X, Ai, b1, Bi, Z, dY, dX, dA, db1, dB, db2, WS, need, 2, 128, 256, 1024, 2, 0, S) == -9
+    assert f(X, Ai, b1, Bi, Z, dY, dX, dA, db1, dB, db2, WS, need, 0, 128, 256, 1024, 3, 0, S) == -3

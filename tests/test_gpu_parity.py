@@ -310,3 +310,27 @@ def test_mfma_probe_reports_plausible_rates():
     # the rate is bounded by the compute units at the measured clock
     ceiling = r["compute_units"] * tps.FLOP_PER_CU_CLK * r["clock_ghz_mean"] / 1e3
     assert 0.3 * ceiling < r["tflops"] < 1.1 * ceiling
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("T,h,f,p", [(1, 8, 8, 1), (131, 264, 136, 4), (512, 1024, 2048, 2)])
+def test_mlp_bwd_recompute(T, h, f, p, dtype):
+    """Selective recompute: Z kept (H recomputed) and nothing kept (Z, H
+    recomputed by the fc1 GEMM) give the oracle's gradients; the second is
+    bitwise the saved-activation backward (same kernels on the same inputs)."""
+    dt = "bf16" if dtype == torch.bfloat16 else "fp32"
+    tol = TOL[dtype]
+    d = synth.mlp_inputs(T, h, f * p, p, dt, 0.05, seed=T * 11 + h, full=False)
+    Xd, Ad, b1d, Bd, dYd = (dev(d[k]) for k in ("X", "A", "b1", "B", "dY"))
+    print(f"recompute T={T} h={h} f={f} p={p} {dt}", flush=True)
+    Z, H, _ = tps.mlp_shard_fwd(Xd, Ad, b1d, Bd, tp_size=p)
+    saved = tps.mlp_shard_bwd(Xd, Ad, Bd, Z, H, dYd, tp_size=p, want_db2=True)
+    from_z = tps.mlp_shard_bwd(Xd, Ad, Bd, Z, None, dYd, tp_size=p, want_db2=True, recompute=True)
+    from_x = tps.mlp_shard_bwd(Xd, Ad, Bd, None, None, dYd, tp_size=p, want_db2=True, recompute=True, b1_i=b1d)
+    torch.cuda.synchronize()
+    ref = oracle.mlp_shard_bwd(*(f64(d[k]) for k in ("X", "A", "b1", "B", "dY")))
+    for k in ("dX", "dA", "db1", "dB"):
+        _rel(f"{k}/z", f64(from_z[k]), ref[k], tol)
+        _rel(f"{k}/x", f64(from_x[k]), ref[k], tol)
+    for k in ("dX", "dA", "db1", "dB", "db2"):
+        assert torch.equal(from_x[k], saved[k]), k
