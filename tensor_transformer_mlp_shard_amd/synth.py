@@ -16,13 +16,13 @@ from dataclasses import dataclass, field
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "seeded", "randn", "mlp_inputs", "attn_inputs", "core_attn_inputs",
-           "inputs_for"]
+           "sp_edge_inputs", "inputs_for"]
 
 
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "mlp", "attn" (attention linears) or "core_attn"
+    kind: str            # "mlp", "attn" (attention linears), "core_attn" or "sp_edge"
     T: int               # tokens (micro-batch x sequence, flattened)
     h: int               # hidden size
     F: int               # full FFN width (mlp) or full QKV width (attn)
@@ -76,6 +76,12 @@ WORKLOADS = {
     "gpt175b_core_attn_tp8": Workload("gpt175b_core_attn_tp8", "core_attn", 8192, 12288, 36864, 8, "bf16", 1.0,
                                       1241, False, "175B TP=8: 12 local heads of 128, 4 x 2048 tokens",
                                       seq=2048, heads=96),
+    # Sequence-parallel edge steps on the rank's share of the tokens: T here is
+    # that share (all tokens / tp), h the hidden size.
+    "gpt_h1024_sp_edge_tp2": Workload("gpt_h1024_sp_edge_tp2", "sp_edge", 2048, 1024, 0, 2, "bf16", 0.02, 1242,
+                                      False, "GPT h=1024 TP=2: 4096 tokens / 2 rows of 1024"),
+    "gpt175b_sp_edge_tp8": Workload("gpt175b_sp_edge_tp8", "sp_edge", 1024, 12288, 0, 8, "bf16", 0.006, 1243,
+                                    False, "175B TP=8: 8192 tokens / 8 rows of 12288"),
 }
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}
@@ -152,7 +158,29 @@ def core_attn_inputs(T: int, heads_local: int, head_dim: int, dtype: str, sigma:
     return {"QKV": randn(g, (T, 3 * w), sigma, dtype), "dO": randn(g, (T, w), 1.0, dtype)}
 
 
+def sp_edge_inputs(rows: int, h: int, dtype: str, sigma_w: float, seed: int) -> dict:
+    """Inputs of the sequence-parallel edge steps on a rank's rows.
+
+    Draw order: X[rows x h] (LayerNorm input), gamma[h] = 1 + N(0, 0.1^2),
+    beta[h] ~ N(0, 0.1^2), dY_ln[rows x h], Y[rows x h] (row-parallel output),
+    b[h] ~ N(0, sigma_w^2), residual[rows x h], dOut[rows x h]; the rest N(0, 1).
+    """
+    g = seeded(seed)
+    out = {"X": randn(g, (rows, h), 1.0, dtype)}
+    gam = torch.randn(h, generator=g, dtype=torch.float32) * 0.1 + 1.0
+    out["gamma"] = gam.to(_TORCH_DTYPE[dtype]).contiguous()
+    out["beta"] = randn(g, (h,), 0.1, dtype)
+    out["dY_ln"] = randn(g, (rows, h), 1.0, dtype)
+    out["Y"] = randn(g, (rows, h), 1.0, dtype)
+    out["b"] = randn(g, (h,), sigma_w, dtype)
+    out["residual"] = randn(g, (rows, h), 1.0, dtype)
+    out["dOut"] = randn(g, (rows, h), 1.0, dtype)
+    return out
+
+
 def inputs_for(w: Workload) -> dict:
+    if w.kind == "sp_edge":
+        return sp_edge_inputs(w.T, w.h, w.dtype, w.sigma_w, w.seed)
     if w.kind == "core_attn":
         return core_attn_inputs(w.T, w.heads_local, w.head_dim, w.dtype, w.sigma_w, w.seed)
     if w.kind == "mlp":

@@ -51,3 +51,12 @@ def test_core_attention_workloads():
     assert x["QKV"].shape == (32, 48) and x["dO"].shape == (32, 16) and x["QKV"].dtype == torch.bfloat16
     y = synth.core_attn_inputs(32, 2, 8, "bf16", 1.0, seed=4)
     assert torch.equal(x["QKV"].view(torch.int16), y["QKV"].view(torch.int16))
+
+
+def test_sp_edge_inputs():
+    x = synth.sp_edge_inputs(8, 64, "bf16", 0.02, seed=5)
+    assert set(x) == {"X", "gamma", "beta", "dY_ln", "Y", "b", "residual", "dOut"}
+    assert x["X"].shape == (8, 64) and x["gamma"].shape == (64,) and x["gamma"].dtype == torch.bfloat16
+    assert abs(float(x["gamma"].float().mean()) - 1.0) < 0.1
+    w = synth.WORKLOADS["gpt175b_sp_edge_tp8"]
+    assert (w.T, w.h) == (8192 // 8, 12288)
