@@ -85,7 +85,9 @@ enum {
   TP_OP_MLP_SHARD_BWD = 3,
   TP_OP_BIAS_GRAD = 4,
   TP_OP_ATTENTION_BWD = 5,
-  TP_OP_MLP_SHARD_BWD_RECOMPUTE = 6
+  TP_OP_MLP_SHARD_BWD_RECOMPUTE = 6,
+  TP_OP_LAYERNORM_BWD = 7,
+  TP_OP_BIAS_DROPOUT_ADD_BWD = 8
 };
 
 /*
@@ -251,10 +253,61 @@ int tp_attention_bwd(const void* QKV_i, const void* O_i, const float* lse, const
                      int64_t head_dim, int32_t tp_size, int32_t causal, int32_t dtype, void* stream);
 
 /*
+ * Sequence-parallel edge steps on the rank's rows ([TUT] "序列并行": on top of
+ * tensor parallelism, LayerNorm and Dropout are split along the sequence
+ * dimension; [INTRO] "课程导入" 1.4.2: sequence parallelism cuts the sequence
+ * and communicates at LayerNorm / Dropout).  rows = the rank's tokens, h = the
+ * hidden size (a multiple of 8, <= 2^21); dtype bf16 or fp32 as elsewhere;
+ * statistics and parameter gradients fp32.
+ *
+ * LayerNorm forward: Y = (X - mean) / sqrt(var + eps) * gamma + beta per row
+ * (var the biased variance over h), X, Y [rows x h], gamma [h], beta [h] or
+ * NULL; mean, rstd [rows] fp32 = the row mean and 1/sqrt(var + eps) (both
+ * NULL for inference, else both given: TP_ERR_ARG).  eps >= 0 (TP_ERR_ARG).
+ */
+int tp_layernorm_fwd(const void* X, const void* gamma, const void* beta, void* Y, float* mean, float* rstd,
+                     int64_t rows, int64_t h, float eps, int32_t dtype, void* stream);
+/*
+ * LayerNorm backward (chain rule of the forward): from X, gamma and the
+ * forward's mean / rstd, and dY [rows x h]:
+ *   dX [rows x h] dtype = rstd * (g - mean_h(g) - xhat * mean_h(g * xhat)),
+ *                 g = dY * gamma, xhat = (X - mean) * rstd;
+ *   dgamma [h] fp32 = sum over rows of dY * xhat;  dbeta [h] fp32 = sum of dY
+ *   (NULL to skip).  accumulate 0/1 as for the MLP.  Deterministic.
+ * workspace: >= tp_workspace_size(TP_OP_LAYERNORM_BWD, rows, h, 0, 1, dtype).
+ */
+int tp_layernorm_bwd(const void* X, const void* gamma, const float* mean, const float* rstd, const void* dY,
+                     void* dX, float* dgamma, float* dbeta, void* workspace, size_t workspace_bytes,
+                     int32_t accumulate, int64_t rows, int64_t h, int32_t dtype, void* stream);
+/*
+ * Bias + dropout + residual add after the row-parallel output (one fused pass,
+ * [TUT] "融合优化技术"):  out = residual + keep * (Y + b) / (1 - p_drop), with
+ * Y, residual, out [rows x h], b [h] or NULL, 0 <= p_drop < 1 (TP_ERR_ARG).
+ * keep: element e (row-major index) is kept when word (offset + e) mod 4 of
+ * Philox4x32-10 (Salmon et al., SC'11) with counter ((offset + e) / 4, 0, 0)
+ * -- 64-bit block number in the first two words -- and key (seed low 32 bits,
+ * seed high 32 bits) is below floor((1 - p_drop) * 2^32).  offset is an
+ * element counter (a multiple of 8, TP_ERR_ARG), so callers give each layer
+ * and rank a disjoint range; the backward regenerates the same mask.
+ */
+int tp_bias_dropout_add_fwd(const void* Y, const void* b, const void* residual, void* out, int64_t rows, int64_t h,
+                            double p_drop, uint64_t seed, uint64_t offset, int32_t dtype, void* stream);
+/*
+ * Its backward: dY [rows x h] dtype = keep * dOut / (1 - p_drop) (same mask);
+ * db [h] fp32 = sum over rows of dY (NULL to skip; then no workspace is
+ * needed), accumulate 0/1; the residual's gradient is dOut itself.
+ * workspace: >= tp_workspace_size(TP_OP_BIAS_DROPOUT_ADD_BWD, rows, h, 0, 1, dtype).
+ */
+int tp_bias_dropout_add_bwd(const void* dOut, void* dY, float* db, void* workspace, size_t workspace_bytes,
+                            int32_t accumulate, int64_t rows, int64_t h, double p_drop, uint64_t seed,
+                            uint64_t offset, int32_t dtype, void* stream);
+
+/*
  * Workspace bytes needed by `op` (TP_OP_*).  Arguments are those of the
  * matching call: T, d_in, d_out = (T, K, N) for the linears, (T, h, F) for the
  * MLP and its recompute form, (T, N, unused) for the bias gradient, (T, heads, head_dim) for the
- * attention backward (dtype TP_BF16).  Returns 0 for invalid arguments.
+ * attention backward (dtype TP_BF16), (rows, h, unused) for the LayerNorm and
+ * bias-dropout-add backwards.  Returns 0 for invalid arguments.
  */
 size_t tp_workspace_size(int32_t op, int64_t T, int64_t d_in, int64_t d_out, int32_t tp_size,
                          int32_t dtype);

@@ -24,7 +24,8 @@ from ._native import NativeLibraryMissing  # noqa: F401
 __all__ = [
     "column_linear", "row_linear", "mlp_shard_fwd", "mlp_shard_bwd", "column_linear_bwd",
     "row_linear_bwd", "bias_grad", "bias_gelu", "workspace_size", "trace_start", "trace_stop",
-    "attention_fwd", "attention_bwd", "mfma_probe", "library_path", "NativeLibraryMissing",
+    "attention_fwd", "attention_bwd", "layernorm_fwd", "layernorm_bwd", "bias_dropout_add_fwd",
+    "bias_dropout_add_bwd", "mfma_probe", "library_path", "NativeLibraryMissing",
 ]
 
 _DT = {torch.bfloat16: _native.TP_BF16, torch.float32: _native.TP_FP32}
@@ -325,6 +326,88 @@ def attention_bwd(qkv, o, lse, dout, *, seq: int, heads: int, head_dim: int, tp_
                                         int(causal), _native.TP_BF16, _stream(dev))
     _native.check(st, "tp_attention_bwd")
     return dq
+
+
+def layernorm_fwd(x, gamma, beta=None, *, eps: float = 1e-5, save_stats: bool = True, out=None):
+    """LayerNorm over the last dimension of x [rows x h] -> (y, mean or None, rstd or None)."""
+    rows, h = x.shape
+    dev, dt = x.device, x.dtype
+    _check("x", x, (rows, h), dt, dev)
+    _check("gamma", gamma, (h,), dt, dev)
+    if beta is not None:
+        _check("beta", beta, (h,), dt, dev)
+    y = out if out is not None else torch.empty_like(x)
+    _check("out", y, (rows, h), dt, dev)
+    mean = torch.empty((rows,), dtype=torch.float32, device=dev) if save_stats else None
+    rstd = torch.empty((rows,), dtype=torch.float32, device=dev) if save_stats else None
+    st = _native.lib().tp_layernorm_fwd(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), rows, h,
+                                        float(eps), _dtype_code(x), _stream(dev))
+    _native.check(st, "tp_layernorm_fwd")
+    return y, mean, rstd
+
+
+def layernorm_bwd(x, gamma, mean, rstd, dy, *, want_dbeta: bool = True, accumulate: bool = False, out=None,
+                  workspace=None):
+    """LayerNorm backward -> dict(dX, dgamma, dbeta)."""
+    rows, h = x.shape
+    dev, dt = x.device, x.dtype
+    for name, t, shp, tdt in (("x", x, (rows, h), dt), ("gamma", gamma, (h,), dt), ("dy", dy, (rows, h), dt),
+                              ("mean", mean, (rows,), torch.float32), ("rstd", rstd, (rows,), torch.float32)):
+        _check(name, t, shp, tdt, dev)
+    out = dict(out or {})
+
+    def get(k, shape, dtype):
+        t = out.get(k)
+        if t is None:
+            if accumulate:
+                raise ValueError(f"accumulate needs out[{k!r}]")
+            return torch.empty(shape, dtype=dtype, device=dev)
+        _check(f"out[{k}]", t, shape, dtype, dev)
+        return t
+
+    dX = out.get("dX") if out.get("dX") is not None else torch.empty_like(x)
+    dg = get("dgamma", (h,), torch.float32)
+    db = get("dbeta", (h,), torch.float32) if want_dbeta else None
+    ws = _workspace(_native.TP_OP_LAYERNORM_BWD, rows, h, 0, 1, dt, dev, workspace)
+    st = _native.lib().tp_layernorm_bwd(_ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dy), _ptr(dX), _ptr(dg),
+                                        _ptr(db), _ptr(ws), ws.numel(), int(accumulate), rows, h, _dtype_code(x),
+                                        _stream(dev))
+    _native.check(st, "tp_layernorm_bwd")
+    return {"dX": dX, "dgamma": dg, "dbeta": db}
+
+
+def bias_dropout_add_fwd(y, b, residual, *, p: float, seed: int, offset: int = 0, out=None):
+    """residual + dropout(y + b) with the Philox4x32-10 keep rule -> out."""
+    rows, h = y.shape
+    dev, dt = y.device, y.dtype
+    _check("y", y, (rows, h), dt, dev)
+    _check("residual", residual, (rows, h), dt, dev)
+    if b is not None:
+        _check("b", b, (h,), dt, dev)
+    o = out if out is not None else torch.empty_like(y)
+    _check("out", o, (rows, h), dt, dev)
+    st = _native.lib().tp_bias_dropout_add_fwd(_ptr(y), _ptr(b), _ptr(residual), _ptr(o), rows, h, float(p),
+                                               int(seed), int(offset), _dtype_code(y), _stream(dev))
+    _native.check(st, "tp_bias_dropout_add_fwd")
+    return o
+
+
+def bias_dropout_add_bwd(dout, *, p: float, seed: int, offset: int = 0, want_db: bool = True, accumulate_into=None,
+                         out=None, workspace=None):
+    """Backward of bias_dropout_add_fwd -> (dY, db or None); the residual's gradient is dout."""
+    rows, h = dout.shape
+    dev, dt = dout.device, dout.dtype
+    _check("dout", dout, (rows, h), dt, dev)
+    dY = out if out is not None else torch.empty_like(dout)
+    db = accumulate_into if accumulate_into is not None else (
+        torch.empty((h,), dtype=torch.float32, device=dev) if want_db else None)
+    ws = _workspace(_native.TP_OP_BIAS_DROPOUT_ADD_BWD, rows, h, 0, 1, dt, dev, workspace) if db is not None else None
+    st = _native.lib().tp_bias_dropout_add_bwd(_ptr(dout), _ptr(dY), _ptr(db), _ptr(ws),
+                                               ws.numel() if ws is not None else 0, int(accumulate_into is not None),
+                                               rows, h, float(p), int(seed), int(offset), _dtype_code(dout),
+                                               _stream(dev))
+    _native.check(st, "tp_bias_dropout_add_bwd")
+    return dY, db
 
 
 def trace_start(max_launches: int = 4096) -> None:

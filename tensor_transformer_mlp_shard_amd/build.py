@@ -28,7 +28,7 @@ COMMON = [
     "-Wno-unused-command-line-argument",
 ]
 
-SOURCES = ["gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip", "attention.hip", "probe.hip", "api.cpp"]
+SOURCES = ["gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip", "attention.hip", "sp_edge.hip", "probe.hip", "api.cpp"]
 
 
 def _compile(src: str, verbose: bool) -> str:

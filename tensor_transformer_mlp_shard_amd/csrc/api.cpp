@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -14,6 +15,7 @@
 #include "attention.h"
 #include "gemm.h"
 #include "side.h"
+#include "sp_edge.h"
 
 namespace tps {
 namespace {
@@ -229,6 +231,13 @@ size_t tp_workspace_size(int32_t op, int64_t T, int64_t d_in, int64_t d_out, int
                                                                           : colsum_ws_bytes(T, d_in);
       return 3 * act + cs;
     }
+    case TP_OP_LAYERNORM_BWD:
+      // dgamma and dbeta partial rows of every workgroup (d_in = h)
+      if (d_in < 1 || d_in > kMaxFeature) return 0;
+      return round_up((size_t)2 * (size_t)layernorm_bwd_chunks(T) * (size_t)d_in * 4);
+    case TP_OP_BIAS_DROPOUT_ADD_BWD:
+      if (d_in < 1 || d_in > kMaxFeature) return 0;
+      return colsum_ws_bytes(T, d_in);
     case TP_OP_ATTENTION_BWD: {
       // d_in = heads, d_out = head_dim: the row-dot Dt [Hl x T] fp32
       if (dtype != TP_BF16 || tp_size < 1 || d_in < 1 || d_in > kMaxDim || d_in % tp_size) return 0;
@@ -517,6 +526,94 @@ int tp_attention_bwd(const void* QKV_i, const void* O_i, const float* lse, const
                      {{dQKV_i, T * 3 * w * 2}, {workspace, (int64_t)need}}));
   HIP_TRY(attention_bwd((const bf16*)QKV_i, (const bf16*)O_i, lse, (const bf16*)dO_i, (bf16*)dQKV_i,
                         (float*)workspace, p, (hipStream_t)stream));
+  return TP_OK;
+}
+
+// ---------------------------------------------------------------- sequence-parallel edge steps
+static int check_rows_h(int64_t rows, int64_t h) {
+  TP_TRY(check_dims({rows, h}));
+  TP_TRY(check_feature({h}));
+  TP_TRY(check_elems({{rows, h}}));
+  return TP_OK;
+}
+
+static int dropout_params(double p_drop, uint64_t offset, uint64_t& threshold, float& scale) {
+  if (!(p_drop >= 0.0 && p_drop < 1.0)) return TP_ERR_ARG;
+  if (offset % 8 != 0) return TP_ERR_ARG;
+  threshold = (uint64_t)std::floor((1.0 - p_drop) * 4294967296.0);
+  scale = (float)(1.0 / (1.0 - p_drop));
+  return TP_OK;
+}
+
+int tp_layernorm_fwd(const void* X, const void* gamma, const void* beta, void* Y, float* mean, float* rstd,
+                     int64_t rows, int64_t h, float eps, int32_t dtype, void* stream) {
+  TP_TRY(check_dtype(dtype));
+  TP_TRY(check_nonnull({X, gamma, Y}));
+  if ((mean == nullptr) != (rstd == nullptr)) return TP_ERR_ARG;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return TP_ERR_ARG;
+  TP_TRY(check_rows_h(rows, h));
+  TP_TRY(check_ptrs_aligned({X, gamma, beta, Y, mean, rstd}));
+  const int64_t es = elsize(dtype);
+  TP_TRY(check_alias({{X, rows * h * es}, {gamma, h * es}, {beta, beta ? h * es : 0}},
+                     {{Y, rows * h * es}, {mean, mean ? rows * 4 : 0}, {rstd, rstd ? rows * 4 : 0}}));
+  HIP_TRY(layernorm_fwd(X, gamma, beta, Y, mean, rstd, rows, h, eps, dtype == TP_BF16, (hipStream_t)stream));
+  return TP_OK;
+}
+
+int tp_layernorm_bwd(const void* X, const void* gamma, const float* mean, const float* rstd, const void* dY, void* dX,
+                     float* dgamma, float* dbeta, void* workspace, size_t workspace_bytes, int32_t accumulate,
+                     int64_t rows, int64_t h, int32_t dtype, void* stream) {
+  TP_TRY(check_dtype(dtype));
+  if (accumulate != 0 && accumulate != 1) return TP_ERR_ARG;
+  TP_TRY(check_nonnull({X, gamma, mean, rstd, dY, dX, dgamma}));
+  TP_TRY(check_rows_h(rows, h));
+  TP_TRY(check_ptrs_aligned({X, gamma, mean, rstd, dY, dX, dgamma, dbeta, workspace}));
+  const size_t need = tp_workspace_size(TP_OP_LAYERNORM_BWD, rows, h, 0, 1, dtype);
+  if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
+  const int64_t es = elsize(dtype);
+  TP_TRY(check_alias({{X, rows * h * es}, {gamma, h * es}, {mean, rows * 4}, {rstd, rows * 4}, {dY, rows * h * es}},
+                     {{dX, rows * h * es}, {dgamma, h * 4}, {dbeta, dbeta ? h * 4 : 0},
+                      {workspace, (int64_t)need}}));
+  HIP_TRY(layernorm_bwd(X, gamma, mean, rstd, dY, dX, dgamma, dbeta, (float*)workspace, accumulate, rows, h,
+                        dtype == TP_BF16, (hipStream_t)stream));
+  return TP_OK;
+}
+
+int tp_bias_dropout_add_fwd(const void* Y, const void* b, const void* residual, void* out, int64_t rows, int64_t h,
+                            double p_drop, uint64_t seed, uint64_t offset, int32_t dtype, void* stream) {
+  TP_TRY(check_dtype(dtype));
+  TP_TRY(check_nonnull({Y, residual, out}));
+  TP_TRY(check_rows_h(rows, h));
+  uint64_t thr;
+  float scale;
+  TP_TRY(dropout_params(p_drop, offset, thr, scale));
+  TP_TRY(check_ptrs_aligned({Y, b, residual, out}));
+  const int64_t es = elsize(dtype);
+  TP_TRY(check_alias({{Y, rows * h * es}, {b, b ? h * es : 0}, {residual, rows * h * es}}, {{out, rows * h * es}}));
+  HIP_TRY(bias_dropout_add_fwd(Y, b, residual, out, rows, h, thr, scale, seed, offset, dtype == TP_BF16,
+                               (hipStream_t)stream));
+  return TP_OK;
+}
+
+int tp_bias_dropout_add_bwd(const void* dOut, void* dY, float* db, void* workspace, size_t workspace_bytes,
+                            int32_t accumulate, int64_t rows, int64_t h, double p_drop, uint64_t seed,
+                            uint64_t offset, int32_t dtype, void* stream) {
+  TP_TRY(check_dtype(dtype));
+  if (accumulate != 0 && accumulate != 1) return TP_ERR_ARG;
+  TP_TRY(check_nonnull({dOut, dY}));
+  TP_TRY(check_rows_h(rows, h));
+  uint64_t thr;
+  float scale;
+  TP_TRY(dropout_params(p_drop, offset, thr, scale));
+  TP_TRY(check_ptrs_aligned({dOut, dY, db, workspace}));
+  const size_t need = db ? tp_workspace_size(TP_OP_BIAS_DROPOUT_ADD_BWD, rows, h, 0, 1, dtype) : 0;
+  if (db && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
+  const int64_t es = elsize(dtype);
+  TP_TRY(check_alias({{dOut, rows * h * es}},
+                     {{dY, rows * h * es}, {db, db ? h * 4 : 0}, {workspace, db ? (int64_t)need : 0}}));
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(dropout_bwd(dOut, dY, rows, h, thr, scale, seed, offset, dtype == TP_BF16, s));
+  if (db) HIP_TRY(colsum(dY, dtype == TP_BF16, db, (float*)workspace, accumulate, rows, h, s));
   return TP_OK;
 }
 

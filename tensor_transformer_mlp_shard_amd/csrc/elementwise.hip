@@ -142,6 +142,16 @@ hipError_t colsum(const void* in, bool in_bf16, float* out, float* ws, int accum
   return hipGetLastError();
 }
 
+hipError_t sum_partials(const float* part, float* out, int64_t N, int chunks, int accumulate, const char* name,
+                        hipStream_t s) {
+  LaunchInfo info{name, 0.0, 4.0 * chunks * (double)N + 4.0 * (accumulate ? 2 : 1) * N};
+  trace_begin(s);
+  hipLaunchKernelGGL(colsum_finalize_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, s, part, out, N, chunks,
+                     accumulate);
+  trace_end(s, info);
+  return hipGetLastError();
+}
+
 hipError_t bias_gelu(const void* Z, const void* b, void* H, bool is_bf16, int64_t T, int64_t N, hipStream_t s) {
   const int64_t n = T * (N / 8);
   const dim3 grid((unsigned)((n + 255) / 256));

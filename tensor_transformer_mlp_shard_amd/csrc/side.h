@@ -12,6 +12,10 @@ int colsum_chunks(int64_t T, int64_t N);
 hipError_t colsum(const void* in, bool in_bf16, float* out, float* ws, int accumulate,
                   int64_t T, int64_t N, hipStream_t s);
 
+// out[n] (+)= sum over c < chunks of part[c * N + n], in a fixed order (elementwise.hip).
+hipError_t sum_partials(const float* part, float* out, int64_t N, int chunks, int accumulate, const char* name,
+                        hipStream_t s);
+
 // H = GeLU(Z + b) elementwise (elementwise.hip).
 hipError_t bias_gelu(const void* Z, const void* b, void* H, bool is_bf16, int64_t T, int64_t N,
                      hipStream_t s);

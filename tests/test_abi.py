@@ -209,3 +209,34 @@ def test_mlp_bwd_recompute_validation(lib):
     assert f(X, Ai, b1, Bi, None, dY, dX, dA, db1, dB, db2, P(dA.value + 64), need, *args) == -6
     assert f(X, Ai, b1, Bi, Z, dY, dX, dA, db1, dB, db2, WS, need, 2, 128, 256, 1024, 2, 0, S) == -9
     assert f(X, Ai, b1, Bi, Z, dY, dX, dA, db1, dB, db2, WS, need, 0, 128, 256, 1024, 3, 0, S) == -3
+
+
+def test_sp_edge_validation(lib):
+    X, G, B, Y, M, R, DY, DX, DG, DB, WS = (P(0x1000000 * (i + 1)) for i in range(11))
+    f = lib.tp_layernorm_fwd
+    assert f(None, G, B, Y, M, R, 64, 1024, 1e-5, 0, S) == -1
+    assert f(X, G, B, Y, M, None, 64, 1024, 1e-5, 0, S) == -9        # mean without rstd
+    assert f(X, G, B, Y, M, R, 64, 1024, -1.0, 0, S) == -9            # eps < 0
+    assert f(X, G, B, Y, M, R, 64, 1020, 1e-5, 0, S) == -4            # h not a multiple of 8
+    assert f(X, G, B, Y, M, R, 0, 1024, 1e-5, 0, S) == -2
+    assert f(X, G, B, X, M, R, 64, 1024, 1e-5, 0, S) == -6            # in place is rejected
+    assert f(X, G, B, Y, M, R, 64, 1024, 1e-5, 3, S) == -5
+    g = lib.tp_layernorm_bwd
+    need = lib.tp_workspace_size(_native.TP_OP_LAYERNORM_BWD, 64, 1024, 0, 1, 0)
+    assert need >= 2 * 8 * 1024 * 4
+    assert g(X, G, M, R, DY, DX, DG, DB, WS, need - 1, 0, 64, 1024, 0, S) == -7
+    assert g(X, G, M, R, DY, DX, None, DB, WS, need, 0, 64, 1024, 0, S) == -1
+    assert g(X, G, M, R, DY, DX, DG, DB, WS, need, 2, 64, 1024, 0, S) == -9
+    assert g(X, G, M, R, DY, DY, DG, DB, WS, need, 0, 64, 1024, 0, S) == -6
+    d = lib.tp_bias_dropout_add_fwd
+    assert d(Y, B, X, DX, 64, 1024, 1.0, 1, 0, 0, S) == -9             # p = 1
+    assert d(Y, B, X, DX, 64, 1024, -0.1, 1, 0, 0, S) == -9
+    assert d(Y, B, X, DX, 64, 1024, 0.1, 1, 4, 0, S) == -9             # offset not a multiple of 8
+    assert d(Y, B, X, X, 64, 1024, 0.1, 1, 0, 0, S) == -6
+    assert d(None, B, X, DX, 64, 1024, 0.1, 1, 0, 0, S) == -1
+    e = lib.tp_bias_dropout_add_bwd
+    need2 = lib.tp_workspace_size(_native.TP_OP_BIAS_DROPOUT_ADD_BWD, 64, 1024, 0, 1, 0)
+    assert need2 > 0
+    assert e(DY, DX, DG, None, 0, 0, 64, 1024, 0.1, 1, 0, 0, S) == -7  # db wanted, no workspace
+    assert e(DY, DY, None, None, 0, 0, 64, 1024, 0.1, 1, 0, 0, S) == -6
+    assert e(DY, DX, None, None, 0, 0, 64, 1024, 0.1, 1, 12, 0, S) == -9

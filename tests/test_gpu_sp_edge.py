@@ -1,0 +1,100 @@
+"""GPU parity of the sequence-parallel edge steps (LayerNorm and bias + dropout +
+residual, forward and backward) against the fp64 oracle.
+
+Real-valued outputs by relative Frobenius error (<= 5e-3 bf16 storage, <= 1e-5
+fp32; the fp32 row statistics <= 1e-5 for both).  The dropout mask is an
+integer decision and must match the oracle's bit for bit: it is read back
+exactly from the backward with dOut = 1 (kept -> 1/(1-p), dropped -> 0)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tensor_transformer_mlp_shard_amd as tps
+from tensor_transformer_mlp_shard_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.bfloat16: 5e-3, torch.float32: 1e-5}
+DEV = "cuda:0"
+DT = {torch.bfloat16: "bf16", torch.float32: "fp32"}
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def _rel(name, got, ref, tol):
+    e = oracle.rel_fro(got, ref)
+    print(f"  {name:7s} rel_fro={e:.3e} (tol {tol:g})", flush=True)
+    assert e <= tol, f"{name}: rel_fro {e:.3e} > {tol:g}"
+
+
+LN_SHAPES = [(1, 8), (3, 1032), (17, 2048), (64, 12288), (5, 18432), (1024, 12288), (2048, 1024)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("rows,h", LN_SHAPES, ids=[f"{r}x{h}" for r, h in LN_SHAPES])
+def test_layernorm(rows, h, dtype):
+    x = synth.sp_edge_inputs(rows, h, DT[dtype], 0.02, seed=rows * 31 + h)
+    tol = TOL[dtype]
+    print(f"layernorm rows={rows} h={h} {DT[dtype]}", flush=True)
+    X, g, b, dY = (x[k].to(DEV) for k in ("X", "gamma", "beta", "dY_ln"))
+    Y, mean, rstd = tps.layernorm_fwd(X, g, b, eps=1e-5)
+    grads = tps.layernorm_bwd(X, g, mean, rstd, dY)
+    torch.cuda.synchronize()
+    Yr, mr, rr = oracle.layernorm_fwd(f64(x["X"]), f64(x["gamma"]), f64(x["beta"]), 1e-5)
+    dXr, dgr, dbr = oracle.layernorm_bwd(f64(x["X"]), f64(x["gamma"]), f64(x["dY_ln"]), 1e-5)
+    _rel("Y", f64(Y), Yr, tol)
+    _rel("mean", f64(mean), mr, 1e-5)
+    _rel("rstd", f64(rstd), rr, 1e-5)
+    _rel("dX", f64(grads["dX"]), dXr, tol)
+    _rel("dgamma", f64(grads["dgamma"]), dgr, tol)
+    _rel("dbeta", f64(grads["dbeta"]), dbr, tol)
+
+
+def test_layernorm_inference_accumulate_determinism():
+    x = synth.sp_edge_inputs(256, 1024, "bf16", 0.02, seed=77)
+    X, g, b, dY = (x[k].to(DEV) for k in ("X", "gamma", "beta", "dY_ln"))
+    Y1, m, r = tps.layernorm_fwd(X, g, b)
+    Y2, m2, r2 = tps.layernorm_fwd(X, g, None, save_stats=False)
+    g1 = tps.layernorm_bwd(X, g, m, r, dY)
+    base = {"dgamma": torch.full_like(g1["dgamma"], 0.25), "dbeta": torch.full_like(g1["dbeta"], -0.5)}
+    acc = {k: v.clone() for k, v in base.items()}
+    tps.layernorm_bwd(X, g, m, r, dY, accumulate=True, out=acc)
+    g2 = tps.layernorm_bwd(X, g, m, r, dY)
+    torch.cuda.synchronize()
+    assert m2 is None and r2 is None
+    Yr, _, _ = oracle.layernorm_fwd(f64(x["X"]), f64(x["gamma"]), None, 1e-5)
+    _rel("Y(no b)", f64(Y2), Yr, 5e-3)
+    for k in base:
+        torch.testing.assert_close(acc[k], base[k] + g1[k], rtol=1e-6, atol=1e-6)
+        assert torch.equal(g1[k], g2[k])
+    assert torch.equal(g1["dX"], g2["dX"])
+
+
+DROP_CASES = [(1, 8, 0.1, 1, 0), (37, 1032, 0.5, (1 << 40) + 3, 8 * 1001), (5, 64, 0.0, 9, 16),
+              (64, 12288, 0.1, 1234, 1 << 35), (1024, 12288, 0.1, 2024, 0)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("rows,h,p,seed,offset", DROP_CASES, ids=[f"{c[0]}x{c[1]}_p{c[2]}" for c in DROP_CASES])
+def test_bias_dropout_add(rows, h, p, seed, offset, dtype):
+    x = synth.sp_edge_inputs(rows, h, DT[dtype], 0.02, seed=rows + h + 5)
+    tol = TOL[dtype]
+    print(f"dropout rows={rows} h={h} p={p} seed={seed} offset={offset} {DT[dtype]}", flush=True)
+    Y, b, R, dO = (x[k].to(DEV) for k in ("Y", "b", "residual", "dOut"))
+    out = tps.bias_dropout_add_fwd(Y, b, R, p=p, seed=seed, offset=offset)
+    ones = torch.ones_like(dO)
+    mask_probe, _ = tps.bias_dropout_add_bwd(ones, p=p, seed=seed, offset=offset, want_db=False)
+    dY, db = tps.bias_dropout_add_bwd(dO, p=p, seed=seed, offset=offset)
+    torch.cuda.synchronize()
+    ref_out, ref_mask = oracle.bias_dropout_add_fwd(f64(x["Y"]), f64(x["b"]), f64(x["residual"]), p, seed, offset)
+    got_mask = f64(mask_probe) != 0.0
+    mism = int(np.sum(got_mask != ref_mask))
+    print(f"  mask    kept {got_mask.mean():.4f} (1-p = {1 - p:.4f}), mismatches {mism}", flush=True)
+    assert mism == 0
+    _rel("out", f64(out), ref_out, tol)
+    dYr, dbr, _ = oracle.bias_dropout_add_bwd(f64(x["dOut"]), p, seed, offset)
+    _rel("dY", f64(dY), dYr, tol)
+    _rel("db", f64(db), dbr, tol)
