@@ -17,7 +17,9 @@ kernel with the most time in the step (timed with HIP events around its
 launches by the library's trace), the register-only matrix-core probe, the
 fp64 CPU oracle timed on a bounded sample of the same workload, and, outside
 the step, core attention on the rank's local heads (175B shape: 4 sequences of
-2048 tokens, 12 heads of 128, causal) forward and backward.
+2048 tokens, 12 heads of 128, causal) forward and backward, the selective
+recompute forms of the MLP backward, and the sequence-parallel edge steps
+(LayerNorm, bias + dropout + residual) in GB/s.
 """
 from __future__ import annotations
 
@@ -160,6 +162,40 @@ def measure_core_attention(torch, device, steps, warmup):
                        "gbs": round(k["bytes"] / (k["total_ms"] * 1e-3) / 1e9, 1)}
                       for k in ca.tps.trace_stop()]
     return out
+
+
+def measure_sp_edge(torch, device, steps, warmup):
+    """Sequence-parallel edge steps on the 175B rank's rows (8192 tokens / 8 =
+    1024 rows of 12288), HBM-bound: GB/s of algorithmic traffic per kernel."""
+    import tensor_transformer_mlp_shard_amd as tps
+    from tensor_transformer_mlp_shard_amd import synth
+
+    w = synth.WORKLOADS["gpt175b_sp_edge_tp8"]
+    x = {k: v.to(device) for k, v in synth.inputs_for(w).items()}
+    y, mean, rstd = tps.layernorm_fwd(x["X"], x["gamma"], x["beta"])
+    lnb = {"dX": torch.empty_like(x["X"]), "dgamma": torch.empty(w.h, device=device),
+           "dbeta": torch.empty(w.h, device=device)}
+    out = torch.empty_like(x["Y"])
+    dy = torch.empty_like(x["Y"])
+
+    def step():
+        tps.layernorm_fwd(x["X"], x["gamma"], x["beta"], out=y)
+        tps.layernorm_bwd(x["X"], x["gamma"], mean, rstd, x["dY_ln"], out=lnb)
+        tps.bias_dropout_add_fwd(x["Y"], x["b"], x["residual"], p=0.1, seed=1, offset=0, out=out)
+        tps.bias_dropout_add_bwd(x["dOut"], p=0.1, seed=1, offset=0, out=dy)
+
+    ms, _ = time_steps(torch, step, steps, warmup)
+    tps.trace_start(4096)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kern = [{"name": k["name"], "launches_per_step": k["launches"] // steps,
+             "us_per_step": round(1e3 * k["total_ms"] / steps, 2),
+             "gbs": round(k["bytes"] / (k["total_ms"] * 1e-3) / 1e9, 1),
+             "frac_hbm": round(k["bytes"] / (k["total_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
+            for k in tps.trace_stop()]
+    return {"workload": f"175B TP=8 sequence-parallel rows: {w.T} x {w.h}, bf16, dropout p=0.1",
+            "ms_per_step": round(ms, 4), "kernels": kern}
 
 
 def measure_recompute(torch, shard, steps, warmup):
@@ -385,6 +421,7 @@ def main():
         "kernels": kern,
     }
     if args.part == "all":
+        out["sp_edge"] = measure_sp_edge(torch, device, min(args.steps, 50), min(args.warmup, 10))
         out["selective_recompute"] = measure_recompute(torch, shard, min(args.steps, 50), min(args.warmup, 10))
         out["core_attention"] = measure_core_attention(torch, device, min(args.steps, 50), min(args.warmup, 10))
     if not args.no_cpu_baseline and args.part == "all":

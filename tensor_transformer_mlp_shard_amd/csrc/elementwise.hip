@@ -61,7 +61,8 @@ __global__ void __launch_bounds__(CS_THREADS) colsum_partial_kernel(const void* 
 }
 
 // Pass 2: a workgroup owns 64 columns (one per lane); wave w adds the partial
-// rows w, w+4, ... and the four wave sums are added in a fixed order.
+// rows w, w+4, ... in that order (loads issued 8 at a time, added in order),
+// and the four wave sums are added in a fixed order.
 __global__ void __launch_bounds__(256) colsum_finalize_kernel(const float* part, float* out, int64_t N,
                                                               int chunks, int accumulate) {
   __shared__ float red[4][64];
@@ -69,7 +70,15 @@ __global__ void __launch_bounds__(256) colsum_finalize_kernel(const float* part,
   const int64_t n = (int64_t)blockIdx.x * 64 + lane;
   float t = 0.0f;
   if (n < N) {
-    for (int c = wave; c < chunks; c += 4) t += part[(int64_t)c * N + n];
+    int c = wave;
+    for (; c + 28 < chunks; c += 32) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(c + 4 * u) * N + n];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t += v[u];
+    }
+    for (; c < chunks; c += 4) t += part[(int64_t)c * N + n];
   }
   red[wave][lane] = t;
   __syncthreads();

@@ -6,7 +6,7 @@
 // extra chunks, from L2).  Mean, then the mean squared deviation (two passes
 // over the registers), in fp32; the row's mean and 1/sqrt(var + eps) are saved.
 //
-// LayerNorm backward.  A workgroup takes rows blockIdx.x, blockIdx.x + grid, ...
+// LayerNorm backward.  A workgroup (8 waves) takes rows blockIdx.x, blockIdx.x + grid, ...
 // For each row it forms xhat and g = dY * gamma per owned chunk (kept in
 // registers), reduces sum(g) and sum(g * xhat) over the row, and writes
 //   dX = rstd * (g - mean(g) - xhat * mean(g * xhat));
@@ -27,8 +27,10 @@
 namespace tps {
 namespace {
 
-constexpr int LN_T = 256;
-constexpr int LN_MAXC = 6;   // register-held 8-element chunks per thread: rows up to 12288 read once
+constexpr int LN_T = 256;       // forward: threads per row
+constexpr int LN_MAXC = 6;      // forward: register-held 8-element chunks per thread (rows up to 12288 read once)
+constexpr int LNB_T = 512;      // backward: threads per workgroup
+constexpr int LNB_MAXC = 3;     // backward: register-held chunks per thread (rows up to 12288)
 
 template <bool BF16>
 __device__ __forceinline__ void load8(const void* base, int64_t off, float* v) {
@@ -58,8 +60,9 @@ __device__ __forceinline__ void store8(void* base, int64_t off, const float* v) 
   }
 }
 
-// Sum over the workgroup (4 waves), the same value in every thread; `red` is 8
-// floats of LDS.  The wave sums are added in a fixed order.
+// Sums over the workgroup (W waves), the same values in every thread; `red` is
+// 2 W floats of LDS.  The wave sums are added in a fixed order.
+template <int W>
 __device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
@@ -70,11 +73,16 @@ __device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
   __syncthreads();  // the previous use of red is finished
   if ((threadIdx.x & 63) == 0) {
     red[w] = a;
-    red[4 + w] = b;
+    red[W + w] = b;
   }
   __syncthreads();
-  a = ((red[0] + red[1]) + red[2]) + red[3];
-  b = ((red[4] + red[5]) + red[6]) + red[7];
+  a = red[0];
+  b = red[W];
+#pragma unroll
+  for (int i = 1; i < W; ++i) {
+    a += red[i];
+    b += red[W + i];
+  }
 }
 
 template <bool BF16>
@@ -102,7 +110,7 @@ __global__ void __launch_bounds__(LN_T) layernorm_fwd_kernel(const void* X, cons
 #pragma unroll
     for (int e = 0; e < 8; ++e) s += t[e];
   }
-  block_sum2(s, unused, red);
+  block_sum2<LN_T / 64>(s, unused, red);
   const float mean = s * inv_h;
   float q = 0.0f;
   unused = 0.0f;
@@ -126,7 +134,7 @@ __global__ void __launch_bounds__(LN_T) layernorm_fwd_kernel(const void* X, cons
       q += d * d;
     }
   }
-  block_sum2(q, unused, red);
+  block_sum2<LN_T / 64>(q, unused, red);
   const float rstd = 1.0f / sqrtf(q * inv_h + eps);
   auto emit = [&](int c, const float* x) {
     float g[8], bb[8] = {0, 0, 0, 0, 0, 0, 0, 0}, y[8];
@@ -153,32 +161,32 @@ __global__ void __launch_bounds__(LN_T) layernorm_fwd_kernel(const void* X, cons
 }
 
 template <bool BF16>
-__global__ void __launch_bounds__(LN_T) layernorm_bwd_kernel(const void* X, const void* gamma, const float* mean,
+__global__ void __launch_bounds__(LNB_T) layernorm_bwd_kernel(const void* X, const void* gamma, const float* mean,
                                                              const float* rstd, const void* dY, void* dX, float* part,
                                                              int64_t rows, int64_t h) {
-  __shared__ float red[8];
+  __shared__ float red[16];
   const int nch = (int)(h / 8);
   const float inv_h = 1.0f / (float)h;
   float* pg_row = part + (int64_t)blockIdx.x * h;                    // dgamma partial of this workgroup
   float* pb_row = part + ((int64_t)gridDim.x + blockIdx.x) * h;      // dbeta partial
-  float pg[LN_MAXC][8], pb[LN_MAXC][8];
+  float pg[LNB_MAXC][8], pb[LNB_MAXC][8];
 #pragma unroll
-  for (int k = 0; k < LN_MAXC; ++k)
+  for (int k = 0; k < LNB_MAXC; ++k)
 #pragma unroll
     for (int e = 0; e < 8; ++e) { pg[k][e] = 0.0f; pb[k][e] = 0.0f; }
   // columns past the register-held chunks accumulate in the partial rows
-  for (int c = threadIdx.x + LN_T * LN_MAXC; c < nch; c += LN_T)
+  for (int c = threadIdx.x + LNB_T * LNB_MAXC; c < nch; c += LNB_T)
 #pragma unroll
     for (int e = 0; e < 8; ++e) { pg_row[8 * c + e] = 0.0f; pb_row[8 * c + e] = 0.0f; }
 
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     const int64_t base = row * h;
     const float mu = mean[row], r = rstd[row];
-    float xh[LN_MAXC][8], gy[LN_MAXC][8];
+    float xh[LNB_MAXC][8], gy[LNB_MAXC][8];
     float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
-    for (int k = 0; k < LN_MAXC; ++k) {
-      const int c = threadIdx.x + LN_T * k;
+    for (int k = 0; k < LNB_MAXC; ++k) {
+      const int c = threadIdx.x + LNB_T * k;
       if (c < nch) {
         float x[8], dy[8], gm[8];
         load8<BF16>(X, base + 8 * c, x);
@@ -196,7 +204,7 @@ __global__ void __launch_bounds__(LN_T) layernorm_bwd_kernel(const void* X, cons
         }
       }
     }
-    for (int c = threadIdx.x + LN_T * LN_MAXC; c < nch; c += LN_T) {
+    for (int c = threadIdx.x + LNB_T * LNB_MAXC; c < nch; c += LNB_T) {
       float x[8], dy[8], gm[8];
       load8<BF16>(X, base + 8 * c, x);
       load8<BF16>(dY, base + 8 * c, dy);
@@ -210,11 +218,11 @@ __global__ void __launch_bounds__(LN_T) layernorm_bwd_kernel(const void* X, cons
         pb_row[8 * c + e] += dy[e];
       }
     }
-    block_sum2(s1, s2, red);
+    block_sum2<LNB_T / 64>(s1, s2, red);
     const float a = s1 * inv_h, b = s2 * inv_h;
 #pragma unroll
-    for (int k = 0; k < LN_MAXC; ++k) {
-      const int c = threadIdx.x + LN_T * k;
+    for (int k = 0; k < LNB_MAXC; ++k) {
+      const int c = threadIdx.x + LNB_T * k;
       if (c < nch) {
         float dx[8];
 #pragma unroll
@@ -222,7 +230,7 @@ __global__ void __launch_bounds__(LN_T) layernorm_bwd_kernel(const void* X, cons
         store8<BF16>(dX, base + 8 * c, dx);
       }
     }
-    for (int c = threadIdx.x + LN_T * LN_MAXC; c < nch; c += LN_T) {
+    for (int c = threadIdx.x + LNB_T * LNB_MAXC; c < nch; c += LNB_T) {
       float x[8], dy[8], gm[8], dx[8];
       load8<BF16>(X, base + 8 * c, x);
       load8<BF16>(dY, base + 8 * c, dy);
@@ -233,8 +241,8 @@ __global__ void __launch_bounds__(LN_T) layernorm_bwd_kernel(const void* X, cons
     }
   }
 #pragma unroll
-  for (int k = 0; k < LN_MAXC; ++k) {
-    const int c = threadIdx.x + LN_T * k;
+  for (int k = 0; k < LNB_MAXC; ++k) {
+    const int c = threadIdx.x + LNB_T * k;
     if (c < nch) {
       *(f32x4*)(pg_row + 8 * c) = f32x4{pg[k][0], pg[k][1], pg[k][2], pg[k][3]};
       *(f32x4*)(pg_row + 8 * c + 4) = f32x4{pg[k][4], pg[k][5], pg[k][6], pg[k][7]};
@@ -314,7 +322,7 @@ __global__ void __launch_bounds__(256) dropout_bwd_kernel(const void* dOut, void
 }  // namespace
 
 int layernorm_bwd_chunks(int64_t rows) {
-  int64_t c = (rows + 7) / 8;   // about 8 rows per workgroup
+  int64_t c = (rows + 3) / 4;   // about 4 rows per workgroup, one workgroup per CU at most
   if (c > 256) c = 256;
   if (c < 1) c = 1;
   return (int)c;
@@ -343,10 +351,10 @@ hipError_t layernorm_bwd(const void* X, const void* gamma, const float* mean, co
   LaunchInfo info{"layernorm_bwd", 0.0, el * (3.0 * rows * h + h) + 8.0 * rows + 8.0 * chunks * h};
   trace_begin(s);
   if (bf16)
-    hipLaunchKernelGGL(layernorm_bwd_kernel<true>, dim3((unsigned)chunks), dim3(LN_T), 0, s, X, gamma, mean, rstd, dY,
+    hipLaunchKernelGGL(layernorm_bwd_kernel<true>, dim3((unsigned)chunks), dim3(LNB_T), 0, s, X, gamma, mean, rstd, dY,
                        dX, ws, rows, h);
   else
-    hipLaunchKernelGGL(layernorm_bwd_kernel<false>, dim3((unsigned)chunks), dim3(LN_T), 0, s, X, gamma, mean, rstd,
+    hipLaunchKernelGGL(layernorm_bwd_kernel<false>, dim3((unsigned)chunks), dim3(LNB_T), 0, s, X, gamma, mean, rstd,
                        dY, dX, ws, rows, h);
   trace_end(s, info);
   hipError_t e = hipGetLastError();
