@@ -41,16 +41,20 @@ struct Shape {
   static_assert(LOADS % 2 == 0 && (LOADS / 2) * NT == BKEYS * CH, "whole K and V loads per thread");
 };
 
-// LDS layouts of a block (rows = keys, 16-byte chunks XOR-permuted per row):
-//  * K: chunk c of row r in slot c ^ (r mod CH).  A score operand read takes
-//    one 16-byte chunk from 32 consecutive rows, which then fall in different
-//    banks.
-//  * V: chunk c of row r in slot c ^ (2 r mod CH).  A transposing read takes
-//    8 bytes from each of 4 consecutive rows; the rows land 32 bytes apart.
+// LDS layout of a block (rows = keys or queries, D bf16 each): 16-byte chunk c
+// of row r sits in slot c ^ f(r), one permutation that keeps both kinds of
+// operand read free of bank conflicts (64 banks of 4 bytes = 256 bytes):
+//  * row reads (16 bytes per lane, chunk c of 16 consecutive rows): f takes 16
+//    distinct values on 16 consecutive rows (D = 128; for D = 64, where two
+//    rows share a 256-byte bank sweep, 8 distinct values on each row parity);
+//  * transposing reads (8 bytes per lane; 32 lanes cover chunks 4j..4j+3 of rows
+//    4i..4i+3): the four rows' 64-byte chunk groups land in four different
+//    quarters of the bank sweep.
+//  D = 128: f(r) = 4 (r mod 4) + (r / 4 mod 4);  D = 64: f(r) = 4 (r / 2 mod 2) + (r / 4 mod 4).
 template <int D>
-__device__ __forceinline__ int k_slot(int c, int r) { return c ^ (r & (Shape<D>::CH - 1)); }
-template <int D>
-__device__ __forceinline__ int v_slot(int c, int r) { return c ^ ((2 * r) & (Shape<D>::CH - 1)); }
+__device__ __forceinline__ int kv_slot(int c, int r) {
+  return D == 128 ? c ^ (4 * (r & 3) + ((r >> 2) & 3)) : c ^ (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
+}
 
 __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -127,9 +131,9 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(FwdArgs a) {
       const int c = tid + NT * (i % (SH::LOADS / 2));
       const int r = c / SH::CH, ch = c % SH::CH;
       if (i < SH::LOADS / 2)
-        *(bf16x8*)(&smem[buf][0][r * SH::ROW_BYTES + k_slot<D>(ch, r) * 16]) = stage[i];
+        *(bf16x8*)(&smem[buf][0][r * SH::ROW_BYTES + kv_slot<D>(ch, r) * 16]) = stage[i];
       else
-        *(bf16x8*)(&smem[buf][1][r * SH::ROW_BYTES + v_slot<D>(ch, r) * 16]) = stage[i];
+        *(bf16x8*)(&smem[buf][1][r * SH::ROW_BYTES + kv_slot<D>(ch, r) * 16]) = stage[i];
     }
   };
 
@@ -160,7 +164,7 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int kr = 32 * t + l32;
-        const bf16x8 kf = *(const bf16x8*)(Ks + kr * SH::ROW_BYTES + k_slot<D>(2 * s + hh, kr) * 16);
+        const bf16x8 kf = *(const bf16x8*)(Ks + kr * SH::ROW_BYTES + kv_slot<D>(2 * s + hh, kr) * 16);
         sacc[t] = mfma(kf, qf[s], sacc[t]);
       }
 
@@ -215,8 +219,8 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(FwdArgs a) {
       for (int t = 0; t < SH::DT; ++t) {
         const int col = 32 * t + tr_c;
         const int ra = 16 * s + tr_r, rb = ra + 8;
-        const bf16x4 lo = read_tr(Vs + ra * SH::ROW_BYTES + v_slot<D>(col >> 3, ra) * 16 + (col & 7) * 2);
-        const bf16x4 hi = read_tr(Vs + rb * SH::ROW_BYTES + v_slot<D>(col >> 3, rb) * 16 + (col & 7) * 2);
+        const bf16x4 lo = read_tr(Vs + ra * SH::ROW_BYTES + kv_slot<D>(col >> 3, ra) * 16 + (col & 7) * 2);
+        const bf16x4 hi = read_tr(Vs + rb * SH::ROW_BYTES + kv_slot<D>(col >> 3, rb) * 16 + (col & 7) * 2);
         bf16x8 vf;
         vf[0] = lo[0]; vf[1] = lo[1]; vf[2] = lo[2]; vf[3] = lo[3];
         vf[4] = hi[0]; vf[5] = hi[1]; vf[6] = hi[2]; vf[7] = hi[3];
@@ -299,21 +303,21 @@ __global__ void __launch_bounds__(NT) attn_bwd_dot_kernel(BwdArgs a) {
   }
 }
 
-// 16-byte operand of an MFMA from a k_slot-swizzled LDS block: row r, 16-wide
+// 16-byte operand of an MFMA from an LDS block: row r, 16-wide
 // slice s, lane half hh (elements 16 s + 8 hh .. + 7).
 template <int D>
 __device__ __forceinline__ bf16x8 lds_row_frag(const char* blk, int r, int s, int hh) {
-  return *(const bf16x8*)(blk + r * Shape<D>::ROW_BYTES + k_slot<D>(2 * s + hh, r) * 16);
+  return *(const bf16x8*)(blk + r * Shape<D>::ROW_BYTES + kv_slot<D>(2 * s + hh, r) * 16);
 }
 
-// Transposed operand from a k_slot-swizzled LDS block: columns 32 t + (0..31)
+// Transposed operand from an LDS block: columns 32 t + (0..31)
 // of rows 16 s + {4 hh + 0..3, 8 + 4 hh + 0..3} (the accumulator order).
 template <int D>
 __device__ __forceinline__ bf16x8 lds_tr_frag(const char* blk, int t, int s, int tr_r, int tr_c) {
   const int col = 32 * t + tr_c;
   const int ra = 16 * s + tr_r, rb = ra + 8;
-  const bf16x4 lo = read_tr(blk + ra * Shape<D>::ROW_BYTES + k_slot<D>(col >> 3, ra) * 16 + (col & 7) * 2);
-  const bf16x4 hi = read_tr(blk + rb * Shape<D>::ROW_BYTES + k_slot<D>(col >> 3, rb) * 16 + (col & 7) * 2);
+  const bf16x4 lo = read_tr(blk + ra * Shape<D>::ROW_BYTES + kv_slot<D>(col >> 3, ra) * 16 + (col & 7) * 2);
+  const bf16x4 hi = read_tr(blk + rb * Shape<D>::ROW_BYTES + kv_slot<D>(col >> 3, rb) * 16 + (col & 7) * 2);
   bf16x8 v;
   v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
   v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
@@ -321,7 +325,7 @@ __device__ __forceinline__ bf16x8 lds_tr_frag(const char* blk, int t, int s, int
 }
 
 // Two 64-row blocks (rows r0.. of the sequence; base / row stride of each) into
-// registers, zero past the sequence end, then into k_slot-swizzled LDS.
+// registers, zero past the sequence end, then into LDS (kv_slot layout).
 template <int D>
 struct PairStager {
   static constexpr int L = Shape<D>::LOADS;  // 16-byte loads per thread (both blocks)
@@ -341,7 +345,7 @@ struct PairStager {
     for (int i = 0; i < L; ++i) {
       const int c = tid + NT * (i % (L / 2));
       const int r = c / Shape<D>::CH, ch = c % Shape<D>::CH;
-      *(bf16x8*)((i < L / 2 ? blk0 : blk1) + r * Shape<D>::ROW_BYTES + k_slot<D>(ch, r) * 16) = st[i];
+      *(bf16x8*)((i < L / 2 ? blk0 : blk1) + r * Shape<D>::ROW_BYTES + kv_slot<D>(ch, r) * 16) = st[i];
     }
   }
 };
