@@ -168,7 +168,8 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(FwdArgs a) {
         sacc[t] = mfma(kf, qf[s], sacc[t]);
       }
 
-    // Scale to log2 units, mask, block maximum of this lane's query.
+    // Mask, block maximum of this lane's query (on the raw scores: the scale is
+    // positive), then p = 2^(s * log2(e)/sqrt(D) - m) as one FMA and an exp2.
     const int k0 = j * BKEYS;
     const bool masked = (k0 + BKEYS > a.S) || (a.causal && k0 + BKEYS - 1 > wq0);
     float mloc = -INFINITY;
@@ -176,32 +177,34 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(FwdArgs a) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float x = sacc[t][v] * a.scale_log2;
         if (masked) {
           const int key = k0 + 32 * t + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (key >= a.S || (a.causal && key > qi)) x = -INFINITY;
+          if (key >= a.S || (a.causal && key > qi)) sacc[t][v] = -INFINITY;
         }
-        sacc[t][v] = x;
-        mloc = fmaxf(mloc, x);
+        mloc = fmaxf(mloc, sacc[t][v]);
       }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);      // finite: key 0 is allowed for every query
+    const float m_new = fmaxf(m_run, mloc * a.scale_log2);   // finite: key 0 is allowed for every query
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float psum = 0.0f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(sacc[t][v] - m_new);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][v], a.scale_log2, -m_new));
         sacc[t][v] = p;
         psum += p;
       }
     l_run = l_run * alpha + psum;
     m_run = m_new;
+    // The running maximum rarely moves after the first blocks: rescale O only
+    // when it moved for some lane of the wave.
+    if (__ballot(alpha != 1.0f) != 0) {
 #pragma unroll
-    for (int t = 0; t < SH::DT; ++t)
+      for (int t = 0; t < SH::DT; ++t)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[t][v] *= alpha;
+        for (int v = 0; v < 16; ++v) oacc[t][v] *= alpha;
+    }
 
     // P^T as the B operand of 16-key slice s: k slot m of lane half hh is key
     // 16 s + 8 (m / 4) + 4 hh + m % 4, i.e. accumulator element 8 (s % 2) + m
