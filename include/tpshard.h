@@ -34,8 +34,12 @@
  * Dtypes.  dtype = TP_BF16: activations, weights, biases and activation
  *   outputs are bfloat16; products accumulate in fp32 on the matrix cores
  *   and are rounded to nearest-even on store.  dtype = TP_FP32: everything is
- *   fp32 with fp32 arithmetic (a check path).  Parameter gradients (dW, db)
- *   are always fp32, for both dtypes.
+ *   fp32 with fp32 arithmetic (a check path).  dtype = TP_FP16: as TP_BF16 with
+ *   IEEE half storage and the fp16 matrix-core instruction -- the fp16 mixed-
+ *   precision path, used with dynamic loss scaling (tp_unscale_check_finite)
+ *   because half's range is narrow ([TUT] "最佳实践与调优建议" and "常见问题").
+ *   Parameter gradients (dW, db) are always fp32, for every dtype.  Core
+ *   attention takes TP_BF16 only.
  * Pointers.  Device pointers (hipMalloc / torch CUDA tensors), 16-byte aligned
  *   (TP_ERR_ALIGNMENT).  Required pointers must be non-NULL (TP_ERR_NULLPTR).
  *   No output may overlap any input or another output (TP_ERR_ALIAS).
@@ -62,7 +66,7 @@
 extern "C" {
 #endif
 
-typedef enum { TP_BF16 = 0, TP_FP32 = 1 } tp_dtype;
+typedef enum { TP_BF16 = 0, TP_FP32 = 1, TP_FP16 = 2 } tp_dtype;
 typedef enum { TP_ACT_NONE = 0, TP_ACT_GELU = 1 } tp_act;
 
 enum {
@@ -230,7 +234,7 @@ int tp_bias_gelu(const void* Z, const void* b, void* H, int64_t T, int64_t N, in
  *   softmax in fp32; no dropout;
  *   lse [Hl x T] fp32 (nullable, e.g. for inference): natural-log log-sum-exp of
  *   each query's scaled scores over its allowed keys (what the backward reads).
- * dtype must be TP_BF16 (TP_ERR_DTYPE otherwise).  Errors: head_dim not 64/128,
+ * dtype must be TP_BF16 (TP_ERR_DTYPE for TP_FP32 and TP_FP16).  Errors: head_dim not 64/128,
  * T not a multiple of seq, or 3*Hl*head_dim > 2^21 -> TP_ERR_DIM; heads not
  * divisible by tp_size -> TP_ERR_TP_DIVISIBILITY; causal not 0/1 -> TP_ERR_ARG;
  * outputs overlapping the input or each other -> TP_ERR_ALIAS.
@@ -301,6 +305,18 @@ int tp_bias_dropout_add_fwd(const void* Y, const void* b, const void* residual, 
 int tp_bias_dropout_add_bwd(const void* dOut, void* dY, float* db, void* workspace, size_t workspace_bytes,
                             int32_t accumulate, int64_t rows, int64_t h, double p_drop, uint64_t seed,
                             uint64_t offset, int32_t dtype, void* stream);
+
+/*
+ * Loss-scaling hook of the fp16 path ([TUT] "常见问题": a loss that turns NaN
+ * under fp16 calls for dynamic loss scaling; [INTRO] 1.4.1: fp32 master
+ * weights).  For an fp32 gradient buffer grads[n] (device, 16-byte aligned):
+ * grads *= inv_scale in place, and *found_nonfinite (device int32, 4-byte
+ * aligned) is set to 1 if any element is inf or NaN -- it is never cleared,
+ * so one flag can collect several buffers; the caller zeroes it before the
+ * step and skips the optimizer step (and lowers the scale) when it is set.
+ * inv_scale > 0 and finite (TP_ERR_ARG); 1 <= n <= 2^36 (TP_ERR_DIM).
+ */
+int tp_unscale_check_finite(float* grads, int64_t n, float inv_scale, int32_t* found_nonfinite, void* stream);
 
 /*
  * Workspace bytes needed by `op` (TP_OP_*).  Arguments are those of the

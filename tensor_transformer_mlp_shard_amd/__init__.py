@@ -25,10 +25,10 @@ __all__ = [
     "column_linear", "row_linear", "mlp_shard_fwd", "mlp_shard_bwd", "column_linear_bwd",
     "row_linear_bwd", "bias_grad", "bias_gelu", "workspace_size", "trace_start", "trace_stop",
     "attention_fwd", "attention_bwd", "layernorm_fwd", "layernorm_bwd", "bias_dropout_add_fwd",
-    "bias_dropout_add_bwd", "mfma_probe", "library_path", "NativeLibraryMissing",
+    "bias_dropout_add_bwd", "unscale_check_finite", "mfma_probe", "library_path", "NativeLibraryMissing",
 ]
 
-_DT = {torch.bfloat16: _native.TP_BF16, torch.float32: _native.TP_FP32}
+_DT = {torch.bfloat16: _native.TP_BF16, torch.float32: _native.TP_FP32, torch.float16: _native.TP_FP16}
 
 
 def library_path() -> str:
@@ -38,7 +38,7 @@ def library_path() -> str:
 
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype not in _DT:
-        raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+        raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16, float16 or float32")
     return _DT[t.dtype]
 
 
@@ -408,6 +408,16 @@ def bias_dropout_add_bwd(dout, *, p: float, seed: int, offset: int = 0, want_db:
                                                _stream(dev))
     _native.check(st, "tp_bias_dropout_add_bwd")
     return dY, db
+
+
+def unscale_check_finite(grads, inv_scale: float, found):
+    """grads (fp32, contiguous) *= inv_scale in place; sets found (int32 [1] on the
+    device) to 1 if any element is inf or NaN.  found is never cleared here."""
+    _check("grads", grads, tuple(grads.shape), torch.float32, grads.device)
+    _check("found", found, (1,), torch.int32, grads.device)
+    st = _native.lib().tp_unscale_check_finite(_ptr(grads), grads.numel(), float(inv_scale), _ptr(found),
+                                               _stream(grads.device))
+    _native.check(st, "tp_unscale_check_finite")
 
 
 def trace_start(max_launches: int = 4096) -> None:

@@ -7,7 +7,7 @@ import threading
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpshard.so")
 
-TP_BF16, TP_FP32 = 0, 1
+TP_BF16, TP_FP32, TP_FP16 = 0, 1, 2
 TP_ACT_NONE, TP_ACT_GELU = 0, 1
 TP_OP_COLUMN_LINEAR_BWD, TP_OP_ROW_LINEAR_BWD, TP_OP_MLP_SHARD_BWD, TP_OP_BIAS_GRAD = 1, 2, 3, 4
 TP_OP_ATTENTION_BWD, TP_OP_MLP_SHARD_BWD_RECOMPUTE, TP_OP_LAYERNORM_BWD, TP_OP_BIAS_DROPOUT_ADD_BWD = 5, 6, 7, 8
@@ -46,6 +46,7 @@ PROTOTYPES = {
                                        ctypes.c_uint64, _i32, _p]),
     "tp_bias_dropout_add_bwd": (_i32, [_p, _p, _fp, _p, _sz, _i32, _i64, _i64, ctypes.c_double, ctypes.c_uint64,
                                        ctypes.c_uint64, _i32, _p]),
+    "tp_unscale_check_finite": (_i32, [_p, _i64, ctypes.c_float, _p, _p]),
     "tp_mfma_probe": (_i32, [_i32, _i32, _p, _p, _p]),
     "tp_wall_clock_rate_khz": (_i32, [ctypes.POINTER(_i32)]),
     "tp_trace_start": (_i32, [_i32]),

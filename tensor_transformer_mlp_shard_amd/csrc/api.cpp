@@ -86,7 +86,12 @@ int check_alias(const std::vector<Buf>& ins, const std::vector<Buf>& outs) {
   return TP_OK;
 }
 
-int check_dtype(int32_t dtype) { return (dtype == TP_BF16 || dtype == TP_FP32) ? TP_OK : TP_ERR_DTYPE; }
+int check_dtype(int32_t dtype) {
+  return (dtype == TP_BF16 || dtype == TP_FP32 || dtype == TP_FP16) ? TP_OK : TP_ERR_DTYPE;
+}
+
+// The element code of a validated dtype.
+Elem elem_of(int32_t dtype) { return dtype == TP_FP32 ? ELEM_F32 : dtype == TP_FP16 ? ELEM_F16 : ELEM_BF16; }
 
 #define TP_TRY(expr)              \
   do {                            \
@@ -100,7 +105,8 @@ int check_dtype(int32_t dtype) { return (dtype == TP_BF16 || dtype == TP_FP32) ?
   } while (0)
 
 hipError_t gemm(int32_t dtype, const GemmArgs& g, bool ak, bool bk, Epi epi, hipStream_t s) {
-  return dtype == TP_FP32 ? gemm_f32(g, ak, bk, epi, s) : gemm_bf16(g, ak, bk, epi, s);
+  if (dtype == TP_FP32) return gemm_f32(g, ak, bk, epi, s);
+  return dtype == TP_FP16 ? gemm_f16(g, ak, bk, epi, s) : gemm_bf16(g, ak, bk, epi, s);
 }
 
 GemmArgs make_args(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N, int64_t K,
@@ -336,8 +342,8 @@ static int mlp_bwd_gemms(const void* X, const void* A_i, const void* B_i, const 
   GemmArgs g4 = make_args(dZ, f, A_i, f, T, h, f, dX_i, h);
   HIP_TRY(gemm(dtype, g4, true, true, EPI_STORE, s));
   // db1_i = sum_t dZ, db2 = sum_t dY
-  if (db1_i) HIP_TRY(colsum(dZ, dtype == TP_BF16, db1_i, part, accumulate, T, f, s));
-  if (db2) HIP_TRY(colsum(dY, dtype == TP_BF16, db2, part, accumulate, T, h, s));
+  if (db1_i) HIP_TRY(colsum(dZ, elem_of(dtype), db1_i, part, accumulate, T, f, s));
+  if (db2) HIP_TRY(colsum(dY, elem_of(dtype), db2, part, accumulate, T, h, s));
   return TP_OK;
 }
 
@@ -404,7 +410,7 @@ int tp_mlp_shard_bwd_recompute(const void* X, const void* A_i, const void* b1_i,
     Z = Zw;
   } else {
     // Z saved (it already holds the bias): H = GeLU(Z)
-    HIP_TRY(bias_gelu(Z_i, nullptr, H, dtype == TP_BF16, T, f, s));
+    HIP_TRY(bias_gelu(Z_i, nullptr, H, elem_of(dtype), T, f, s));
   }
   float* part = (float*)(ws + 3 * act);
   return mlp_bwd_gemms(X, A_i, B_i, Z, H, dY, dX_i, dA_i, db1_i, dB_i, db2, dZ, part, accumulate, T, h, f, dtype,
@@ -437,7 +443,7 @@ int tp_column_linear_bwd(const void* X, const void* W_i, const void* dY_i, void*
   GemmArgs g2 = make_args(X, K, dY_i, n, K, n, T, dW_i, n);
   g2.accumulate = accumulate;
   HIP_TRY(gemm(dtype, g2, false, false, EPI_F32, s));
-  if (db_i) HIP_TRY(colsum(dY_i, dtype == TP_BF16, db_i, (float*)workspace, accumulate, T, n, s));
+  if (db_i) HIP_TRY(colsum(dY_i, elem_of(dtype), db_i, (float*)workspace, accumulate, T, n, s));
   return TP_OK;
 }
 
@@ -466,7 +472,7 @@ int tp_row_linear_bwd(const void* X_i, const void* W_i, const void* dY, void* dX
   GemmArgs g2 = make_args(X_i, k, dY, N, k, N, T, dW_i, N);
   g2.accumulate = accumulate;
   HIP_TRY(gemm(dtype, g2, false, false, EPI_F32, s));
-  if (db) HIP_TRY(colsum(dY, dtype == TP_BF16, db, (float*)workspace, accumulate, T, N, s));
+  if (db) HIP_TRY(colsum(dY, elem_of(dtype), db, (float*)workspace, accumulate, T, N, s));
   return TP_OK;
 }
 
@@ -482,7 +488,7 @@ int tp_bias_grad(const void* dY, float* db, void* workspace, size_t workspace_by
   const size_t need = tp_workspace_size(TP_OP_BIAS_GRAD, T, N, 0, 1, dtype);
   if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
   TP_TRY(check_alias({{dY, T * N * elsize(dtype)}}, {{db, N * 4}, {workspace, (int64_t)need}}));
-  HIP_TRY(colsum(dY, dtype == TP_BF16, db, (float*)workspace, accumulate, T, N, (hipStream_t)stream));
+  HIP_TRY(colsum(dY, elem_of(dtype), db, (float*)workspace, accumulate, T, N, (hipStream_t)stream));
   return TP_OK;
 }
 
@@ -495,7 +501,7 @@ int tp_bias_gelu(const void* Z, const void* b, void* H, int64_t T, int64_t N, in
   TP_TRY(check_ptrs_aligned({Z, b, H}));
   const int64_t es = elsize(dtype);
   TP_TRY(check_alias({{Z, T * N * es}, {b, N * es}}, {{H, T * N * es}}));
-  HIP_TRY(bias_gelu(Z, b, H, dtype == TP_BF16, T, N, (hipStream_t)stream));
+  HIP_TRY(bias_gelu(Z, b, H, elem_of(dtype), T, N, (hipStream_t)stream));
   return TP_OK;
 }
 
@@ -556,7 +562,7 @@ int tp_layernorm_fwd(const void* X, const void* gamma, const void* beta, void* Y
   const int64_t es = elsize(dtype);
   TP_TRY(check_alias({{X, rows * h * es}, {gamma, h * es}, {beta, beta ? h * es : 0}},
                      {{Y, rows * h * es}, {mean, mean ? rows * 4 : 0}, {rstd, rstd ? rows * 4 : 0}}));
-  HIP_TRY(layernorm_fwd(X, gamma, beta, Y, mean, rstd, rows, h, eps, dtype == TP_BF16, (hipStream_t)stream));
+  HIP_TRY(layernorm_fwd(X, gamma, beta, Y, mean, rstd, rows, h, eps, elem_of(dtype), (hipStream_t)stream));
   return TP_OK;
 }
 
@@ -575,7 +581,7 @@ int tp_layernorm_bwd(const void* X, const void* gamma, const float* mean, const 
                      {{dX, rows * h * es}, {dgamma, h * 4}, {dbeta, dbeta ? h * 4 : 0},
                       {workspace, (int64_t)need}}));
   HIP_TRY(layernorm_bwd(X, gamma, mean, rstd, dY, dX, dgamma, dbeta, (float*)workspace, accumulate, rows, h,
-                        dtype == TP_BF16, (hipStream_t)stream));
+                        elem_of(dtype), (hipStream_t)stream));
   return TP_OK;
 }
 
@@ -590,7 +596,7 @@ int tp_bias_dropout_add_fwd(const void* Y, const void* b, const void* residual, 
   TP_TRY(check_ptrs_aligned({Y, b, residual, out}));
   const int64_t es = elsize(dtype);
   TP_TRY(check_alias({{Y, rows * h * es}, {b, b ? h * es : 0}, {residual, rows * h * es}}, {{out, rows * h * es}}));
-  HIP_TRY(bias_dropout_add_fwd(Y, b, residual, out, rows, h, thr, scale, seed, offset, dtype == TP_BF16,
+  HIP_TRY(bias_dropout_add_fwd(Y, b, residual, out, rows, h, thr, scale, seed, offset, elem_of(dtype),
                                (hipStream_t)stream));
   return TP_OK;
 }
@@ -612,8 +618,20 @@ int tp_bias_dropout_add_bwd(const void* dOut, void* dY, float* db, void* workspa
   TP_TRY(check_alias({{dOut, rows * h * es}},
                      {{dY, rows * h * es}, {db, db ? h * 4 : 0}, {workspace, db ? (int64_t)need : 0}}));
   hipStream_t s = (hipStream_t)stream;
-  HIP_TRY(dropout_bwd(dOut, dY, rows, h, thr, scale, seed, offset, dtype == TP_BF16, s));
-  if (db) HIP_TRY(colsum(dY, dtype == TP_BF16, db, (float*)workspace, accumulate, rows, h, s));
+  HIP_TRY(dropout_bwd(dOut, dY, rows, h, thr, scale, seed, offset, elem_of(dtype), s));
+  if (db) HIP_TRY(colsum(dY, elem_of(dtype), db, (float*)workspace, accumulate, rows, h, s));
+  return TP_OK;
+}
+
+// ---------------------------------------------------------------- loss scaling
+int tp_unscale_check_finite(float* grads, int64_t n, float inv_scale, int32_t* found_nonfinite, void* stream) {
+  TP_TRY(check_nonnull({grads, found_nonfinite}));
+  if (n < 1 || n > kMaxElems) return TP_ERR_DIM;
+  if (!(inv_scale > 0.0f) || !std::isfinite(inv_scale)) return TP_ERR_ARG;
+  TP_TRY(check_ptrs_aligned({grads}));
+  if ((uintptr_t)found_nonfinite % 4 != 0) return TP_ERR_ALIGNMENT;
+  TP_TRY(check_alias({{grads, n * 4}}, {{found_nonfinite, 4}}));
+  HIP_TRY(unscale_check(grads, n, inv_scale, (int*)found_nonfinite, (hipStream_t)stream));
   return TP_OK;
 }
 

@@ -10,6 +10,7 @@
 // are no atomics, so the result is bitwise reproducible.
 //
 // Bias + GeLU.  H = GeLU(Z + b) with 8 elements per lane (16-byte bf16 loads).
+#include "elem.h"
 #include "side.h"
 
 namespace tps {
@@ -18,21 +19,7 @@ namespace {
 constexpr int CS_COLS = 512;  // columns per workgroup in pass 1
 constexpr int CS_THREADS = 256;
 
-template <bool IN_BF16>
-__device__ __forceinline__ void load8(const void* base, int64_t off, float* v) {
-  if (IN_BF16) {
-    const bf16x8 x = *(const bf16x8*)((const bf16*)base + off);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
-  } else {
-    const f32x4 a = *(const f32x4*)((const float*)base + off);
-    const f32x4 b = *(const f32x4*)((const float*)base + off + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
-  }
-}
-
-template <bool IN_BF16>
+template <typename E>
 __global__ void __launch_bounds__(CS_THREADS) colsum_partial_kernel(const void* in, float* part, int64_t T,
                                                                     int64_t N, int64_t rows_per_chunk) {
   __shared__ float red[4][CS_COLS];
@@ -44,7 +31,7 @@ __global__ void __launch_bounds__(CS_THREADS) colsum_partial_kernel(const void* 
   if (col < N) {
     for (int64_t r = r0 + wave; r < r1; r += 4) {
       float v[8];
-      load8<IN_BF16>(in, r * N + col, v);
+      load8<E>(in, r * N + col, v);
 #pragma unroll
       for (int e = 0; e < 8; ++e) s[e] += v[e];
     }
@@ -88,7 +75,7 @@ __global__ void __launch_bounds__(256) colsum_finalize_kernel(const float* part,
   }
 }
 
-template <bool IS_BF16>
+template <typename E>
 __global__ void __launch_bounds__(256) bias_gelu_kernel(const void* Z, const void* b, void* H, int64_t T,
                                                         int64_t N) {
   const int64_t nv = N / 8;
@@ -97,27 +84,53 @@ __global__ void __launch_bounds__(256) bias_gelu_kernel(const void* Z, const voi
   const int64_t row = idx / nv;
   const int64_t c = (idx - row * nv) * 8;
   float z[8], bb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  load8<IS_BF16>(Z, row * N + c, z);
-  if (b != nullptr) load8<IS_BF16>(b, c, bb);
+  load8<E>(Z, row * N + c, z);
+  if (b != nullptr) load8<E>(b, c, bb);
   float h[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float x = z[e] + bb[e];
     h[e] = 0.5f * x * (1.0f + erff(x * 0.7071067811865475f));
   }
-  if (IS_BF16) {
-    bf16x8 o;
+  store8<E>(H, row * N + c, h);
+}
+
+// Loss-scaling check: g *= inv_scale over n fp32 values (4 per thread per
+// step, grid-stride), and *found = 1 when any value is inf or NaN (one store
+// per wave that saw one; the flag is never cleared here).
+__global__ void __launch_bounds__(256) unscale_check_kernel(float* g, int64_t n, float inv_scale, int* found) {
+  const int64_t stride = (int64_t)gridDim.x * 256 * 4;
+  bool bad = false;
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 4 <= n) {
+      f32x4 v = *(f32x4*)(g + i);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (bf16)h[e];
-    *(bf16x8*)((bf16*)H + row * N + c) = o;
-  } else {
-    float* p = (float*)H + row * N + c;
-    *(f32x4*)p = f32x4{h[0], h[1], h[2], h[3]};
-    *(f32x4*)(p + 4) = f32x4{h[4], h[5], h[6], h[7]};
+      for (int e = 0; e < 4; ++e) {
+        bad |= !__builtin_isfinite(v[e]);
+        v[e] *= inv_scale;
+      }
+      *(f32x4*)(g + i) = v;
+    } else {
+      for (int64_t k = i; k < n; ++k) {
+        bad |= !__builtin_isfinite(g[k]);
+        g[k] *= inv_scale;
+      }
+    }
   }
+  if (__ballot(bad) != 0 && (threadIdx.x & 63) == 0) *found = 1;
 }
 
 }  // namespace
+
+hipError_t unscale_check(float* g, int64_t n, float inv_scale, int* found, hipStream_t s) {
+  int64_t blocks = (n + 1023) / 1024;
+  if (blocks > 4096) blocks = 4096;
+  LaunchInfo info{"unscale_check", 0.0, 8.0 * n};
+  trace_begin(s);
+  hipLaunchKernelGGL(unscale_check_kernel, dim3((unsigned)blocks), dim3(256), 0, s, g, n, inv_scale, found);
+  trace_end(s, info);
+  return hipGetLastError();
+}
 
 int colsum_chunks(int64_t T, int64_t N) {
   const int64_t col_blocks = (N + CS_COLS - 1) / CS_COLS;
@@ -129,17 +142,19 @@ int colsum_chunks(int64_t T, int64_t N) {
   return (int)chunks;
 }
 
-hipError_t colsum(const void* in, bool in_bf16, float* out, float* ws, int accumulate, int64_t T, int64_t N,
+hipError_t colsum(const void* in, Elem el, float* out, float* ws, int accumulate, int64_t T, int64_t N,
                   hipStream_t s) {
   const int chunks = colsum_chunks(T, N);
   const int64_t rows_per_chunk = (T + chunks - 1) / chunks;
   const dim3 grid1((unsigned)((N + CS_COLS - 1) / CS_COLS), (unsigned)chunks);
-  LaunchInfo info{"colsum_partial", 0.0, (in_bf16 ? 2.0 : 4.0) * T * (double)N + 4.0 * chunks * (double)N};
+  LaunchInfo info{"colsum_partial", 0.0, elem_bytes(el) * T * (double)N + 4.0 * chunks * (double)N};
   trace_begin(s);
-  if (in_bf16)
-    hipLaunchKernelGGL(colsum_partial_kernel<true>, grid1, dim3(CS_THREADS), 0, s, in, ws, T, N, rows_per_chunk);
+  if (el == ELEM_BF16)
+    hipLaunchKernelGGL(colsum_partial_kernel<bf16>, grid1, dim3(CS_THREADS), 0, s, in, ws, T, N, rows_per_chunk);
+  else if (el == ELEM_F16)
+    hipLaunchKernelGGL(colsum_partial_kernel<f16>, grid1, dim3(CS_THREADS), 0, s, in, ws, T, N, rows_per_chunk);
   else
-    hipLaunchKernelGGL(colsum_partial_kernel<false>, grid1, dim3(CS_THREADS), 0, s, in, ws, T, N, rows_per_chunk);
+    hipLaunchKernelGGL(colsum_partial_kernel<float>, grid1, dim3(CS_THREADS), 0, s, in, ws, T, N, rows_per_chunk);
   trace_end(s, info);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -161,14 +176,14 @@ hipError_t sum_partials(const float* part, float* out, int64_t N, int chunks, in
   return hipGetLastError();
 }
 
-hipError_t bias_gelu(const void* Z, const void* b, void* H, bool is_bf16, int64_t T, int64_t N, hipStream_t s) {
+hipError_t bias_gelu(const void* Z, const void* b, void* H, Elem el, int64_t T, int64_t N, hipStream_t s) {
   const int64_t n = T * (N / 8);
   const dim3 grid((unsigned)((n + 255) / 256));
-  const double el = is_bf16 ? 2.0 : 4.0;
-  LaunchInfo info{"bias_gelu", 0.0, el * (2.0 * T * (double)N + (b ? N : 0))};
+  LaunchInfo info{"bias_gelu", 0.0, elem_bytes(el) * (2.0 * T * (double)N + (b ? N : 0))};
   trace_begin(s);
-  if (is_bf16) hipLaunchKernelGGL(bias_gelu_kernel<true>, grid, dim3(256), 0, s, Z, b, H, T, N);
-  else hipLaunchKernelGGL(bias_gelu_kernel<false>, grid, dim3(256), 0, s, Z, b, H, T, N);
+  if (el == ELEM_BF16) hipLaunchKernelGGL(bias_gelu_kernel<bf16>, grid, dim3(256), 0, s, Z, b, H, T, N);
+  else if (el == ELEM_F16) hipLaunchKernelGGL(bias_gelu_kernel<f16>, grid, dim3(256), 0, s, Z, b, H, T, N);
+  else hipLaunchKernelGGL(bias_gelu_kernel<float>, grid, dim3(256), 0, s, Z, b, H, T, N);
   trace_end(s, info);
   return hipGetLastError();
 }

@@ -35,6 +35,7 @@ struct GemmArgs {
 // GEMM launchers (gemm_bf16.hip / gemm_f32.hip). Return hipSuccess or the
 // launch error.  a_kcontig / b_kcontig select the operand layouts.
 hipError_t gemm_bf16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s);
+hipError_t gemm_f16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s);
 hipError_t gemm_f32(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s);
 
 }  // namespace tps

@@ -1,7 +1,7 @@
-// bf16 GEMM with fused epilogues on the gfx950 matrix cores.
+// 16-bit (bf16 or fp16) GEMM with fused epilogues on the gfx950 matrix cores.
 //
 // C[M x N] = op(A)[M x K] * op(B)[K x N], fp32 accumulation in
-// v_mfma_f32_32x32x16_bf16, one epilogue applied to the accumulators in
+// v_mfma_f32_32x32x16_bf16 (or its fp16 twin), one epilogue applied to the accumulators in
 // registers before the only store (bias, bias + exact-erf GeLU with the
 // pre-activation saved, GeLU' for the backward, or fp32 store / accumulate).
 //
@@ -57,7 +57,24 @@ __device__ __forceinline__ float gelu_grad_f(float z) {
   return cdf + z * pdf;
 }
 
-__device__ __forceinline__ float bf2f(bf16 v) { return (float)v; }
+// The two 16-bit element types: operand vectors and the matching MFMA.
+template <typename E> struct Vec;
+template <> struct Vec<bf16> {
+  typedef bf16x8 v8;
+  typedef bf16x4 v4;
+  static constexpr const char* name = "bf16";
+};
+template <> struct Vec<f16> {
+  typedef f16x8 v8;
+  typedef f16x4 v4;
+  static constexpr const char* name = "f16";
+};
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 
 // Workgroup -> output tile.  Workgroups are handed to the 8 XCDs round-robin,
 // so consecutive ids are remapped to one XCD's contiguous range of logical
@@ -224,8 +241,10 @@ struct Copier {
 };
 
 // A consumer wave's MFMA operand reads from an LDS stage.
-template <class C, bool AK, bool BKC>
+template <class C, bool AK, bool BKC, typename E>
 struct Reader {
+  using V8 = typename Vec<E>::v8;
+  using V4 = typename Vec<E>::v4;
   int wm, wn, l32, hi, kswz, tr_row, tr_col, tr_swz_a, tr_swz_b;
 
   __device__ __forceinline__ void init(int wave, int lane) {
@@ -240,27 +259,27 @@ struct Reader {
     tr_swz_a = mn_swz<C::BM>(i16 >> 2);
     tr_swz_b = mn_swz<C::BN>(i16 >> 2);
   }
-  __device__ __forceinline__ bf16x8 frag_k(const char* panel, int row0, int s) const {
+  __device__ __forceinline__ V8 frag_k(const char* panel, int row0, int s) const {
     const int r = row0 + l32;
     const int slot = (2 * s + hi) ^ kswz;
-    return *(const bf16x8*)(panel + r * (KT * 2) + slot * 16);
+    return *(const V8*)(panel + r * (KT * 2) + slot * 16);
   }
-  __device__ __forceinline__ bf16x8 frag_mn(const char* panel, int row_bytes, int swz, int col0, int s) const {
+  __device__ __forceinline__ V8 frag_mn(const char* panel, int row_bytes, int swz, int col0, int s) const {
     const int col = col0 + tr_col;
     const int slot = (col >> 3) ^ swz;
     const char* p0 = panel + (16 * s + tr_row) * row_bytes + slot * 16 + (col & 7) * 2;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
     const i16x4 hv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) i16x4*)(p0 + 4 * row_bytes));
-    const bf16x4 lo_b = __builtin_bit_cast(bf16x4, lo);
-    const bf16x4 hi_b = __builtin_bit_cast(bf16x4, hv);
-    bf16x8 v;
+    const V4 lo_b = __builtin_bit_cast(V4, lo);
+    const V4 hi_b = __builtin_bit_cast(V4, hv);
+    V8 v;
     v[0] = lo_b[0]; v[1] = lo_b[1]; v[2] = lo_b[2]; v[3] = lo_b[3];
     v[4] = hi_b[0]; v[5] = hi_b[1]; v[6] = hi_b[2]; v[7] = hi_b[3];
     return v;
   }
   // Operands of 16-wide k slice s of K step kt.
-  __device__ __forceinline__ void load(const char* smem, int kt, int s, bf16x8* fa, bf16x8* fb) const {
+  __device__ __forceinline__ void load(const char* smem, int kt, int s, V8* fa, V8* fb) const {
     const char* sa = smem + (kt % C::NSTAGE) * C::STAGE;
     const char* sb = sa + C::A_BYTES;
 #pragma unroll
@@ -274,9 +293,10 @@ struct Reader {
 
 // Epilogue of one consumer wave.  Block (i, j), lane: row m = l32, columns
 // 8q + 4*(lane/32) + 0..3.
-template <class C, int EPI>
+template <class C, int EPI, typename E>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::FM][C::FN], int m0, int n0,
                                          int wave, int lane) {
+  using V4 = typename Vec<E>::v4;
   // The coordinates are passed through empty asm so that the compiler derives the
   // epilogue addresses here instead of hoisting them above the K loop, where they
   // would hold registers for its whole duration.
@@ -307,39 +327,40 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::FM]
           *(f32x4*)c = o;
         } else {
           if ((EPI == EPI_STORE || EPI == EPI_BIAS_GELU) && g.bias != nullptr) {
-            const bf16x4 b = *(const bf16x4*)((const bf16*)g.bias + n);
+            const V4 b = *(const V4*)((const E*)g.bias + n);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] += bf2f(b[e]);
+            for (int e = 0; e < 4; ++e) v[e] += (float)(b[e]);
           }
           if (EPI == EPI_BIAS_GELU && g.C2 != nullptr) {
-            bf16x4 z;
+            V4 z;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) z[e] = (bf16)v[e];
-            *(bf16x4*)((bf16*)g.C2 + (int64_t)m * g.ldc2 + n) = z;
+            for (int e = 0; e < 4; ++e) z[e] = (E)v[e];
+            *(V4*)((E*)g.C2 + (int64_t)m * g.ldc2 + n) = z;
           }
           if (EPI == EPI_BIAS_GELU) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = gelu_f(v[e]);
           }
           if (EPI == EPI_DGELU) {
-            const bf16x4 z = *(const bf16x4*)((const bf16*)g.aux + (int64_t)m * g.ldaux + n);
+            const V4 z = *(const V4*)((const E*)g.aux + (int64_t)m * g.ldaux + n);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f(bf2f(z[e]));
+            for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f((float)(z[e]));
           }
-          bf16x4 o;
+          V4 o;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
-          *(bf16x4*)((bf16*)g.C + (int64_t)m * g.ldc + n) = o;
+          for (int e = 0; e < 4; ++e) o[e] = (E)v[e];
+          *(V4*)((E*)g.C + (int64_t)m * g.ldc + n) = o;
         }
       }
     }
   }
 }
 
-template <class C, bool AK, bool BKC, int EPI>
+template <class C, bool AK, bool BKC, int EPI, typename E>
 __global__ void __attribute__((amdgpu_flat_work_group_size(C::NT, C::NT),
                                amdgpu_waves_per_eu(C::WAVES_PER_EU, C::WAVES_PER_EU)))
-gemm_bf16_kernel(GemmArgs g) {
+gemm_kernel(GemmArgs g) {
+  using V8 = typename Vec<E>::v8;
   constexpr int FM = C::FM, FN = C::FN, NVM = C::NVM, PREF = C::PREF;
   constexpr int NS = KT / 16;             // 16-wide k slices per step
   constexpr int LB = (NS - 1) & 1;        // operand buffer of the last slice (double buffering)
@@ -381,7 +402,7 @@ gemm_bf16_kernel(GemmArgs g) {
   }
 
   // ------------------------------------------------------------ consumer wave
-  Reader<C, AK, BKC> rd;
+  Reader<C, AK, BKC, E> rd;
   rd.init(wave, lane);
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -391,13 +412,11 @@ gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  auto mfma = [&](const bf16x8* fa_, const bf16x8* fb_, int i, int j) {
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb_[j], fa_[i], acc[i][j], 0, 0, 0);
-  };
+  auto mfma = [&](const V8* fa_, const V8* fb_, int i, int j) { acc[i][j] = mfma32(fb_[j], fa_[i], acc[i][j]); };
 
   if constexpr (C::NPROD > 0) {
     __syncthreads();  // step 0 is in LDS
-    bf16x8 fa[2][FM], fb[2][FN];
+    V8 fa[2][FM], fb[2][FN];
     rd.load(smem, 0, 0, fa[0], fb[0]);
     for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
@@ -436,7 +455,7 @@ gemm_bf16_kernel(GemmArgs g) {
     __syncthreads();
     constexpr int PRE_MF = FM * FN * (NS - 1) + FM_HALF * FN;   // MFMAs before the barrier
     static_assert(PRE_MF >= NVM, "not enough MFMAs to spread the copies over");
-    bf16x8 fa[FM], fb[FN];
+    V8 fa[FM], fb[FN];
     for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -463,7 +482,7 @@ gemm_bf16_kernel(GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no copy into this workgroup's LDS outlives it
   }
 
-  epilogue<C, EPI>(g, acc, m0, n0, wave, lane);
+  epilogue<C, EPI, E>(g, acc, m0, n0, wave, lane);
 }
 
 // Tile menu: split kernels (8 consumer + 4 producer waves) and shared kernels
@@ -476,9 +495,9 @@ using T128x128 = Cfg<128, 128, 4, 2>;
 using T256x384 = Cfg<256, 384, 0, 2>;
 using T384x256 = Cfg<384, 256, 0, 4>;
 
-template <class C, bool AK, bool BKC, int EPI>
+template <class C, bool AK, bool BKC, int EPI, typename E>
 const char* kname() {
-  static const std::string s = std::string("gemm_bf16_") + (AK ? "n" : "t") + (BKC ? "t" : "n") + "_" +
+  static const std::string s = std::string("gemm_") + Vec<E>::name + "_" + (AK ? "n" : "t") + (BKC ? "t" : "n") + "_" +
                                (EPI == EPI_STORE ? "store" : EPI == EPI_BIAS_GELU ? "bias_gelu"
                                 : EPI == EPI_DGELU ? "dgelu" : "f32") +
                                "_" + std::to_string(C::BM) + "x" + std::to_string(C::BN);
@@ -500,13 +519,13 @@ int choose_group_m(int tiles_m, int bm, int bn) {
   return best;
 }
 
-template <class C, bool AK, bool BKC, int EPI>
+template <class C, bool AK, bool BKC, int EPI, typename E>
 hipError_t launch_tile(const GemmArgs& g_in, hipStream_t s, const char** name) {
-  *name = kname<C, AK, BKC, EPI>();
+  *name = kname<C, AK, BKC, EPI, E>();
   GemmArgs g = g_in;
   const int tiles_m = (g.M + C::BM - 1) / C::BM, tiles_n = (g.N + C::BN - 1) / C::BN;
   g.group_m = choose_group_m(tiles_m, C::BM, C::BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<C, AK, BKC, EPI>), dim3(tiles_m * tiles_n), dim3(C::NT), 0, s, g);
+  hipLaunchKernelGGL((gemm_kernel<C, AK, BKC, EPI, E>), dim3(tiles_m * tiles_n), dim3(C::NT), 0, s, g);
   return hipGetLastError();
 }
 
@@ -530,23 +549,22 @@ TileChoice choose_tile(int M, int N) {
   return pick;
 }
 
-template <bool AK, bool BKC, int EPI>
+template <bool AK, bool BKC, int EPI, typename E>
 hipError_t launch_shape(const GemmArgs& g, hipStream_t s, const char** name) {
   const TileChoice t = choose_tile(g.M, g.N);
-  if (t.bm == 256 && t.bn == 384) return launch_tile<T256x384, AK, BKC, EPI>(g, s, name);
-  if (t.bm == 384 && t.bn == 256) return launch_tile<T384x256, AK, BKC, EPI>(g, s, name);
-  if (t.bm == 256 && t.bn == 192) return launch_tile<T256x192, AK, BKC, EPI>(g, s, name);
-  if (t.bm == 192 && t.bn == 256) return launch_tile<T192x256, AK, BKC, EPI>(g, s, name);
-  if (t.bm == 256 && t.bn == 128) return launch_tile<T256x128, AK, BKC, EPI>(g, s, name);
-  if (t.bm == 128 && t.bn == 256) return launch_tile<T128x256, AK, BKC, EPI>(g, s, name);
-  return launch_tile<T128x128, AK, BKC, EPI>(g, s, name);
+  if (t.bm == 256 && t.bn == 384) return launch_tile<T256x384, AK, BKC, EPI, E>(g, s, name);
+  if (t.bm == 384 && t.bn == 256) return launch_tile<T384x256, AK, BKC, EPI, E>(g, s, name);
+  if (t.bm == 256 && t.bn == 192) return launch_tile<T256x192, AK, BKC, EPI, E>(g, s, name);
+  if (t.bm == 192 && t.bn == 256) return launch_tile<T192x256, AK, BKC, EPI, E>(g, s, name);
+  if (t.bm == 256 && t.bn == 128) return launch_tile<T256x128, AK, BKC, EPI, E>(g, s, name);
+  if (t.bm == 128 && t.bn == 256) return launch_tile<T128x256, AK, BKC, EPI, E>(g, s, name);
+  return launch_tile<T128x128, AK, BKC, EPI, E>(g, s, name);
 }
 
-}  // namespace
-
-hipError_t gemm_bf16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s) {
+template <typename E>
+hipError_t gemm16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s) {
   LaunchInfo info;
-  info.name = "gemm_bf16";
+  info.name = "gemm16";
   info.flops = 2.0 * g.M * (double)g.N * g.K;
   const double out_bytes = (epi == EPI_F32 ? 4.0 * (g.accumulate ? 2 : 1) : 2.0) * g.M * (double)g.N;
   info.bytes = 2.0 * ((double)g.M * g.K + (double)g.K * g.N) + out_bytes +
@@ -556,13 +574,24 @@ hipError_t gemm_bf16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi,
   // weight gradient (TN).
   hipError_t e = hipErrorInvalidValue;
   trace_begin(s);
-  if (a_kcontig && !b_kcontig && epi == EPI_STORE) e = launch_shape<true, false, EPI_STORE>(g, s, &info.name);
-  else if (a_kcontig && !b_kcontig && epi == EPI_BIAS_GELU) e = launch_shape<true, false, EPI_BIAS_GELU>(g, s, &info.name);
-  else if (a_kcontig && b_kcontig && epi == EPI_STORE) e = launch_shape<true, true, EPI_STORE>(g, s, &info.name);
-  else if (a_kcontig && b_kcontig && epi == EPI_DGELU) e = launch_shape<true, true, EPI_DGELU>(g, s, &info.name);
-  else if (!a_kcontig && !b_kcontig && epi == EPI_F32) e = launch_shape<false, false, EPI_F32>(g, s, &info.name);
+  if (a_kcontig && !b_kcontig && epi == EPI_STORE) e = launch_shape<true, false, EPI_STORE, E>(g, s, &info.name);
+  else if (a_kcontig && !b_kcontig && epi == EPI_BIAS_GELU)
+    e = launch_shape<true, false, EPI_BIAS_GELU, E>(g, s, &info.name);
+  else if (a_kcontig && b_kcontig && epi == EPI_STORE) e = launch_shape<true, true, EPI_STORE, E>(g, s, &info.name);
+  else if (a_kcontig && b_kcontig && epi == EPI_DGELU) e = launch_shape<true, true, EPI_DGELU, E>(g, s, &info.name);
+  else if (!a_kcontig && !b_kcontig && epi == EPI_F32) e = launch_shape<false, false, EPI_F32, E>(g, s, &info.name);
   trace_end(s, info);
   return e;
+}
+
+}  // namespace
+
+hipError_t gemm_bf16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s) {
+  return gemm16<bf16>(g, a_kcontig, b_kcontig, epi, s);
+}
+
+hipError_t gemm_f16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s) {
+  return gemm16<f16>(g, a_kcontig, b_kcontig, epi, s);
 }
 
 }  // namespace tps

@@ -21,6 +21,7 @@
 // increments) on the element's counter, so the backward regenerates the mask
 // instead of storing it.  A thread handles 8 consecutive elements: two Philox
 // blocks (the offset is a multiple of 8).
+#include "elem.h"
 #include "side.h"
 #include "sp_edge.h"
 
@@ -31,34 +32,6 @@ constexpr int LN_T = 256;       // forward: threads per row
 constexpr int LN_MAXC = 6;      // forward: register-held 8-element chunks per thread (rows up to 12288 read once)
 constexpr int LNB_T = 512;      // backward: threads per workgroup
 constexpr int LNB_MAXC = 3;     // backward: register-held chunks per thread (rows up to 12288)
-
-template <bool BF16>
-__device__ __forceinline__ void load8(const void* base, int64_t off, float* v) {
-  if (BF16) {
-    const bf16x8 x = *(const bf16x8*)((const bf16*)base + off);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
-  } else {
-    const f32x4 a = *(const f32x4*)((const float*)base + off);
-    const f32x4 b = *(const f32x4*)((const float*)base + off + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
-  }
-}
-
-template <bool BF16>
-__device__ __forceinline__ void store8(void* base, int64_t off, const float* v) {
-  if (BF16) {
-    bf16x8 x;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (bf16)v[e];
-    *(bf16x8*)((bf16*)base + off) = x;
-  } else {
-    float* p = (float*)base + off;
-    *(f32x4*)p = f32x4{v[0], v[1], v[2], v[3]};
-    *(f32x4*)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
-  }
-}
 
 // Sums over the workgroup (W waves), the same values in every thread; `red` is
 // 2 W floats of LDS.  The wave sums are added in a fixed order.
@@ -85,7 +58,7 @@ __device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
   }
 }
 
-template <bool BF16>
+template <typename T>
 __global__ void __launch_bounds__(LN_T) layernorm_fwd_kernel(const void* X, const void* gamma, const void* beta,
                                                              void* Y, float* mean_out, float* rstd_out, int64_t h,
                                                              float eps) {
@@ -99,14 +72,14 @@ __global__ void __launch_bounds__(LN_T) layernorm_fwd_kernel(const void* X, cons
   for (int k = 0; k < LN_MAXC; ++k) {
     const int c = threadIdx.x + LN_T * k;
     if (c < nch) {
-      load8<BF16>(X, base + 8 * c, v[k]);
+      load8<T>(X, base + 8 * c, v[k]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) s += v[k][e];
     }
   }
   for (int c = threadIdx.x + LN_T * LN_MAXC; c < nch; c += LN_T) {
     float t[8];
-    load8<BF16>(X, base + 8 * c, t);
+    load8<T>(X, base + 8 * c, t);
 #pragma unroll
     for (int e = 0; e < 8; ++e) s += t[e];
   }
@@ -127,7 +100,7 @@ __global__ void __launch_bounds__(LN_T) layernorm_fwd_kernel(const void* X, cons
   }
   for (int c = threadIdx.x + LN_T * LN_MAXC; c < nch; c += LN_T) {
     float t[8];
-    load8<BF16>(X, base + 8 * c, t);
+    load8<T>(X, base + 8 * c, t);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float d = t[e] - mean;
@@ -138,11 +111,11 @@ __global__ void __launch_bounds__(LN_T) layernorm_fwd_kernel(const void* X, cons
   const float rstd = 1.0f / sqrtf(q * inv_h + eps);
   auto emit = [&](int c, const float* x) {
     float g[8], bb[8] = {0, 0, 0, 0, 0, 0, 0, 0}, y[8];
-    load8<BF16>(gamma, 8 * c, g);
-    if (beta != nullptr) load8<BF16>(beta, 8 * c, bb);
+    load8<T>(gamma, 8 * c, g);
+    if (beta != nullptr) load8<T>(beta, 8 * c, bb);
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = (x[e] - mean) * rstd * g[e] + bb[e];
-    store8<BF16>(Y, base + 8 * c, y);
+    store8<T>(Y, base + 8 * c, y);
   };
 #pragma unroll
   for (int k = 0; k < LN_MAXC; ++k) {
@@ -151,7 +124,7 @@ __global__ void __launch_bounds__(LN_T) layernorm_fwd_kernel(const void* X, cons
   }
   for (int c = threadIdx.x + LN_T * LN_MAXC; c < nch; c += LN_T) {
     float x[8];
-    load8<BF16>(X, base + 8 * c, x);
+    load8<T>(X, base + 8 * c, x);
     emit(c, x);
   }
   if (threadIdx.x == 0 && mean_out != nullptr) {
@@ -160,7 +133,7 @@ __global__ void __launch_bounds__(LN_T) layernorm_fwd_kernel(const void* X, cons
   }
 }
 
-template <bool BF16>
+template <typename T>
 __global__ void __launch_bounds__(LNB_T) layernorm_bwd_kernel(const void* X, const void* gamma, const float* mean,
                                                              const float* rstd, const void* dY, void* dX, float* part,
                                                              int64_t rows, int64_t h) {
@@ -189,9 +162,9 @@ __global__ void __launch_bounds__(LNB_T) layernorm_bwd_kernel(const void* X, con
       const int c = threadIdx.x + LNB_T * k;
       if (c < nch) {
         float x[8], dy[8], gm[8];
-        load8<BF16>(X, base + 8 * c, x);
-        load8<BF16>(dY, base + 8 * c, dy);
-        load8<BF16>(gamma, 8 * c, gm);
+        load8<T>(X, base + 8 * c, x);
+        load8<T>(dY, base + 8 * c, dy);
+        load8<T>(gamma, 8 * c, gm);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float xhat = (x[e] - mu) * r, g = dy[e] * gm[e];
@@ -206,9 +179,9 @@ __global__ void __launch_bounds__(LNB_T) layernorm_bwd_kernel(const void* X, con
     }
     for (int c = threadIdx.x + LNB_T * LNB_MAXC; c < nch; c += LNB_T) {
       float x[8], dy[8], gm[8];
-      load8<BF16>(X, base + 8 * c, x);
-      load8<BF16>(dY, base + 8 * c, dy);
-      load8<BF16>(gamma, 8 * c, gm);
+      load8<T>(X, base + 8 * c, x);
+      load8<T>(dY, base + 8 * c, dy);
+      load8<T>(gamma, 8 * c, gm);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float xhat = (x[e] - mu) * r, g = dy[e] * gm[e];
@@ -227,17 +200,17 @@ __global__ void __launch_bounds__(LNB_T) layernorm_bwd_kernel(const void* X, con
         float dx[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) dx[e] = r * (gy[k][e] - a - xh[k][e] * b);
-        store8<BF16>(dX, base + 8 * c, dx);
+        store8<T>(dX, base + 8 * c, dx);
       }
     }
     for (int c = threadIdx.x + LNB_T * LNB_MAXC; c < nch; c += LNB_T) {
       float x[8], dy[8], gm[8], dx[8];
-      load8<BF16>(X, base + 8 * c, x);
-      load8<BF16>(dY, base + 8 * c, dy);
-      load8<BF16>(gamma, 8 * c, gm);
+      load8<T>(X, base + 8 * c, x);
+      load8<T>(dY, base + 8 * c, dy);
+      load8<T>(gamma, 8 * c, gm);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dx[e] = r * (dy[e] * gm[e] - a - (x[e] - mu) * r * b);
-      store8<BF16>(dX, base + 8 * c, dx);
+      store8<T>(dX, base + 8 * c, dx);
     }
   }
 #pragma unroll
@@ -286,7 +259,7 @@ __device__ __forceinline__ void keep8(int64_t e0, uint64_t offset, uint64_t seed
   for (int e = 0; e < 8; ++e) keep[e] = (uint64_t)w[e] < threshold;
 }
 
-template <bool BF16>
+template <typename T>
 __global__ void __launch_bounds__(256) bias_dropout_add_kernel(const void* Y, const void* b, const void* residual,
                                                                void* out, int64_t n8, int64_t h, uint64_t threshold,
                                                                float scale, uint64_t seed, uint64_t offset) {
@@ -296,15 +269,15 @@ __global__ void __launch_bounds__(256) bias_dropout_add_kernel(const void* Y, co
   float y[8], bb[8] = {0, 0, 0, 0, 0, 0, 0, 0}, r[8], o[8];
   bool keep[8];
   keep8(e0, offset, seed, threshold, keep);
-  load8<BF16>(Y, e0, y);
-  if (b != nullptr) load8<BF16>(b, e0 % h, bb);
-  load8<BF16>(residual, e0, r);
+  load8<T>(Y, e0, y);
+  if (b != nullptr) load8<T>(b, e0 % h, bb);
+  load8<T>(residual, e0, r);
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = r[e] + (keep[e] ? (y[e] + bb[e]) * scale : 0.0f);
-  store8<BF16>(out, e0, o);
+  store8<T>(out, e0, o);
 }
 
-template <bool BF16>
+template <typename T>
 __global__ void __launch_bounds__(256) dropout_bwd_kernel(const void* dOut, void* dY, int64_t n8, uint64_t threshold,
                                                           float scale, uint64_t seed, uint64_t offset) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -313,10 +286,10 @@ __global__ void __launch_bounds__(256) dropout_bwd_kernel(const void* dOut, void
   float g[8], o[8];
   bool keep[8];
   keep8(e0, offset, seed, threshold, keep);
-  load8<BF16>(dOut, e0, g);
+  load8<T>(dOut, e0, g);
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = keep[e] ? g[e] * scale : 0.0f;
-  store8<BF16>(dY, e0, o);
+  store8<T>(dY, e0, o);
 }
 
 }  // namespace
@@ -329,33 +302,36 @@ int layernorm_bwd_chunks(int64_t rows) {
 }
 
 hipError_t layernorm_fwd(const void* X, const void* gamma, const void* beta, void* Y, float* mean, float* rstd,
-                         int64_t rows, int64_t h, float eps, bool bf16, hipStream_t s) {
-  const double el = bf16 ? 2.0 : 4.0;
+                         int64_t rows, int64_t h, float eps, Elem et, hipStream_t s) {
+  const double el = elem_bytes(et);
   LaunchInfo info{"layernorm_fwd", 0.0, el * (2.0 * rows * h + (beta ? 2.0 : 1.0) * h) + (mean ? 8.0 * rows : 0.0)};
+  const dim3 grid((unsigned)rows);
   trace_begin(s);
-  if (bf16)
-    hipLaunchKernelGGL(layernorm_fwd_kernel<true>, dim3((unsigned)rows), dim3(LN_T), 0, s, X, gamma, beta, Y, mean,
-                       rstd, h, eps);
+  if (et == ELEM_BF16)
+    hipLaunchKernelGGL(layernorm_fwd_kernel<bf16>, grid, dim3(LN_T), 0, s, X, gamma, beta, Y, mean, rstd, h, eps);
+  else if (et == ELEM_F16)
+    hipLaunchKernelGGL(layernorm_fwd_kernel<f16>, grid, dim3(LN_T), 0, s, X, gamma, beta, Y, mean, rstd, h, eps);
   else
-    hipLaunchKernelGGL(layernorm_fwd_kernel<false>, dim3((unsigned)rows), dim3(LN_T), 0, s, X, gamma, beta, Y, mean,
-                       rstd, h, eps);
+    hipLaunchKernelGGL(layernorm_fwd_kernel<float>, grid, dim3(LN_T), 0, s, X, gamma, beta, Y, mean, rstd, h, eps);
   trace_end(s, info);
   return hipGetLastError();
 }
 
 hipError_t layernorm_bwd(const void* X, const void* gamma, const float* mean, const float* rstd, const void* dY,
                          void* dX, float* dgamma, float* dbeta, float* ws, int accumulate, int64_t rows, int64_t h,
-                         bool bf16, hipStream_t s) {
+                         Elem et, hipStream_t s) {
   const int chunks = layernorm_bwd_chunks(rows);
-  const double el = bf16 ? 2.0 : 4.0;
+  const double el = elem_bytes(et);
   LaunchInfo info{"layernorm_bwd", 0.0, el * (3.0 * rows * h + h) + 8.0 * rows + 8.0 * chunks * h};
+  const dim3 grid((unsigned)chunks);
   trace_begin(s);
-  if (bf16)
-    hipLaunchKernelGGL(layernorm_bwd_kernel<true>, dim3((unsigned)chunks), dim3(LNB_T), 0, s, X, gamma, mean, rstd, dY,
-                       dX, ws, rows, h);
+  if (et == ELEM_BF16)
+    hipLaunchKernelGGL(layernorm_bwd_kernel<bf16>, grid, dim3(LNB_T), 0, s, X, gamma, mean, rstd, dY, dX, ws, rows, h);
+  else if (et == ELEM_F16)
+    hipLaunchKernelGGL(layernorm_bwd_kernel<f16>, grid, dim3(LNB_T), 0, s, X, gamma, mean, rstd, dY, dX, ws, rows, h);
   else
-    hipLaunchKernelGGL(layernorm_bwd_kernel<false>, dim3((unsigned)chunks), dim3(LNB_T), 0, s, X, gamma, mean, rstd,
-                       dY, dX, ws, rows, h);
+    hipLaunchKernelGGL(layernorm_bwd_kernel<float>, grid, dim3(LNB_T), 0, s, X, gamma, mean, rstd, dY, dX, ws, rows,
+                       h);
   trace_end(s, info);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -365,34 +341,37 @@ hipError_t layernorm_bwd(const void* X, const void* gamma, const float* mean, co
 }
 
 hipError_t bias_dropout_add_fwd(const void* Y, const void* b, const void* residual, void* out, int64_t rows,
-                                int64_t h, uint64_t threshold, float scale, uint64_t seed, uint64_t offset, bool bf16,
+                                int64_t h, uint64_t threshold, float scale, uint64_t seed, uint64_t offset, Elem et,
                                 hipStream_t s) {
   const int64_t n8 = rows * h / 8;
-  const double el = bf16 ? 2.0 : 4.0;
-  LaunchInfo info{"bias_dropout_add", 0.0, el * (3.0 * rows * h + (b ? h : 0))};
+  LaunchInfo info{"bias_dropout_add", 0.0, elem_bytes(et) * (3.0 * rows * h + (b ? h : 0))};
   trace_begin(s);
   const dim3 grid((unsigned)((n8 + 255) / 256));
-  if (bf16)
-    hipLaunchKernelGGL(bias_dropout_add_kernel<true>, grid, dim3(256), 0, s, Y, b, residual, out, n8, h, threshold,
+  if (et == ELEM_BF16)
+    hipLaunchKernelGGL(bias_dropout_add_kernel<bf16>, grid, dim3(256), 0, s, Y, b, residual, out, n8, h, threshold,
+                       scale, seed, offset);
+  else if (et == ELEM_F16)
+    hipLaunchKernelGGL(bias_dropout_add_kernel<f16>, grid, dim3(256), 0, s, Y, b, residual, out, n8, h, threshold,
                        scale, seed, offset);
   else
-    hipLaunchKernelGGL(bias_dropout_add_kernel<false>, grid, dim3(256), 0, s, Y, b, residual, out, n8, h, threshold,
+    hipLaunchKernelGGL(bias_dropout_add_kernel<float>, grid, dim3(256), 0, s, Y, b, residual, out, n8, h, threshold,
                        scale, seed, offset);
   trace_end(s, info);
   return hipGetLastError();
 }
 
 hipError_t dropout_bwd(const void* dOut, void* dY, int64_t rows, int64_t h, uint64_t threshold, float scale,
-                       uint64_t seed, uint64_t offset, bool bf16, hipStream_t s) {
+                       uint64_t seed, uint64_t offset, Elem et, hipStream_t s) {
   const int64_t n8 = rows * h / 8;
-  const double el = bf16 ? 2.0 : 4.0;
-  LaunchInfo info{"dropout_bwd", 0.0, el * 2.0 * rows * h};
+  LaunchInfo info{"dropout_bwd", 0.0, elem_bytes(et) * 2.0 * rows * h};
   trace_begin(s);
   const dim3 grid((unsigned)((n8 + 255) / 256));
-  if (bf16)
-    hipLaunchKernelGGL(dropout_bwd_kernel<true>, grid, dim3(256), 0, s, dOut, dY, n8, threshold, scale, seed, offset);
+  if (et == ELEM_BF16)
+    hipLaunchKernelGGL(dropout_bwd_kernel<bf16>, grid, dim3(256), 0, s, dOut, dY, n8, threshold, scale, seed, offset);
+  else if (et == ELEM_F16)
+    hipLaunchKernelGGL(dropout_bwd_kernel<f16>, grid, dim3(256), 0, s, dOut, dY, n8, threshold, scale, seed, offset);
   else
-    hipLaunchKernelGGL(dropout_bwd_kernel<false>, grid, dim3(256), 0, s, dOut, dY, n8, threshold, scale, seed, offset);
+    hipLaunchKernelGGL(dropout_bwd_kernel<float>, grid, dim3(256), 0, s, dOut, dY, n8, threshold, scale, seed, offset);
   trace_end(s, info);
   return hipGetLastError();
 }

@@ -27,7 +27,7 @@ class Workload:
     h: int               # hidden size
     F: int               # full FFN width (mlp) or full QKV width (attn)
     tp: int              # tensor-parallel degree
-    dtype: str           # "bf16" or "fp32"
+    dtype: str           # "bf16", "fp16" or "fp32"
     sigma_w: float       # weight / bias std
     seed: int
     full: bool           # draw unsharded weights (then slice) or the rank's shard only
@@ -84,7 +84,7 @@ WORKLOADS = {
                                     False, "175B TP=8: 8192 tokens / 8 rows of 12288"),
 }
 
-_TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}
+_TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32, "fp16": torch.float16}
 
 
 def seeded(seed: int) -> torch.Generator:

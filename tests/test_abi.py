@@ -103,7 +103,7 @@ def test_mlp_fwd_validation(lib):
     assert f(A0, A1, None, A2, None, A3, A4, 128, 256, 1024, 3, 0, S) == -3
     assert f(A0, A1, None, A2, None, A3, A4, 128, 260, 1024, 2, 0, S) == -4
     assert f(A0, A1, None, A2, A3, A3, A4, 128, 256, 1024, 2, 0, S) == -6          # Z == H
-    assert f(A0, A1, None, A2, None, A3, A4, 128, 256, 1024, 2, 2, S) == -5
+    assert f(A0, A1, None, A2, None, A3, A4, 128, 256, 1024, 2, 3, S) == -5          # no dtype 3
 
 
 def test_mlp_bwd_validation(lib):
@@ -163,6 +163,7 @@ def test_attention_fwd_validation(lib):
     # (QKV, O, lse, T, seq, heads, head_dim, tp, causal, dtype, stream); 2 local heads of 64 -> QKV 384 wide
     assert f(A0, A1, A2, 256, 128, 4, 64, 2, 1, 1, S) == -5          # fp32: MFMA kernels are bf16 only
     assert f(A0, A1, A2, 256, 128, 4, 64, 2, 1, 7, S) == -5
+    assert f(A0, A1, A2, 256, 128, 4, 64, 2, 1, 2, S) == -5          # fp16: not for attention
     assert f(A0, A1, A2, 256, 128, 4, 96, 2, 1, 0, S) == -2          # head_dim not 64/128
     assert f(A0, A1, A2, 250, 128, 4, 64, 2, 1, 0, S) == -2          # T not whole sequences
     assert f(A0, A1, A2, 0, 128, 4, 64, 2, 1, 0, S) == -2
@@ -240,3 +241,16 @@ def test_sp_edge_validation(lib):
     assert e(DY, DX, DG, None, 0, 0, 64, 1024, 0.1, 1, 0, 0, S) == -7  # db wanted, no workspace
     assert e(DY, DY, None, None, 0, 0, 64, 1024, 0.1, 1, 0, 0, S) == -6
     assert e(DY, DX, None, None, 0, 0, 64, 1024, 0.1, 1, 12, 0, S) == -9
+
+
+def test_unscale_check_validation(lib):
+    f = lib.tp_unscale_check_finite
+    G, F = P(0x1000000), P(0x2000000)
+    assert f(None, 16, ctypes.c_float(0.5), F, S) == -1
+    assert f(G, 16, ctypes.c_float(0.5), None, S) == -1
+    assert f(G, 0, ctypes.c_float(0.5), F, S) == -2
+    assert f(G, 16, ctypes.c_float(0.0), F, S) == -9
+    assert f(G, 16, ctypes.c_float(float("inf")), F, S) == -9
+    assert f(G, 16, ctypes.c_float(float("nan")), F, S) == -9
+    assert f(P(0x1000004), 16, ctypes.c_float(0.5), F, S) == -4
+    assert f(G, 16, ctypes.c_float(0.5), P(0x1000008), S) == -6        # flag inside the buffer

@@ -19,7 +19,8 @@ from tensor_transformer_mlp_shard_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-TOL = {torch.bfloat16: 5e-3, torch.float32: 1e-5}
+TOL = {torch.bfloat16: 5e-3, torch.float16: 5e-3, torch.float32: 1e-5}
+DTS = {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}
 DEV = "cuda:0"
 
 
@@ -147,6 +148,42 @@ def test_gpt175b_mlp_tp8_sampled():
                       _sample(w.T, 64, 13), _sample(w.f, 64, 14))
 
 
+def test_gpt175b_mlp_tp8_sampled_fp16():
+    """The same 175B shard with half storage (fp16 matrix-core path)."""
+    w = synth.WORKLOADS["gpt175b_mlp_tp8"]
+    d = synth.mlp_inputs(w.T, w.h, w.F, w.tp, "fp16", w.sigma_w, w.seed, full=False)
+    print("gpt175b mlp tp8 fp16", flush=True)
+    check_mlp_sampled(d["X"], d["A"], d["b1"], d["B"], d["dY"], w.tp,
+                      _sample(w.T, 64, 13), _sample(w.f, 64, 14))
+
+
+def test_unscale_check_finite():
+    """Loss-scaling hook: exact power-of-two unscale, flag raised by inf or NaN
+    anywhere (tail elements included) and never cleared."""
+    rng = np.random.default_rng(3)
+    found = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for n in (1, 5, 4096, 1 << 20, (1 << 20) + 3):
+        x = (rng.standard_normal(n) * 1e3).astype(np.float32)
+        g = torch.from_numpy(x.copy()).to(DEV)
+        tps.unscale_check_finite(g, 2.0 ** -10, found)
+        torch.cuda.synchronize()
+        ref, bad = oracle.unscale_check_finite(x, 2.0 ** -10)
+        assert not bad and int(found.item()) == 0
+        assert np.array_equal(g.cpu().numpy().astype(np.float64), ref), n
+    for n, pos, val in ((5, 4, np.inf), (4096, 17, np.nan), ((1 << 20) + 3, (1 << 20) + 2, -np.inf)):
+        x = rng.standard_normal(n).astype(np.float32)
+        x[pos] = val
+        found.zero_()
+        g = torch.from_numpy(x).to(DEV)
+        tps.unscale_check_finite(g, 0.5, found)
+        torch.cuda.synchronize()
+        assert int(found.item()) == 1, (n, pos)
+        clean = torch.ones(64, device=DEV)
+        tps.unscale_check_finite(clean, 1.0, found)     # a finite buffer leaves the flag set
+        torch.cuda.synchronize()
+        assert int(found.item()) == 1
+
+
 def test_gpt175b_attn_tp8_sampled():
     w = synth.WORKLOADS["gpt175b_attn_tp8"]
     d = synth.inputs_for(w)
@@ -192,19 +229,19 @@ EDGE = [
 ]
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32], ids=["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("shape", EDGE, ids=[f"T{s[0]}_h{s[1]}_f{s[2]}_p{s[3]}" for s in EDGE])
 def test_mlp_edges(shape, dtype):
     T, h, f, p = shape
-    dt = "bf16" if dtype == torch.bfloat16 else "fp32"
+    dt = DTS[dtype]
     d = synth.mlp_inputs(T, h, f * p, p, dt, 0.05, seed=T * 7 + h, full=False)
     print(f"edge {shape} {dt}", flush=True)
     check_mlp_full(d["X"], d["A"], d["b1"], d["B"], d["dY"], p, dtype)
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32], ids=["bf16", "fp16", "fp32"])
 def test_linears_edges(dtype):
-    dt = "bf16" if dtype == torch.bfloat16 else "fp32"
+    dt = DTS[dtype]
     tol = TOL[dtype]
     for T, K, N, p in [(5, 48, 96, 2), (133, 288, 544, 4), (300, 1024, 264, 1)]:
         print(f"linears T{T} K{K} N{N} p{p} {dt}", flush=True)
@@ -273,9 +310,9 @@ def test_accumulate_adds():
         torch.testing.assert_close(acc[k], base[k] + g1[k], rtol=1e-6, atol=1e-6)
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32], ids=["bf16", "fp16", "fp32"])
 def test_bias_gelu_and_bias_grad(dtype):
-    dt = "bf16" if dtype == torch.bfloat16 else "fp32"
+    dt = DTS[dtype]
     g = synth.seeded(31)
     Z = synth.randn(g, (333, 1048), 2.0, dt)
     b = synth.randn(g, (1048,), 0.5, dt)
@@ -312,13 +349,13 @@ def test_mfma_probe_reports_plausible_rates():
     assert 0.3 * ceiling < r["tflops"] < 1.1 * ceiling
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32], ids=["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("T,h,f,p", [(1, 8, 8, 1), (131, 264, 136, 4), (512, 1024, 2048, 2)])
 def test_mlp_bwd_recompute(T, h, f, p, dtype):
     """Selective recompute: Z kept (H recomputed) and nothing kept (Z, H
     recomputed by the fc1 GEMM) give the oracle's gradients; the second is
     bitwise the saved-activation backward (same kernels on the same inputs)."""
-    dt = "bf16" if dtype == torch.bfloat16 else "fp32"
+    dt = DTS[dtype]
     tol = TOL[dtype]
     d = synth.mlp_inputs(T, h, f * p, p, dt, 0.05, seed=T * 11 + h, full=False)
     Xd, Ad, b1d, Bd, dYd = (dev(d[k]) for k in ("X", "A", "b1", "B", "dY"))

@@ -15,9 +15,9 @@ from tensor_transformer_mlp_shard_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-TOL = {torch.bfloat16: 5e-3, torch.float32: 1e-5}
+TOL = {torch.bfloat16: 5e-3, torch.float16: 5e-3, torch.float32: 1e-5}
 DEV = "cuda:0"
-DT = {torch.bfloat16: "bf16", torch.float32: "fp32"}
+DT = {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}
 
 
 def f64(t):
@@ -33,7 +33,7 @@ def _rel(name, got, ref, tol):
 LN_SHAPES = [(1, 8), (3, 1032), (17, 2048), (64, 12288), (5, 18432), (1024, 12288), (2048, 1024)]
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32], ids=["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("rows,h", LN_SHAPES, ids=[f"{r}x{h}" for r, h in LN_SHAPES])
 def test_layernorm(rows, h, dtype):
     x = synth.sp_edge_inputs(rows, h, DT[dtype], 0.02, seed=rows * 31 + h)
@@ -77,7 +77,7 @@ DROP_CASES = [(1, 8, 0.1, 1, 0), (37, 1032, 0.5, (1 << 40) + 3, 8 * 1001), (5, 6
               (64, 12288, 0.1, 1234, 1 << 35), (1024, 12288, 0.1, 2024, 0)]
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32], ids=["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("rows,h,p,seed,offset", DROP_CASES, ids=[f"{c[0]}x{c[1]}_p{c[2]}" for c in DROP_CASES])
 def test_bias_dropout_add(rows, h, p, seed, offset, dtype):
     x = synth.sp_edge_inputs(rows, h, DT[dtype], 0.02, seed=rows + h + 5)
