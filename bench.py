@@ -324,6 +324,9 @@ def main():
     ap.add_argument("--cpu-frac", type=int, default=1, help="oracle sample = 1/N of the tokens")
     ap.add_argument("--part", choices=["all", "mlp", "attn", "core_attn"], default="all",
                     help="run only one part (for profiling runs)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the measurements outside the step (selective recompute, core attention, "
+                         "sequence-parallel edge): for profiler runs whose per-kernel averages must be the step's")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of this many MiB, three times (a known-size "
                          "reference for hardware byte counters)")
@@ -420,7 +423,7 @@ def main():
                        "note": "register-only bf16 MFMA stream on random operands, no memory traffic"},
         "kernels": kern,
     }
-    if args.part == "all":
+    if args.part == "all" and not args.no_extras:
         out["sp_edge"] = measure_sp_edge(torch, device, min(args.steps, 50), min(args.warmup, 10))
         out["selective_recompute"] = measure_recompute(torch, shard, min(args.steps, 50), min(args.warmup, 10))
         out["core_attention"] = measure_core_attention(torch, device, min(args.steps, 50), min(args.warmup, 10))
