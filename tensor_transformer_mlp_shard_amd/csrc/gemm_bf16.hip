@@ -32,7 +32,8 @@
 //
 // Output.  The MFMA is issued with the B fragment as its first operand, so a
 // lane's 16 results of a block are 4 runs of 4 consecutive columns of one row
-// of C: the epilogue loads bias / Z and stores 4 values at a time.
+// of C; the epilogue stages them through LDS and writes whole 16-byte runs of
+// rows (and reads GeLU's Z the same way).
 //
 // Edges.  M, N and K may be ragged against the tile (T is arbitrary); loads
 // outside the matrix read zero and stores outside it are skipped.  Feature
@@ -291,68 +292,131 @@ struct Reader {
   }
 };
 
-// Epilogue of one consumer wave.  Block (i, j), lane: row m = l32, columns
-// 8q + 4*(lane/32) + 0..3.
+// Epilogue of one consumer wave, through LDS.  The accumulators hold, per lane,
+// 4 runs of 4 consecutive columns of one row (block (i, j), lane: row l32,
+// columns 32 j + 8 q + 4 (lane / 32) + 0..3); stored directly, every store
+// instruction would write 16-byte pieces of 32 different rows.  Instead each
+// wave stages 32-row strips of its sub-tile in the (now idle) LDS ring --
+// rows padded so the register-order accesses fall in different banks -- and
+// moves them between LDS and memory as 16-byte chunks with consecutive lanes
+// along a row.  The GeLU' operand Z comes in the same way.
 template <class C, int EPI, typename E>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::FM][C::FN], int m0, int n0,
-                                         int wave, int lane) {
+                                         int wave, int lane, char* smem) {
   using V4 = typename Vec<E>::v4;
+  using V8 = typename Vec<E>::v8;
   // The coordinates are passed through empty asm so that the compiler derives the
   // epilogue addresses here instead of hoisting them above the K loop, where they
   // would hold registers for its whole duration.
   asm volatile("" : "+v"(lane));
   asm volatile("" : "+s"(m0), "+s"(n0), "+s"(wave));
-  const int l32 = lane & 31;
-  const int col_lane = 4 * (lane >> 5);
+  constexpr bool F32 = EPI == EPI_F32;
+  constexpr int ES = F32 ? 4 : 2;                    // output element bytes
+  constexpr int ROWB = C::WN * ES;                   // bytes of a strip row
+  constexpr int PITCH = ROWB + (F32 ? 16 : 8);       // padded LDS row pitch
+  constexpr int CPR = ROWB / 16;                     // 16-byte chunks per row
+  constexpr int NCH = 32 * CPR;                      // chunks per strip
+  constexpr int NIT = (NCH + 63) / 64;
+  static_assert(ROWB % 16 == 0, "strip rows are whole 16-byte chunks");
+  static_assert(C::NCONS * 32 * PITCH <= C::NSTAGE * C::STAGE, "strips fit in the ring");
+  char* strip = smem + wave * 32 * PITCH;
+  const int l32 = lane & 31, hh = lane >> 5;
   const int wm = wave / C::CN, wn = wave % C::CN;
+  const int col0 = n0 + wn * C::WN;
+
+  // Strip rows <-> memory, 16-byte chunks (cols past N and rows past M skipped).
+  auto to_mem = [&](void* base, int64_t ld, int row0) {
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-    const int m = m0 + wm * C::WM + 32 * i + l32;
-    if (m >= g.M) continue;
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * C::WN + 32 * j + 8 * q + col_lane;
-        if (n >= g.N) continue;
-        float v[4] = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                      acc[i][j][4 * q + 3]};
-        if (EPI == EPI_F32) {
-          float* c = (float*)g.C + (int64_t)m * g.ldc + n;
-          f32x4 o = {v[0], v[1], v[2], v[3]};
-          if (g.accumulate) {
-            const f32x4 old = *(const f32x4*)c;
-            o[0] += old[0]; o[1] += old[1]; o[2] += old[2]; o[3] += old[3];
-          }
-          *(f32x4*)c = o;
-        } else {
-          if ((EPI == EPI_STORE || EPI == EPI_BIAS_GELU) && g.bias != nullptr) {
-            const V4 b = *(const V4*)((const E*)g.bias + n);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] += (float)(b[e]);
-          }
-          if (EPI == EPI_BIAS_GELU && g.C2 != nullptr) {
-            V4 z;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) z[e] = (E)v[e];
-            *(V4*)((E*)g.C2 + (int64_t)m * g.ldc2 + n) = z;
-          }
-          if (EPI == EPI_BIAS_GELU) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = gelu_f(v[e]);
-          }
-          if (EPI == EPI_DGELU) {
-            const V4 z = *(const V4*)((const E*)g.aux + (int64_t)m * g.ldaux + n);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] *= gelu_grad_f((float)(z[e]));
-          }
-          V4 o;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = (E)v[e];
-          *(V4*)((E*)g.C + (int64_t)m * g.ldc + n) = o;
+    for (int it = 0; it < NIT; ++it) {
+      const int c = it * 64 + lane;
+      if (NCH % 64 != 0 && c >= NCH) continue;
+      const int r = c / CPR, cc = c % CPR;
+      const int m = row0 + r, n = col0 + cc * (16 / ES);
+      if (m >= g.M || n >= g.N) continue;
+      const char* p = strip + r * PITCH + cc * 16;
+      if (F32) {
+        f32x4 v = *(const f32x4*)p;
+        float* dst = (float*)base + (int64_t)m * ld + n;
+        if (g.accumulate) {
+          const f32x4 old = *(const f32x4*)dst;
+          v[0] += old[0]; v[1] += old[1]; v[2] += old[2]; v[3] += old[3];
         }
+        *(f32x4*)dst = v;
+      } else {
+        *(V8*)((E*)base + (int64_t)m * ld + n) = *(const V8*)p;
       }
     }
+  };
+  auto from_mem = [&](const void* base, int64_t ld, int row0) {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int c = it * 64 + lane;
+      if (NCH % 64 != 0 && c >= NCH) continue;
+      const int r = c / CPR, cc = c % CPR;
+      const int m = row0 + r, n = col0 + cc * 8;
+      V8 v{};
+      if (m < g.M && n < g.N) v = *(const V8*)((const E*)base + (int64_t)m * ld + n);
+      *(V8*)(strip + r * PITCH + cc * 16) = v;
+    }
+  };
+  // This lane's 4 values of run (j, q) in the strip.
+  auto at = [&](int j, int q) { return strip + l32 * PITCH + (32 * j + 8 * q + 4 * hh) * ES; };
+
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    const int row0 = m0 + wm * C::WM + 32 * i;
+    if (F32) {
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *(f32x4*)at(j, q) = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+      to_mem(g.C, g.ldc, row0);
+      continue;
+    }
+    if (EPI == EPI_DGELU) from_mem(g.aux, g.ldaux, row0);
+    // z = acc (+ bias) for run (j, q)
+    auto zval = [&](int j, int q, float* z) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[e] = acc[i][j][4 * q + e];
+      const int n = col0 + 32 * j + 8 * q + 4 * hh;
+      if ((EPI == EPI_STORE || EPI == EPI_BIAS_GELU) && g.bias != nullptr && n < g.N) {
+        const V4 b = *(const V4*)((const E*)g.bias + n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[e] += (float)b[e];
+      }
+    };
+    if (EPI == EPI_BIAS_GELU && g.C2 != nullptr) {
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float z[4];
+          zval(j, q, z);
+          V4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (E)z[e];
+          *(V4*)at(j, q) = o;
+        }
+      to_mem(g.C2, g.ldc2, row0);
+    }
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float z[4];
+        zval(j, q, z);
+        if (EPI == EPI_DGELU) {
+          const V4 zz = *(const V4*)at(j, q);   // the saved pre-activation, staged above
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[e] *= gelu_grad_f((float)zz[e]);
+        }
+        V4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (E)(EPI == EPI_BIAS_GELU ? gelu_f(z[e]) : z[e]);
+        *(V4*)at(j, q) = o;
+      }
+    to_mem(g.C, g.ldc, row0);
   }
 }
 
@@ -482,7 +546,8 @@ gemm_kernel(GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no copy into this workgroup's LDS outlives it
   }
 
-  epilogue<C, EPI, E>(g, acc, m0, n0, wave, lane);
+  __syncthreads();  // every consumer is done with the ring (producer copies have drained)
+  epilogue<C, EPI, E>(g, acc, m0, n0, wave, lane, smem);
 }
 
 // Tile menu: split kernels (8 consumer + 4 producer waves) and shared kernels
