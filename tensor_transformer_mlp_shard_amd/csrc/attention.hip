@@ -157,16 +157,25 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(FwdArgs a) {
     const char* Ks = smem[buf][0];
     const char* Vs = smem[buf][1];
 
-    // S^T[key][query] for keys 32t + (0..31) of the block.
+    // S^T[key][query] for keys 32t + (0..31) of the block; the operands of
+    // slice s + 1 are read while the MFMAs of slice s run.
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    auto kfrag = [&](int s, int t) {
+      const int kr = 32 * t + l32;
+      return *(const bf16x8*)(Ks + kr * SH::ROW_BYTES + kv_slot<D>(2 * s + hh, kr) * 16);
+    };
+    bf16x8 kf[2][2];
+    kf[0][0] = kfrag(0, 0);
+    kf[0][1] = kfrag(0, 1);
 #pragma unroll
-    for (int s = 0; s < SH::KS; ++s)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int kr = 32 * t + l32;
-        const bf16x8 kf = *(const bf16x8*)(Ks + kr * SH::ROW_BYTES + kv_slot<D>(2 * s + hh, kr) * 16);
-        sacc[t] = mfma(kf, qf[s], sacc[t]);
+    for (int s = 0; s < SH::KS; ++s) {
+      if (s + 1 < SH::KS) {
+        kf[(s + 1) & 1][0] = kfrag(s + 1, 0);
+        kf[(s + 1) & 1][1] = kfrag(s + 1, 1);
       }
+      sacc[0] = mfma(kf[s & 1][0], qf[s], sacc[0]);
+      sacc[1] = mfma(kf[s & 1][1], qf[s], sacc[1]);
+    }
 
     // Mask, block maximum of this lane's query (on the raw scores: the scale is
     // positive), then p = 2^(s * log2(e)/sqrt(D) - m) as one FMA and an exp2.
@@ -215,19 +224,27 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) pf[s][m] = (bf16)sacc[s >> 1][8 * (s & 1) + m];
 
-    // O^T[d][query] += V^T P^T; V^T read with the same key order.
+    // O^T[d][query] += V^T P^T; V^T read with the same key order, one operand
+    // ahead of the MFMA that uses it.
+    auto vfrag = [&](int s, int t) {
+      const int col = 32 * t + tr_c;
+      const int ra = 16 * s + tr_r, rb = ra + 8;
+      const bf16x4 lo = read_tr(Vs + ra * SH::ROW_BYTES + kv_slot<D>(col >> 3, ra) * 16 + (col & 7) * 2);
+      const bf16x4 hi = read_tr(Vs + rb * SH::ROW_BYTES + kv_slot<D>(col >> 3, rb) * 16 + (col & 7) * 2);
+      bf16x8 v;
+      v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+      v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+      return v;
+    };
+    bf16x8 vf[2];
+    vf[0] = vfrag(0, 0);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int t = 0; t < SH::DT; ++t) {
-        const int col = 32 * t + tr_c;
-        const int ra = 16 * s + tr_r, rb = ra + 8;
-        const bf16x4 lo = read_tr(Vs + ra * SH::ROW_BYTES + kv_slot<D>(col >> 3, ra) * 16 + (col & 7) * 2);
-        const bf16x4 hi = read_tr(Vs + rb * SH::ROW_BYTES + kv_slot<D>(col >> 3, rb) * 16 + (col & 7) * 2);
-        bf16x8 vf;
-        vf[0] = lo[0]; vf[1] = lo[1]; vf[2] = lo[2]; vf[3] = lo[3];
-        vf[4] = hi[0]; vf[5] = hi[1]; vf[6] = hi[2]; vf[7] = hi[3];
-        oacc[t] = mfma(vf, pf[s], oacc[t]);
+        const int n = s * SH::DT + t;
+        if (n + 1 < 4 * SH::DT) vf[(n + 1) & 1] = vfrag((n + 1) / SH::DT, (n + 1) % SH::DT);
+        oacc[t] = mfma(vf[n & 1], pf[s], oacc[t]);
       }
 
     if (j + 1 < nkb) store_block(buf ^ 1);
