@@ -116,12 +116,16 @@ __device__ __forceinline__ unsigned lds_address(const void* p) {
   return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
 }
 
+// A voffset at or beyond every record range: the lane reads zeros.
+constexpr int OOB = 0x7ffffff0;
+
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
   const uint64_t a = (uint64_t)base;
-  // The record count is capped at 1 GiB: every in-range offset of one K step is
-  // below that (feature dimensions are at most 2^21), and the OOB offset above it
-  // then always fails the range check, dword by dword.
-  const int64_t n = bytes < 0 ? 0 : (bytes > 0x40000000 ? 0x40000000 : bytes);
+  // The record count is capped at OOB, so an OOB offset always fails the range
+  // check, dword by dword.  Every in-range offset of one K step stays below the
+  // cap: the largest is row 383 of a 384-row panel whose rows are 2^21 elements
+  // (the feature-dimension limit) apart, 383 * 2^22 + 1008 bytes < 2^31 - 16.
+  const int64_t n = bytes < 0 ? 0 : (bytes > OOB ? OOB : bytes);
   i32x4 r;
   r[0] = __builtin_amdgcn_readfirstlane((int)(a & 0xffffffffu));
   r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff));
@@ -129,8 +133,6 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
   r[3] = 0x00020000;
   return r;
 }
-
-constexpr int OOB = 0x7ffffff0;  // a voffset beyond every record range: the lane reads zeros
 
 template <int COLS>
 __device__ __forceinline__ int mn_swz(int r) {

@@ -16,7 +16,7 @@ from dataclasses import dataclass, field
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "seeded", "randn", "mlp_inputs", "attn_inputs", "core_attn_inputs",
-           "sp_edge_inputs", "inputs_for"]
+           "sp_edge_inputs", "device_randn", "inputs_for"]
 
 
 @dataclass(frozen=True)
@@ -99,6 +99,18 @@ def randn(gen: torch.Generator, shape, sigma: float, dtype: str) -> torch.Tensor
     if sigma != 1.0:
         t.mul_(sigma)
     return t.to(_TORCH_DTYPE[dtype]).contiguous()
+
+
+def device_randn(shape, sigma: float, dtype: str, seed: int, device) -> torch.Tensor:
+    """Seeded N(0, sigma^2) draw made on the device (for inputs too large to
+    draw on the host), rounded to ``dtype``.  The same seed and shape give the
+    same bits on the same device type."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    t = torch.randn(*shape, generator=g, dtype=torch.float32, device=device)
+    if sigma != 1.0:
+        t.mul_(sigma)
+    return t.to(_TORCH_DTYPE[dtype])
 
 
 def mlp_inputs(T: int, h: int, F: int, tp: int, dtype: str, sigma_w: float, seed: int,
