@@ -16,8 +16,9 @@ Prints one JSON line.  Extra fields: per-part times, a roofline entry for the
 kernel with the most time in the step (timed with HIP events around its
 launches by the library's trace), the register-only matrix-core probe, the
 fp64 CPU oracle timed on a bounded sample of the same workload, and, outside
-the step, core attention on the rank's local heads (175B shape: 4 sequences of
-2048 tokens, 12 heads of 128, causal) forward and backward, the selective
+the step, the same step in fp16, core attention on the rank's local heads (175B
+shape: 4 sequences of 2048 tokens, 12 heads of 128, causal) forward and
+backward, the selective
 recompute forms of the MLP backward, and the sequence-parallel edge steps
 (LayerNorm, bias + dropout + residual) in GB/s.
 """
@@ -52,7 +53,9 @@ def _flops_attn(T, h, q, k):
 class Shard:
     """Device-resident inputs, outputs and workspaces of the two parts."""
 
-    def __init__(self, device):
+    def __init__(self, device, dtype: str = "bf16"):
+        import dataclasses
+
         import torch
 
         import tensor_transformer_mlp_shard_amd as tps
@@ -60,8 +63,8 @@ class Shard:
 
         self.tps = tps
         self.torch = torch
-        wm = synth.WORKLOADS["gpt175b_mlp_tp8"]
-        wa = synth.WORKLOADS["gpt175b_attn_tp8"]
+        wm = dataclasses.replace(synth.WORKLOADS["gpt175b_mlp_tp8"], dtype=dtype)
+        wa = dataclasses.replace(synth.WORKLOADS["gpt175b_attn_tp8"], dtype=dtype)
         self.wm, self.wa = wm, wa
         m = synth.inputs_for(wm)
         a = synth.inputs_for(wa)
@@ -71,7 +74,7 @@ class Shard:
         self.Xa, self.Wq, self.bq, self.O, self.Wo, self.dQ, self.dYa = (
             d(a[k]) for k in ("X", "W_qkv", "b_qkv", "O", "W_o", "dQKV", "dY"))
         T, h, f, p = wm.T, wm.h, wm.f, wm.tp
-        bf, fp = torch.bfloat16, torch.float32
+        bf, fp = {"bf16": torch.bfloat16, "fp16": torch.float16}[dtype], torch.float32
         e = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)  # noqa: E731
         self.fwd_out = {"Z": e((T, f), bf), "H": e((T, f), bf), "Y": e((T, h), bf)}
         self.bwd_out = {"dX": e((T, h), bf), "dA": e((h, f), fp), "dB": e((f, h), fp), "db1": e((f,), fp),
@@ -424,6 +427,11 @@ def main():
         "kernels": kern,
     }
     if args.part == "all" and not args.no_extras:
+        sh16 = Shard(device, "fp16")
+        ms16, _ = time_steps(torch, sh16.step, min(args.steps, 50), min(args.warmup, 10))
+        out["fp16_step"] = {"ms": round(ms16, 4), "tflops": round(flops / (ms16 * 1e-3) / 1e12, 2),
+                            "note": "the same step with IEEE-half storage (fp16 matrix-core instruction)"}
+        del sh16
         out["sp_edge"] = measure_sp_edge(torch, device, min(args.steps, 50), min(args.warmup, 10))
         out["selective_recompute"] = measure_recompute(torch, shard, min(args.steps, 50), min(args.warmup, 10))
         out["core_attention"] = measure_core_attention(torch, device, min(args.steps, 50), min(args.warmup, 10))
