@@ -28,12 +28,18 @@ COMMON = [
     "-Wno-unused-command-line-argument",
 ]
 
+# Per-source extra flags.  The attention backward needs more than 256 registers
+# per lane; left to its heuristic the compiler then parks the MFMA accumulators
+# in AGPRs and copies them back and forth around every block (hundreds of
+# v_accvgpr moves per block), so the VGPR form of the MFMA is forced there.
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 SOURCES = ["gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip", "attention.hip", "sp_edge.hip", "probe.hip", "api.cpp"]
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -6,7 +6,8 @@
 //
 // Forward kernel.  A workgroup owns 128 queries of one (sequence, head); each
 // of its 4 waves owns 32 of them.  Keys and values stream through LDS in blocks
-// of 64 (double-buffered, loaded through registers).  Per block a wave computes
+// of 64, double-buffered and copied HBM -> LDS directly (buffer loads with the
+// LDS flag; no register staging).  Per block a wave computes
 // the transposed scores S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so that
 // each lane holds 32 scores of ONE query (its column) and the softmax
 // statistics (running max m, running sum l) are per-lane scalars; the two lanes
@@ -20,6 +21,9 @@
 #include "attention.h"
 
 #include <cmath>
+#include <type_traits>
+
+#include "lds_dma.h"
 
 namespace tps {
 namespace {
@@ -60,6 +64,11 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The value held by lane ^ 32 (xhalf = (lane ^ 32) * 4).
+__device__ __forceinline__ float other_half(float v, int xhalf) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(xhalf, __float_as_int(v)));
+}
+
 // 4 consecutive bf16 of rows r0..r0+3, transposed: lane (16-lane group g, index
 // i) supplies the address of row r0 + i/4, column c0 + 4 (i % 4); it receives
 // column c0 + i of the 4 rows.
@@ -88,11 +97,65 @@ __device__ __forceinline__ void fwd_coords(const FwdArgs& a, int& qb, int& b, in
   h = r % a.Hl;
 }
 
+// Per-lane LDS byte offsets of one wave's operand reads inside a K (or V)
+// block.  The swizzle depends only on the low four bits of a row, which the
+// row steps of the loops (32 keys for K, 16 keys for V) leave unchanged, so the
+// steps, the buffer and the K/V half are compile-time offsets on top of these.
+template <int D>
+struct KvReadOffsets {
+  int k[Shape<D>::KS];                       // K rows l32 (+ 32 t), 16-wide d slice s
+  int va[Shape<D>::DT], vb[Shape<D>::DT];    // V transposing reads, d tile t: rows tr_r, tr_r + 8 (+ 16 s)
+  __device__ __forceinline__ void init(int l32, int hh, int tr_r, int tr_c) {
+#pragma unroll
+    for (int s = 0; s < Shape<D>::KS; ++s) k[s] = l32 * Shape<D>::ROW_BYTES + kv_slot<D>(2 * s + hh, l32) * 16;
+#pragma unroll
+    for (int t = 0; t < Shape<D>::DT; ++t) {
+      const int col = 32 * t + tr_c;
+      va[t] = tr_r * Shape<D>::ROW_BYTES + kv_slot<D>(col >> 3, tr_r) * 16 + (col & 7) * 2;
+      vb[t] = (tr_r + 8) * Shape<D>::ROW_BYTES + kv_slot<D>(col >> 3, tr_r + 8) * 16 + (col & 7) * 2;
+    }
+  }
+};
+
+// Copies of 64-row blocks of a [rows x D] slice (row stride ld elements)
+// straight into LDS in the kv_slot layout: each wave moves NI KiB of a block,
+// lane i of copy c landing at byte 1024 (wave NI + c) + 16 i, which is chunk
+// slot s of row r; it fetches the chunk that the swizzle puts there.  Rows at
+// or past `rows_left` read as zero through the buffer range check.
+template <int D>
+struct BlockCopier {
+  static constexpr int NI = Shape<D>::BLOCK_BYTES / 1024 / AW;
+  int off[NI];
+  __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int q = (wave * NI + i) * 64 + lane;
+      const int r = q / Shape<D>::CH, sl = q % Shape<D>::CH;
+      off[i] = r * (int)(ld * 2) + kv_slot<D>(sl, r) * 16;
+    }
+  }
+  // Block starting at `first` (row 0 of the copy); `rows_left` rows from there are data.
+  __device__ __forceinline__ void issue(const bf16* first, int64_t ld, int rows_left, unsigned lds, int wave) const {
+    const i32x4 rs = make_rsrc(first, rows_left > 0 ? ((int64_t)(rows_left - 1) * ld + D) * 2 : 0);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) lds_dma16(rs, off[i], lds + (wave * NI + i) * 1024);
+  }
+};
+
+// Lazy rescaling: a lane's reference maximum m moves only when a block's
+// maximum exceeds it by more than this many powers of two, so probabilities
+// are at most 2^8 (exact in fp32, and bf16 keeps fp32's exponent range) and the
+// O accumulators are rescaled only on the rare blocks where m moves.
+constexpr float RESCALE_LOG2 = 8.0f;
+
 template <int D>
 __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(FwdArgs a) {
   using SH = Shape<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2][2][SH::BLOCK_BYTES];  // [buffer][K, V]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int BUF = 2 * SH::BLOCK_BYTES;  // one buffer: a K block, then a V block
+  constexpr int EPS = 32 / SH::KS;           // score elements converted per 16-wide d slice
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   int qb, b, h;
   fwd_coords(a, qb, b, h);
@@ -107,6 +170,24 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(FwdArgs a) {
   const bool qvalid = qi < a.S;
   const int kend = a.causal ? min(a.S, q0 + BQ) : a.S;
   const int nkb = (kend + BKEYS - 1) / BKEYS;
+  // Keys at or past `lim` are masked for this lane's query.
+  const int lim = a.causal ? min(a.S, qi + 1) : a.S;
+  const int xhalf = (lane ^ 32) << 2;      // ds_bpermute address of the lane sharing this query
+
+  BlockCopier<D> cp;
+  cp.init(ld, wave, lane);
+  const unsigned lds0 = lds_address(smem);
+  auto issue_k = [&](int j, int buf) {
+    cp.issue(kbase + (int64_t)j * BKEYS * ld, ld, a.S - j * BKEYS, lds0 + buf * BUF, wave);
+  };
+  auto issue_v = [&](int j, int buf) {
+    cp.issue(vbase + (int64_t)j * BKEYS * ld, ld, a.S - j * BKEYS, lds0 + buf * BUF + SH::BLOCK_BYTES, wave);
+  };
+  // K runs one block ahead of V: block j's K is in buffer j % 2 until its
+  // scores are computed (during block j - 1), its V until block j is done.
+  issue_k(0, 0);
+  issue_v(0, 0);
+  if (nkb > 1) issue_k(1, 1);
 
   // Q operand (k = d, column = query), resident for the whole key loop.
   bf16x8 qf[SH::KS];
@@ -114,123 +195,123 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(FwdArgs a) {
   for (int s = 0; s < SH::KS; ++s)
     qf[s] = qvalid ? *(const bf16x8*)(qbase + (int64_t)qi * ld + 16 * s + 8 * hh) : bf16x8{};
 
-  bf16x8 stage[SH::LOADS];
-  auto load_block = [&](int j) {
-    const int k0 = j * BKEYS;
-#pragma unroll
-    for (int i = 0; i < SH::LOADS; ++i) {
-      const int c = tid + NT * (i % (SH::LOADS / 2));
-      const int r = c / SH::CH, ch = c % SH::CH;
-      const bf16* src = (i < SH::LOADS / 2 ? kbase : vbase) + (int64_t)(k0 + r) * ld + ch * 8;
-      stage[i] = (k0 + r < a.S) ? *(const bf16x8*)src : bf16x8{};
-    }
-  };
-  auto store_block = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < SH::LOADS; ++i) {
-      const int c = tid + NT * (i % (SH::LOADS / 2));
-      const int r = c / SH::CH, ch = c % SH::CH;
-      if (i < SH::LOADS / 2)
-        *(bf16x8*)(&smem[buf][0][r * SH::ROW_BYTES + kv_slot<D>(ch, r) * 16]) = stage[i];
-      else
-        *(bf16x8*)(&smem[buf][1][r * SH::ROW_BYTES + kv_slot<D>(ch, r) * 16]) = stage[i];
-    }
-  };
-
   // Transposing-read coordinates of this lane (16-lane group g = lane / 16:
   // lane half g / 2, column half g % 2).
   const int g16 = lane >> 4, i16 = lane & 15;
-  const int tr_r = 4 * (g16 >> 1) + (i16 >> 2);       // + 16 s (+ 8 for the second read)
-  const int tr_c = 16 * (g16 & 1) + 4 * (i16 & 3);     // + 32 dt
+  KvReadOffsets<D> ro;
+  ro.init(l32, hh, 4 * (g16 >> 1) + (i16 >> 2), 16 * (g16 & 1) + 4 * (i16 & 3));
 
   f32x16 oacc[SH::DT];
 #pragma unroll
   for (int t = 0; t < SH::DT; ++t) oacc[t] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_ref = -INFINITY, l_run = 0.0f;
 
-  load_block(0);
-  store_block(0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
-  for (int j = 0; j < nkb; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < nkb) load_block(j + 1);
-    const char* Ks = smem[buf][0];
-    const char* Vs = smem[buf][1];
 
-    // S^T[key][query] for keys 32t + (0..31) of the block; the operands of
-    // slice s + 1 are read while the MFMAs of slice s run.
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-    auto kfrag = [&](int s, int t) {
-      const int kr = 32 * t + l32;
-      return *(const bf16x8*)(Ks + kr * SH::ROW_BYTES + kv_slot<D>(2 * s + hh, kr) * 16);
-    };
+  // S^T[key][query] of one block (keys 32 t + (0..31) in sc[t]) from the K
+  // block at Ks; the operands of slice s + 1 are read while slice s runs.
+  auto kfrag = [&](const char* Ks, int s, int t) {
+    return *(const bf16x8*)(Ks + ro.k[s] + t * 32 * SH::ROW_BYTES);
+  };
+  f32x16 scA[2] = {f32x16{}, f32x16{}}, scB[2];
+  {
     bf16x8 kf[2][2];
-    kf[0][0] = kfrag(0, 0);
-    kf[0][1] = kfrag(0, 1);
+    kf[0][0] = kfrag(smem, 0, 0);
+    kf[0][1] = kfrag(smem, 0, 1);
 #pragma unroll
     for (int s = 0; s < SH::KS; ++s) {
       if (s + 1 < SH::KS) {
-        kf[(s + 1) & 1][0] = kfrag(s + 1, 0);
-        kf[(s + 1) & 1][1] = kfrag(s + 1, 1);
+        kf[(s + 1) & 1][0] = kfrag(smem, s + 1, 0);
+        kf[(s + 1) & 1][1] = kfrag(smem, s + 1, 1);
       }
-      sacc[0] = mfma(kf[s & 1][0], qf[s], sacc[0]);
-      sacc[1] = mfma(kf[s & 1][1], qf[s], sacc[1]);
+      scA[0] = mfma(kf[s & 1][0], qf[s], scA[0]);
+      scA[1] = mfma(kf[s & 1][1], qf[s], scA[1]);
     }
+  }
+  __syncthreads();  // block 0's K buffer is free for block 2
 
-    // Mask, block maximum of this lane's query (on the raw scores: the scale is
-    // positive), then p = 2^(s * log2(e)/sqrt(D) - m) as one FMA and an exp2.
+  // Key block j (BI = j % 2, a constant, so every LDS address is a per-lane
+  // base plus an immediate): its scores are in sc; the next block's scores are
+  // computed into sn while this block's probabilities are formed, so the
+  // matrix cores and the vector ALU work side by side.
+  auto block = [&](int j, auto bic, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    constexpr int BI = decltype(bic)::value;
     const int k0 = j * BKEYS;
-    const bool masked = (k0 + BKEYS > a.S) || (a.causal && k0 + BKEYS - 1 > wq0);
+    // Mask (only blocks that reach past the sequence end or this wave's first
+    // query) and this lane's block maximum on the raw scores (the scale is positive).
+    if ((k0 + BKEYS > a.S) || (a.causal && k0 + BKEYS - 1 > wq0)) {
+      const int x = lim - k0 - 4 * hh;  // accumulator element (t, v) is key k0 + 4 hh + c(t, v)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int c = 32 * t + 8 * (v >> 2) + (v & 3);
+          sc[t][v] = c >= x ? -INFINITY : sc[t][v];
+        }
+    }
     float mloc = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        if (masked) {
-          const int key = k0 + 32 * t + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (key >= a.S || (a.causal && key > qi)) sacc[t][v] = -INFINITY;
-        }
-        mloc = fmaxf(mloc, sacc[t][v]);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc * a.scale_log2);   // finite: key 0 is allowed for every query
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float psum = 0.0f;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[t][v], a.scale_log2, -m_new));
-        sacc[t][v] = p;
-        psum += p;
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // The running maximum rarely moves after the first blocks: rescale O only
-    // when it moved for some lane of the wave.
-    if (__ballot(alpha != 1.0f) != 0) {
+      for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, sc[t][v]);
+    mloc = fmaxf(mloc, other_half(mloc, xhalf));
+    const float mblk = mloc * a.scale_log2;  // finite on block 0: key 0 is allowed for every query
+    if (__ballot(mblk > m_ref + RESCALE_LOG2) != 0) {
+      const float m_new = mblk > m_ref + RESCALE_LOG2 ? mblk : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_run *= alpha;
 #pragma unroll
       for (int t = 0; t < SH::DT; ++t)
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[t][v] *= alpha;
+      m_ref = m_new;
     }
 
-    // P^T as the B operand of 16-key slice s: k slot m of lane half hh is key
-    // 16 s + 8 (m / 4) + 4 hh + m % 4, i.e. accumulator element 8 (s % 2) + m
-    // of score tile s / 2.
+    // Copies: block j + 2's K into this K buffer (its scores were computed
+    // before the last barrier), block j + 1's V into the other V buffer.
+    if (j + 2 < nkb) issue_k(j + 2, BI);
+    if (j + 1 < nkb) issue_v(j + 1, BI ^ 1);
+
+    // Block j + 1's scores (garbage past the last block, then unused), slice
+    // by slice, each slice followed by its share of block j's probabilities
+    // p = 2^(s * log2(e)/sqrt(D) - m) (one FMA and an exp2), packed to bf16 as
+    // the B operand of O^T += V^T P^T: k slot m of 16-key slice q and lane half
+    // hh is key 16 q + 8 (m / 4) + 4 hh + m % 4, i.e. score element 8 q + m.
+    const char* Kn = smem + (BI ^ 1) * BUF;
+    const char* Vs = smem + BI * BUF + SH::BLOCK_BYTES;
+    sn[0] = f32x16{};
+    sn[1] = f32x16{};
     bf16x8 pf[4];
+    float ps0 = 0.0f, ps1 = 0.0f;
+    bf16x8 kf[2][2];
+    kf[0][0] = kfrag(Kn, 0, 0);
+    kf[0][1] = kfrag(Kn, 0, 1);
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < SH::KS; ++s) {
+      if (s + 1 < SH::KS) {
+        kf[(s + 1) & 1][0] = kfrag(Kn, s + 1, 0);
+        kf[(s + 1) & 1][1] = kfrag(Kn, s + 1, 1);
+      }
+      sn[0] = mfma(kf[s & 1][0], qf[s], sn[0]);
+      sn[1] = mfma(kf[s & 1][1], qf[s], sn[1]);
 #pragma unroll
-      for (int m = 0; m < 8; ++m) pf[s][m] = (bf16)sacc[s >> 1][8 * (s & 1) + m];
+      for (int e = EPS * s; e < EPS * (s + 1); e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e >> 4][e & 15], a.scale_log2, -m_ref));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e >> 4][(e + 1) & 15], a.scale_log2, -m_ref));
+        pf[e >> 3][e & 7] = (bf16)p0;
+        pf[e >> 3][(e + 1) & 7] = (bf16)p1;
+        ps0 += p0;
+        ps1 += p1;
+      }
+    }
+    l_run += ps0 + ps1;
 
     // O^T[d][query] += V^T P^T; V^T read with the same key order, one operand
     // ahead of the MFMA that uses it.
     auto vfrag = [&](int s, int t) {
-      const int col = 32 * t + tr_c;
-      const int ra = 16 * s + tr_r, rb = ra + 8;
-      const bf16x4 lo = read_tr(Vs + ra * SH::ROW_BYTES + kv_slot<D>(col >> 3, ra) * 16 + (col & 7) * 2);
-      const bf16x4 hi = read_tr(Vs + rb * SH::ROW_BYTES + kv_slot<D>(col >> 3, rb) * 16 + (col & 7) * 2);
+      const bf16x4 lo = read_tr(Vs + ro.va[t] + 16 * s * SH::ROW_BYTES);
+      const bf16x4 hi = read_tr(Vs + ro.vb[t] + 16 * s * SH::ROW_BYTES);
       bf16x8 v;
       v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
       v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
@@ -247,11 +328,17 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(FwdArgs a) {
         oacc[t] = mfma(vf[n & 1], pf[s], oacc[t]);
       }
 
-    if (j + 1 < nkb) store_block(buf ^ 1);
+    // This wave's copies have landed and every wave is done with the buffers
+    // the next block's copies overwrite.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
+  };
+  for (int j = 0; j < nkb; j += 2) {
+    block(j, std::integral_constant<int, 0>{}, scA, scB);
+    if (j + 1 < nkb) block(j + 1, std::integral_constant<int, 1>{}, scB, scA);
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = l_run + other_half(l_run, xhalf);
   if (qvalid) {
     const float inv = 1.0f / l_tot;
     bf16* orow = a.o + (row0 + qi) * (int64_t)a.Hl * D + (int64_t)h * D;
@@ -265,7 +352,7 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(FwdArgs a) {
         *(bf16x4*)(orow + 32 * t + 8 * g + 4 * hh) = o4;
       }
     if (a.lse != nullptr && hh == 0)
-      a.lse[(int64_t)h * a.T + row0 + qi] = (m_run + __log2f(l_tot)) * 0.6931471805599453f;
+      a.lse[(int64_t)h * a.T + row0 + qi] = (m_ref + __log2f(l_tot)) * 0.6931471805599453f;
   }
 }
 
@@ -277,14 +364,14 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(FwdArgs a) {
 // Three kernels, no atomics (bitwise reproducible):
 //  * attn_bwd_dot: Dt for every (token, head);
 //  * attn_bwd_dkdv: a workgroup owns 128 keys (32 per wave, one per lane
-//    column); K and V of its keys stay in registers; queries stream through
-//    LDS in blocks of 64.  Scores are computed as S[query][key] so each lane
+//    column); K and V of its keys stay in registers; queries (Q and dO rows)
+//    are copied HBM -> LDS directly in double-buffered blocks of 64.  Scores are computed as S[query][key] so each lane
 //    holds one key's column, and P and dS feed dV^T += dO^T P and
 //    dK^T += Q^T dS from registers (queries in the accumulator order, dO^T and
 //    Q^T read from LDS with transposing reads in that order);
 //  * attn_bwd_dq: a workgroup owns 128 queries (32 per wave, one per lane
-//    column) as in the forward; keys and values stream through LDS in blocks
-//    of 64; S^T and dP^T = V dO^T give dS^T, which feeds dQ^T += K^T dS^T.
+//    column) as in the forward; keys and values are copied HBM -> LDS directly
+//    in double-buffered blocks of 64; S^T and dP^T = V dO^T give dS^T, which feeds dQ^T += K^T dS^T.
 
 struct BwdArgs {
   const bf16* qkv;
@@ -323,60 +410,15 @@ __global__ void __launch_bounds__(NT) attn_bwd_dot_kernel(BwdArgs a) {
   }
 }
 
-// 16-byte operand of an MFMA from an LDS block: row r, 16-wide
-// slice s, lane half hh (elements 16 s + 8 hh .. + 7).
-template <int D>
-__device__ __forceinline__ bf16x8 lds_row_frag(const char* blk, int r, int s, int hh) {
-  return *(const bf16x8*)(blk + r * Shape<D>::ROW_BYTES + kv_slot<D>(2 * s + hh, r) * 16);
-}
-
-// Transposed operand from an LDS block: columns 32 t + (0..31)
-// of rows 16 s + {4 hh + 0..3, 8 + 4 hh + 0..3} (the accumulator order).
-template <int D>
-__device__ __forceinline__ bf16x8 lds_tr_frag(const char* blk, int t, int s, int tr_r, int tr_c) {
-  const int col = 32 * t + tr_c;
-  const int ra = 16 * s + tr_r, rb = ra + 8;
-  const bf16x4 lo = read_tr(blk + ra * Shape<D>::ROW_BYTES + kv_slot<D>(col >> 3, ra) * 16 + (col & 7) * 2);
-  const bf16x4 hi = read_tr(blk + rb * Shape<D>::ROW_BYTES + kv_slot<D>(col >> 3, rb) * 16 + (col & 7) * 2);
-  bf16x8 v;
-  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
-  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
-  return v;
-}
-
-// Two 64-row blocks (rows r0.. of the sequence; base / row stride of each) into
-// registers, zero past the sequence end, then into LDS (kv_slot layout).
-template <int D>
-struct PairStager {
-  static constexpr int L = Shape<D>::LOADS;  // 16-byte loads per thread (both blocks)
-  bf16x8 st[L];
-  __device__ __forceinline__ void load(const bf16* base0, int64_t ld0, const bf16* base1, int64_t ld1, int r0, int S,
-                                       int tid) {
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-      const int c = tid + NT * (i % (L / 2));
-      const int r = c / Shape<D>::CH, ch = c % Shape<D>::CH;
-      const bf16* src = i < L / 2 ? base0 + (int64_t)(r0 + r) * ld0 + ch * 8 : base1 + (int64_t)(r0 + r) * ld1 + ch * 8;
-      st[i] = (r0 + r < S) ? *(const bf16x8*)src : bf16x8{};
-    }
-  }
-  __device__ __forceinline__ void store(char* blk0, char* blk1, int tid) const {
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-      const int c = tid + NT * (i % (L / 2));
-      const int r = c / Shape<D>::CH, ch = c % Shape<D>::CH;
-      *(bf16x8*)((i < L / 2 ? blk0 : blk1) + r * Shape<D>::ROW_BYTES + kv_slot<D>(ch, r) * 16) = st[i];
-    }
-  }
-};
-
 template <int D>
 __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
   using SH = Shape<D>;
-  constexpr int QB = 64;  // queries per LDS block
-  __shared__ __attribute__((aligned(16))) char smem[2][2][SH::BLOCK_BYTES];  // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) float stat[2][2][QB];              // [buffer][lse2, Dt]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int QB = 64;                     // queries per LDS block
+  constexpr int BUF = 2 * SH::BLOCK_BYTES;   // one buffer: a Q block, then a dO block
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
+  __shared__ __attribute__((aligned(16))) float stat[2][2][QB];  // [buffer][lse * log2(e), Dt]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int bh = a.B * a.Hl;
   const int kb = (int)(blockIdx.x / bh);           // causal: low key blocks have the most queries
@@ -386,10 +428,40 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
   const bf16* qbase = a.qkv + row0 * ld + (int64_t)h * D;
   const bf16* kbase = qbase + (int64_t)a.Hl * D;
   const bf16* vbase = qbase + 2LL * a.Hl * D;
-  const bf16* dobase = a.dout + row0 * (int64_t)a.Hl * D + (int64_t)h * D;
   const int64_t ldo = (int64_t)a.Hl * D;
-  const int kj = kb * 128 + wave * 32 + l32;      // this lane's key
+  const bf16* dobase = a.dout + row0 * ldo + (int64_t)h * D;
+  const int kw0 = kb * 128 + wave * 32;           // first key of this wave
+  const int kj = kw0 + l32;                       // this lane's key
   const bool kvalid = kj < a.S;
+  const int qstart = a.causal ? kb * 128 : 0;     // earlier queries see none of these keys
+  const int nqblk = (a.S - qstart + QB - 1) / QB;
+
+  BlockCopier<D> cq, co;
+  cq.init(ld, wave, lane);
+  co.init(ldo, wave, lane);
+  const unsigned lds0 = lds_address(smem);
+  auto issue = [&](int j, int buf) {
+    const int q0 = qstart + j * QB;
+    cq.issue(qbase + (int64_t)q0 * ld, ld, a.S - q0, lds0 + buf * BUF, wave);
+    co.issue(dobase + (int64_t)q0 * ldo, ldo, a.S - q0, lds0 + buf * BUF + SH::BLOCK_BYTES, wave);
+  };
+  // The block's per-query statistics go through wave 0's registers (2 x 64 floats).
+  float st_l2 = 0.0f, st_dt = 0.0f;
+  auto load_stats = [&](int q0) {
+    if (wave == 0) {
+      const int q = q0 + lane;
+      st_l2 = q < a.S ? a.lse[(int64_t)h * a.T + row0 + q] * LOG2E : INFINITY;
+      st_dt = q < a.S ? a.dt[(int64_t)h * a.T + row0 + q] : 0.0f;
+    }
+  };
+  auto store_stats = [&](int buf) {
+    if (wave == 0) {
+      stat[buf][0][lane] = st_l2;
+      stat[buf][1][lane] = st_dt;
+    }
+  };
+  issue(0, 0);
+  load_stats(qstart);
 
   // K and V of this lane's key as the B operand (k = d) of S and dP.
   bf16x8 kf[SH::KS], vf[SH::KS];
@@ -399,33 +471,29 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
     vf[s] = kvalid ? *(const bf16x8*)(vbase + (int64_t)kj * ld + 16 * s + 8 * hh) : bf16x8{};
   }
   const int g16 = lane >> 4, i16 = lane & 15;
-  const int tr_r = 4 * (g16 >> 1) + (i16 >> 2);
-  const int tr_c = 16 * (g16 & 1) + 4 * (i16 & 3);
+  KvReadOffsets<D> ro;  // row reads of Q / dO (.k), transposing reads of dO^T / Q^T (.va, .vb)
+  ro.init(l32, hh, 4 * (g16 >> 1) + (i16 >> 2), 16 * (g16 & 1) + 4 * (i16 & 3));
 
   f32x16 dk[SH::DT], dv[SH::DT];
 #pragma unroll
   for (int t = 0; t < SH::DT; ++t) { dk[t] = f32x16{}; dv[t] = f32x16{}; }
 
-  const int qstart = a.causal ? kb * 128 : 0;      // earlier queries see none of these keys
-  const int nqblk = (a.S - qstart + QB - 1) / QB;
-  PairStager<D> stg;
-  auto load_stats = [&](int buf, int q0) {
-    if (tid < QB) {
-      const int q = q0 + tid;
-      stat[buf][0][tid] = q < a.S ? a.lse[(int64_t)h * a.T + row0 + q] * LOG2E : INFINITY;
-      stat[buf][1][tid] = q < a.S ? a.dt[(int64_t)h * a.T + row0 + q] : 0.0f;
-    }
-  };
-  stg.load(qbase, ld, dobase, ldo, qstart, a.S, tid);
-  stg.store(smem[0][0], smem[0][1], tid);
-  load_stats(0, qstart);
+  store_stats(0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
-  for (int j = 0; j < nqblk; ++j) {
-    const int buf = j & 1;
+
+  // Query block j from LDS buffer BI = j % 2 (a constant, so every LDS address
+  // is a per-lane base plus an immediate) while block j + 1 is copied into the
+  // other buffer.
+  auto block = [&](int j, auto bic) {
+    constexpr int BI = decltype(bic)::value;
     const int q0 = qstart + j * QB;
-    if (j + 1 < nqblk) stg.load(qbase, ld, dobase, ldo, q0 + QB, a.S, tid);
-    const char* Qs = smem[buf][0];
-    const char* Gs = smem[buf][1];
+    if (j + 1 < nqblk) {
+      issue(j + 1, BI ^ 1);
+      load_stats(q0 + QB);
+    }
+    const char* Qs = smem + BI * BUF;
+    const char* Gs = Qs + SH::BLOCK_BYTES;
 
     // S[query][key] and dP[query][key] for queries 32 t + (0..31) of the block.
     f32x16 sc[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
@@ -433,48 +501,63 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
     for (int s = 0; s < SH::KS; ++s)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        sc[t] = mfma(lds_row_frag<D>(Qs, 32 * t + l32, s, hh), kf[s], sc[t]);
-        dp[t] = mfma(lds_row_frag<D>(Gs, 32 * t + l32, s, hh), vf[s], dp[t]);
+        const int o = ro.k[s] + t * 32 * SH::ROW_BYTES;
+        sc[t] = mfma(*(const bf16x8*)(Qs + o), kf[s], sc[t]);
+        dp[t] = mfma(*(const bf16x8*)(Gs + o), vf[s], dp[t]);
       }
+    // Causal mask, only where some query of the block precedes one of this
+    // wave's keys: accumulator element (t, v) is query q0 + 4 hh + c(t, v).
+    if (a.causal && q0 < kw0 + 31) {
+      const int x = kj - q0 - 4 * hh;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int c = 32 * t + 8 * (v >> 2) + (v & 3);
+          sc[t][v] = c < x ? -INFINITY : sc[t][v];
+        }
+    }
     // P and dS; this lane's entries are queries 32 t + 8 g + 4 hh + e.
-    const bool masked = a.causal && q0 < kb * 128 + wave * 32 + 31;
+    bf16x8 pf[4], sf[4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int qo = 32 * t + 8 * g + 4 * hh;
-        const f32x4 l2 = *(const f32x4*)&stat[buf][0][qo];
-        const f32x4 dd = *(const f32x4*)&stat[buf][1][qo];
+        const f32x4 l2 = *(const f32x4*)&stat[BI][0][qo];
+        const f32x4 dd = *(const f32x4*)&stat[BI][1][qo];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v = 4 * g + e;
-          float p = __builtin_amdgcn_exp2f(sc[t][v] * a.scale_log2 - l2[e]);
-          if (masked && kj > q0 + qo + e) p = 0.0f;
-          sc[t][v] = p;
-          dp[t][v] = p * (dp[t][v] - dd[e]);
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][v], a.scale_log2, -l2[e]));
+          pf[2 * t + (g >> 1)][4 * (g & 1) + e] = (bf16)p;
+          sf[2 * t + (g >> 1)][4 * (g & 1) + e] = (bf16)(p * (dp[t][v] - dd[e]));
         }
-      }
-    bf16x8 pf[4], sf[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        pf[s][m] = (bf16)sc[s >> 1][8 * (s & 1) + m];
-        sf[s][m] = (bf16)dp[s >> 1][8 * (s & 1) + m];
       }
     // dV^T += dO^T P, dK^T += Q^T dS (k = the block's queries in accumulator order).
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int t = 0; t < SH::DT; ++t) {
-        dv[t] = mfma(lds_tr_frag<D>(Gs, t, s, tr_r, tr_c), pf[s], dv[t]);
-        dk[t] = mfma(lds_tr_frag<D>(Qs, t, s, tr_r, tr_c), sf[s], dk[t]);
+        const int oa = ro.va[t] + 16 * q * SH::ROW_BYTES, ob = ro.vb[t] + 16 * q * SH::ROW_BYTES;
+        bf16x8 gv, qv;
+        const bf16x4 g_lo = read_tr(Gs + oa), g_hi = read_tr(Gs + ob);
+        const bf16x4 q_lo = read_tr(Qs + oa), q_hi = read_tr(Qs + ob);
+        gv[0] = g_lo[0]; gv[1] = g_lo[1]; gv[2] = g_lo[2]; gv[3] = g_lo[3];
+        gv[4] = g_hi[0]; gv[5] = g_hi[1]; gv[6] = g_hi[2]; gv[7] = g_hi[3];
+        qv[0] = q_lo[0]; qv[1] = q_lo[1]; qv[2] = q_lo[2]; qv[3] = q_lo[3];
+        qv[4] = q_hi[0]; qv[5] = q_hi[1]; qv[6] = q_hi[2]; qv[7] = q_hi[3];
+        dv[t] = mfma(gv, pf[q], dv[t]);
+        dk[t] = mfma(qv, sf[q], dk[t]);
       }
-    if (j + 1 < nqblk) {
-      stg.store(smem[buf ^ 1][0], smem[buf ^ 1][1], tid);
-      load_stats(buf ^ 1, q0 + QB);
-    }
+    if (j + 1 < nqblk) store_stats(BI ^ 1);
+    // This wave's copies have landed and every wave is done with this buffer.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
+  };
+  for (int j = 0; j < nqblk; j += 2) {
+    block(j, std::integral_constant<int, 0>{});
+    if (j + 1 < nqblk) block(j + 1, std::integral_constant<int, 1>{});
   }
 
   if (kvalid) {
@@ -497,10 +580,12 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
 }
 
 template <int D>
-__global__ void __launch_bounds__(NT, 1) attn_bwd_dq_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(NT, 2) attn_bwd_dq_kernel(BwdArgs a) {
   using SH = Shape<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2][2][SH::BLOCK_BYTES];  // [buffer][K, V]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int BUF = 2 * SH::BLOCK_BYTES;  // one buffer: a K block, then a V block
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int bh = a.B * a.Hl;
   const int qb = a.nb - 1 - (int)(blockIdx.x / bh);  // longest causal query blocks first
@@ -518,6 +603,17 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dq_kernel(BwdArgs a) {
   const bool qvalid = qi < a.S;
   const int kend = a.causal ? min(a.S, q0 + BQ) : a.S;
   const int nkb = (kend + BKEYS - 1) / BKEYS;
+  const int lim = a.causal ? min(a.S, qi + 1) : a.S;  // keys at or past lim are masked
+
+  BlockCopier<D> cp;
+  cp.init(ld, wave, lane);
+  const unsigned lds0 = lds_address(smem);
+  auto issue = [&](int j, int buf) {
+    const int k0 = j * BKEYS;
+    cp.issue(kbase + (int64_t)k0 * ld, ld, a.S - k0, lds0 + buf * BUF, wave);
+    cp.issue(vbase + (int64_t)k0 * ld, ld, a.S - k0, lds0 + buf * BUF + SH::BLOCK_BYTES, wave);
+  };
+  issue(0, 0);
 
   // Q and dO of this lane's query as the B operand (k = d) of S^T and dP^T.
   bf16x8 qf[SH::KS], gf[SH::KS];
@@ -529,23 +625,22 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dq_kernel(BwdArgs a) {
   const float lse2 = qvalid ? a.lse[(int64_t)h * a.T + row0 + qi] * LOG2E : INFINITY;
   const float dti = qvalid ? a.dt[(int64_t)h * a.T + row0 + qi] : 0.0f;
   const int g16 = lane >> 4, i16 = lane & 15;
-  const int tr_r = 4 * (g16 >> 1) + (i16 >> 2);
-  const int tr_c = 16 * (g16 & 1) + 4 * (i16 & 3);
+  KvReadOffsets<D> ro;  // row reads of K / V (.k), transposing reads of K^T (.va, .vb)
+  ro.init(l32, hh, 4 * (g16 >> 1) + (i16 >> 2), 16 * (g16 & 1) + 4 * (i16 & 3));
 
   f32x16 dq[SH::DT];
 #pragma unroll
   for (int t = 0; t < SH::DT; ++t) dq[t] = f32x16{};
 
-  PairStager<D> stg;
-  stg.load(kbase, ld, vbase, ld, 0, a.S, tid);
-  stg.store(smem[0][0], smem[0][1], tid);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
-  for (int j = 0; j < nkb; ++j) {
-    const int buf = j & 1;
+
+  auto block = [&](int j, auto bic) {
+    constexpr int BI = decltype(bic)::value;
     const int k0 = j * BKEYS;
-    if (j + 1 < nkb) stg.load(kbase, ld, vbase, ld, k0 + BKEYS, a.S, tid);
-    const char* Ks = smem[buf][0];
-    const char* Vs = smem[buf][1];
+    if (j + 1 < nkb) issue(j + 1, BI ^ 1);
+    const char* Ks = smem + BI * BUF;
+    const char* Vs = Ks + SH::BLOCK_BYTES;
 
     // S^T[key][query] and dP^T[key][query] = (V dO^T) for keys 32 t + (0..31).
     f32x16 sc[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
@@ -553,33 +648,50 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dq_kernel(BwdArgs a) {
     for (int s = 0; s < SH::KS; ++s)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        sc[t] = mfma(lds_row_frag<D>(Ks, 32 * t + l32, s, hh), qf[s], sc[t]);
-        dp[t] = mfma(lds_row_frag<D>(Vs, 32 * t + l32, s, hh), gf[s], dp[t]);
+        const int o = ro.k[s] + t * 32 * SH::ROW_BYTES;
+        sc[t] = mfma(*(const bf16x8*)(Ks + o), qf[s], sc[t]);
+        dp[t] = mfma(*(const bf16x8*)(Vs + o), gf[s], dp[t]);
       }
-    const bool masked = (k0 + BKEYS > a.S) || (a.causal && k0 + BKEYS - 1 > wq0);
+    // Mask (only blocks that reach past the sequence end or this wave's first
+    // query): accumulator element (t, v) is key k0 + 4 hh + c(t, v).
+    if ((k0 + BKEYS > a.S) || (a.causal && k0 + BKEYS - 1 > wq0)) {
+      const int x = lim - k0 - 4 * hh;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int c = 32 * t + 8 * (v >> 2) + (v & 3);
+          sc[t][v] = c >= x ? -INFINITY : sc[t][v];
+        }
+    }
+    // dS^T = P^T * (dP^T - Dt) as the B operand of 16-key slice q (accumulator order).
+    bf16x8 sf[4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float p = __builtin_amdgcn_exp2f(sc[t][v] * a.scale_log2 - lse2);
-        if (masked) {
-          const int key = k0 + 32 * t + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (key >= a.S || (a.causal && key > qi)) p = 0.0f;
-        }
-        dp[t][v] = p * (dp[t][v] - dti);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][v], a.scale_log2, -lse2));
+        sf[2 * t + (v >> 3)][v & 7] = (bf16)(p * (dp[t][v] - dti));
       }
-    bf16x8 sf[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int m = 0; m < 8; ++m) sf[s][m] = (bf16)dp[s >> 1][8 * (s & 1) + m];
     // dQ^T += K^T dS^T (k = the block's keys in accumulator order).
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int t = 0; t < SH::DT; ++t) dq[t] = mfma(lds_tr_frag<D>(Ks, t, s, tr_r, tr_c), sf[s], dq[t]);
-    if (j + 1 < nkb) stg.store(smem[buf ^ 1][0], smem[buf ^ 1][1], tid);
+      for (int t = 0; t < SH::DT; ++t) {
+        const bf16x4 lo = read_tr(Ks + ro.va[t] + 16 * q * SH::ROW_BYTES);
+        const bf16x4 hi = read_tr(Ks + ro.vb[t] + 16 * q * SH::ROW_BYTES);
+        bf16x8 kv;
+        kv[0] = lo[0]; kv[1] = lo[1]; kv[2] = lo[2]; kv[3] = lo[3];
+        kv[4] = hi[0]; kv[5] = hi[1]; kv[6] = hi[2]; kv[7] = hi[3];
+        dq[t] = mfma(kv, sf[q], dq[t]);
+      }
+    // This wave's copies have landed and every wave is done with this buffer.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
+  };
+  for (int j = 0; j < nkb; j += 2) {
+    block(j, std::integral_constant<int, 0>{});
+    if (j + 1 < nkb) block(j + 1, std::integral_constant<int, 1>{});
   }
 
   if (qvalid) {

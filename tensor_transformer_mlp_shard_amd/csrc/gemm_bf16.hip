@@ -40,6 +40,7 @@
 // dimensions are multiples of 8, so a 16-byte vector is entirely inside or
 // entirely outside.
 #include "gemm.h"
+#include "lds_dma.h"
 
 #include <string>
 
@@ -97,43 +98,6 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
   tn = in_group / gsize;
 }
 
-// Direct global -> LDS copy of 16 bytes per lane: buffer_load_dwordx4 ... lds.
-// Lane i's 16 bytes land at LDS byte address lds_addr + 16 i (lds_addr goes to
-// M0 and must be wave-uniform); a lane whose offset is outside the buffer's
-// record range writes zeros.  Issued as inline asm so that the compiler does not
-// order every later LDS read behind the copy (it cannot tell which LDS bytes the
-// copy writes); completion is awaited explicitly with vmcnt before the barrier
-// that publishes the stage.  M0 is not used for anything else in these kernels.
-__device__ __forceinline__ void lds_dma16(const i32x4& rsrc, int voffset, unsigned lds_addr) {
-  // One wait state between the M0 write and the LDS-DMA that reads it.
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds_addr), "v"(voffset), "s"(rsrc)
-               : "m0");
-}
-
-__device__ __forceinline__ unsigned lds_address(const void* p) {
-  return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
-}
-
-// A voffset at or beyond every record range: the lane reads zeros.
-constexpr int OOB = 0x7ffffff0;
-
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
-  const uint64_t a = (uint64_t)base;
-  // The record count is capped at OOB, so an OOB offset always fails the range
-  // check, dword by dword.  Every in-range offset of one K step stays below the
-  // cap: the largest is row 383 of a 384-row panel whose rows are 2^21 elements
-  // (the feature-dimension limit) apart, 383 * 2^22 + 1008 bytes < 2^31 - 16.
-  const int64_t n = bytes < 0 ? 0 : (bytes > OOB ? OOB : bytes);
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(a & 0xffffffffu));
-  r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff));
-  r[2] = __builtin_amdgcn_readfirstlane((int)n);
-  r[3] = 0x00020000;
-  return r;
-}
-
 template <int COLS>
 __device__ __forceinline__ int mn_swz(int r) {
   return (COLS * 2) % 256 == 0 ? 4 * (r & 3) : 2 * (r & 3);
@@ -149,9 +113,6 @@ __device__ __forceinline__ int mn_swz(int r) {
 //    2 * (r & 3) (384-byte rows already alternate bank halves).  Either stays
 //    inside the row.
 
-// s_waitcnt immediate that waits until at most n vector-memory operations are
-// outstanding (expcnt and lgkmcnt left at their maxima).
-constexpr int waitcnt_vm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
 
 // Kernel shape: tile, waves and their roles, LDS ring.
 template <int BM_, int BN_, int NPROD_, int CM_>
@@ -175,7 +136,10 @@ struct Cfg {
   static_assert((PREF - 1) * NVM <= 63, "vmcnt range");
 };
 
-// One copying wave's share of every K step's copies.
+// One copying wave's share of every K step's copies.  Every in-range offset of
+// one K step stays below the record-count cap of make_rsrc: the largest is row
+// 383 of a 384-row panel whose rows are 2^21 elements (the feature-dimension
+// limit) apart, 383 * 2^22 + 1008 bytes < 2^31 - 16.
 template <class C, bool AK, bool BKC>
 struct Copier {
   const char* a_base;
