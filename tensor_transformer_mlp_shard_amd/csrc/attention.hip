@@ -495,16 +495,38 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
     const char* Qs = smem + BI * BUF;
     const char* Gs = Qs + SH::BLOCK_BYTES;
 
-    // S[query][key] and dP[query][key] for queries 32 t + (0..31) of the block.
+    // S[query][key] and dP[query][key] for queries 32 t + (0..31) of the block;
+    // the Q and dO operands are read RD slices ahead of their MFMAs.
+    constexpr int RD = 2;
     f32x16 sc[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int s = 0; s < SH::KS; ++s)
+    bf16x8 qr[RD + 1][2], gr[RD + 1][2];
+    auto rows = [&](int s) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int o = ro.k[s] + t * 32 * SH::ROW_BYTES;
-        sc[t] = mfma(*(const bf16x8*)(Qs + o), kf[s], sc[t]);
-        dp[t] = mfma(*(const bf16x8*)(Gs + o), vf[s], dp[t]);
+        qr[s % (RD + 1)][t] = *(const bf16x8*)(Qs + o);
+        gr[s % (RD + 1)][t] = *(const bf16x8*)(Gs + o);
       }
+    };
+#pragma unroll
+    for (int s = 0; s < RD; ++s) rows(s);
+#pragma unroll
+    for (int s = 0; s < SH::KS; ++s) {
+      if (s + RD < SH::KS) rows(s + RD);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sc[t] = mfma(qr[s % (RD + 1)][t], kf[s], sc[t]);
+        dp[t] = mfma(gr[s % (RD + 1)][t], vf[s], dp[t]);
+      }
+    }
+    // Keep the operand reads RD slices ahead (the scheduler would otherwise
+    // sink each read next to its MFMA and expose the LDS latency).
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * RD, 0);
+#pragma unroll
+    for (int s = 0; s < SH::KS; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if (s + RD < SH::KS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
     // Causal mask, only where some query of the block precedes one of this
     // wave's keys: accumulator element (t, v) is query q0 + 4 hh + c(t, v).
     if (a.causal && q0 < kw0 + 31) {
@@ -517,12 +539,34 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
           sc[t][v] = c < x ? -INFINITY : sc[t][v];
         }
     }
-    // P and dS; this lane's entries are queries 32 t + 8 g + 4 hh + e.
-    bf16x8 pf[4], sf[4];
+    // Per 16-query slice q (accumulator elements 8 q .. 8 q + 7, queries
+    // 16 q + {0..3, 8..11} + 4 hh): P and dS, then dV^T += dO^T P and
+    // dK^T += Q^T dS for that slice, so the vector work of slice q + 1 runs
+    // beside the MFMAs of slice q.  dO^T and Q^T are read with transposing
+    // reads in the same query order, VPD operand pairs ahead.
+    constexpr int NOP = 4 * SH::DT, VPD = 4;
+    bf16x8 gv[VPD], qv[VPD];
+    auto tr_pair = [&](int n) {
+      const int q = n / SH::DT, t = n % SH::DT;
+      const int oa = ro.va[t] + 16 * q * SH::ROW_BYTES, ob = ro.vb[t] + 16 * q * SH::ROW_BYTES;
+      const bf16x4 g_lo = read_tr(Gs + oa), g_hi = read_tr(Gs + ob);
+      const bf16x4 q_lo = read_tr(Qs + oa), q_hi = read_tr(Qs + ob);
+      bf16x8& g = gv[n % VPD];
+      bf16x8& qq = qv[n % VPD];
+      g[0] = g_lo[0]; g[1] = g_lo[1]; g[2] = g_lo[2]; g[3] = g_lo[3];
+      g[4] = g_hi[0]; g[5] = g_hi[1]; g[6] = g_hi[2]; g[7] = g_hi[3];
+      qq[0] = q_lo[0]; qq[1] = q_lo[1]; qq[2] = q_lo[2]; qq[3] = q_lo[3];
+      qq[4] = q_hi[0]; qq[5] = q_hi[1]; qq[6] = q_hi[2]; qq[7] = q_hi[3];
+    };
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int n = 0; n < VPD; ++n) tr_pair(n);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+    for (int q = 0; q < 4; ++q) {
+      const int t = q >> 1;
+      bf16x8 pf, sf;
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const int g = 2 * (q & 1) + gg;
         const int qo = 32 * t + 8 * g + 4 * hh;
         const f32x4 l2 = *(const f32x4*)&stat[BI][0][qo];
         const f32x4 dd = *(const f32x4*)&stat[BI][1][qo];
@@ -530,26 +574,18 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int v = 4 * g + e;
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][v], a.scale_log2, -l2[e]));
-          pf[2 * t + (g >> 1)][4 * (g & 1) + e] = (bf16)p;
-          sf[2 * t + (g >> 1)][4 * (g & 1) + e] = (bf16)(p * (dp[t][v] - dd[e]));
+          pf[4 * gg + e] = (bf16)p;
+          sf[4 * gg + e] = (bf16)(p * (dp[t][v] - dd[e]));
         }
       }
-    // dV^T += dO^T P, dK^T += Q^T dS (k = the block's queries in accumulator order).
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int t = 0; t < SH::DT; ++t) {
-        const int oa = ro.va[t] + 16 * q * SH::ROW_BYTES, ob = ro.vb[t] + 16 * q * SH::ROW_BYTES;
-        bf16x8 gv, qv;
-        const bf16x4 g_lo = read_tr(Gs + oa), g_hi = read_tr(Gs + ob);
-        const bf16x4 q_lo = read_tr(Qs + oa), q_hi = read_tr(Qs + ob);
-        gv[0] = g_lo[0]; gv[1] = g_lo[1]; gv[2] = g_lo[2]; gv[3] = g_lo[3];
-        gv[4] = g_hi[0]; gv[5] = g_hi[1]; gv[6] = g_hi[2]; gv[7] = g_hi[3];
-        qv[0] = q_lo[0]; qv[1] = q_lo[1]; qv[2] = q_lo[2]; qv[3] = q_lo[3];
-        qv[4] = q_hi[0]; qv[5] = q_hi[1]; qv[6] = q_hi[2]; qv[7] = q_hi[3];
-        dv[t] = mfma(gv, pf[q], dv[t]);
-        dk[t] = mfma(qv, sf[q], dk[t]);
+      for (int d = 0; d < SH::DT; ++d) {
+        const int n = q * SH::DT + d;
+        dv[d] = mfma(gv[n % VPD], pf, dv[d]);
+        dk[d] = mfma(qv[n % VPD], sf, dk[d]);
+        if (n + VPD < NOP) tr_pair(n + VPD);
       }
+    }
     if (j + 1 < nqblk) store_stats(BI ^ 1);
     // This wave's copies have landed and every wave is done with this buffer.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -642,16 +678,36 @@ __global__ void __launch_bounds__(NT, 2) attn_bwd_dq_kernel(BwdArgs a) {
     const char* Ks = smem + BI * BUF;
     const char* Vs = Ks + SH::BLOCK_BYTES;
 
-    // S^T[key][query] and dP^T[key][query] = (V dO^T) for keys 32 t + (0..31).
+    // S^T[key][query] and dP^T[key][query] = (V dO^T) for keys 32 t + (0..31);
+    // the K and V operands are read RD slices ahead of their MFMAs.
+    constexpr int RD = 2;
     f32x16 sc[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int s = 0; s < SH::KS; ++s)
+    bf16x8 kr[RD + 1][2], vr[RD + 1][2];
+    auto rows = [&](int s) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int o = ro.k[s] + t * 32 * SH::ROW_BYTES;
-        sc[t] = mfma(*(const bf16x8*)(Ks + o), qf[s], sc[t]);
-        dp[t] = mfma(*(const bf16x8*)(Vs + o), gf[s], dp[t]);
+        kr[s % (RD + 1)][t] = *(const bf16x8*)(Ks + o);
+        vr[s % (RD + 1)][t] = *(const bf16x8*)(Vs + o);
       }
+    };
+#pragma unroll
+    for (int s = 0; s < RD; ++s) rows(s);
+#pragma unroll
+    for (int s = 0; s < SH::KS; ++s) {
+      if (s + RD < SH::KS) rows(s + RD);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sc[t] = mfma(kr[s % (RD + 1)][t], qf[s], sc[t]);
+        dp[t] = mfma(vr[s % (RD + 1)][t], gf[s], dp[t]);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * RD, 0);
+#pragma unroll
+    for (int s = 0; s < SH::KS; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if (s + RD < SH::KS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
     // Mask (only blocks that reach past the sequence end or this wave's first
     // query): accumulator element (t, v) is key k0 + 4 hh + c(t, v).
     if ((k0 + BKEYS > a.S) || (a.causal && k0 + BKEYS - 1 > wq0)) {
@@ -673,18 +729,25 @@ __global__ void __launch_bounds__(NT, 2) attn_bwd_dq_kernel(BwdArgs a) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][v], a.scale_log2, -lse2));
         sf[2 * t + (v >> 3)][v & 7] = (bf16)(p * (dp[t][v] - dti));
       }
-    // dQ^T += K^T dS^T (k = the block's keys in accumulator order).
+    // dQ^T += K^T dS^T (k = the block's keys in accumulator order), K^T read
+    // with transposing reads VPD operands ahead.
+    constexpr int NOP = 4 * SH::DT, VPD = 4;
+    bf16x8 kv[VPD];
+    auto ktr = [&](int n) {
+      const int q = n / SH::DT, t = n % SH::DT;
+      const bf16x4 lo = read_tr(Ks + ro.va[t] + 16 * q * SH::ROW_BYTES);
+      const bf16x4 hi = read_tr(Ks + ro.vb[t] + 16 * q * SH::ROW_BYTES);
+      bf16x8& v = kv[n % VPD];
+      v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+      v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+    };
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int n = 0; n < VPD; ++n) ktr(n);
 #pragma unroll
-      for (int t = 0; t < SH::DT; ++t) {
-        const bf16x4 lo = read_tr(Ks + ro.va[t] + 16 * q * SH::ROW_BYTES);
-        const bf16x4 hi = read_tr(Ks + ro.vb[t] + 16 * q * SH::ROW_BYTES);
-        bf16x8 kv;
-        kv[0] = lo[0]; kv[1] = lo[1]; kv[2] = lo[2]; kv[3] = lo[3];
-        kv[4] = hi[0]; kv[5] = hi[1]; kv[6] = hi[2]; kv[7] = hi[3];
-        dq[t] = mfma(kv, sf[q], dq[t]);
-      }
+    for (int n = 0; n < NOP; ++n) {
+      dq[n % SH::DT] = mfma(kv[n % VPD], sf[n / SH::DT], dq[n % SH::DT]);
+      if (n + VPD < NOP) ktr(n + VPD);
+    }
     // This wave's copies have landed and every wave is done with this buffer.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
