@@ -17,11 +17,15 @@
 // for tens of cycles, so a SIMD needs a second wave to keep the matrix pipe fed:
 //  * "split" kernels (tiles up to 256 x 192): 8 consumer waves (2 per SIMD) and
 //    4 producer waves that only issue the copies;
-//  * "shared" kernels (256 x 384 and 384 x 256): 8 waves, each a consumer of a
-//    128 x 96 (or 96 x 128) sub-tile that also issues 1/8 of the copies; the
-//    bigger tile moves 29% fewer bytes per FLOP from L2 and reads 31% fewer
-//    operand bytes from LDS, which matters because the chip runs at its power
-//    limit and data movement lowers the clock.
+//  * "shared" kernels (256 x 384, 384 x 256, 192 x 384): 8 waves, each a
+//    consumer of a 128 x 96 (96 x 128, 96 x 96) sub-tile; all 8 (six for
+//    192 x 384, whose 36 KiB per step do not split eight ways) also issue the
+//    copies.  The biggest tile moves 29% fewer bytes per FLOP from L2 and
+//    reads 31% fewer operand bytes from LDS than 256 x 192, which matters
+//    because the chip runs at its power limit and data movement lowers the
+//    clock; 192 x 384 sits in between and fills whole waves of 256 tiles
+//    where the others leave a partial wave (the 12288 x 4608 and 1536 x 12288
+//    weight gradients).
 //
 // Layouts.  Each operand is kept in LDS in its memory orientation:
 //  * K-contiguous panels (rows of A, or rows of B stored as [N x K]): a lane's
@@ -114,8 +118,10 @@ __device__ __forceinline__ int mn_swz(int r) {
 //    inside the row.
 
 
-// Kernel shape: tile, waves and their roles, LDS ring.
-template <int BM_, int BN_, int NPROD_, int CM_>
+// Kernel shape: tile, waves and their roles, LDS ring.  NSHCOPY_ (shared
+// kernels only): how many of the 8 waves issue the copies, when a K step's
+// 1 KiB copies do not divide evenly over all 8.
+template <int BM_, int BN_, int NPROD_, int CM_, int NSHCOPY_ = 8>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int NCONS = 8, NPROD = NPROD_, NW = NCONS + NPROD, NT = 64 * NW;
@@ -125,7 +131,7 @@ struct Cfg {
   static constexpr int A_BYTES = BM * KT * 2, B_BYTES = BN * KT * 2, STAGE = A_BYTES + B_BYTES;
   static constexpr int NSTAGE = (163840 / STAGE) < 5 ? (163840 / STAGE) : 5;  // <= 160 KiB of LDS
   static constexpr int PREF = NSTAGE - 1;       // K steps in flight ahead of the one computed
-  static constexpr int NCOPY = NPROD > 0 ? NPROD : NCONS;  // waves that issue the copies
+  static constexpr int NCOPY = NPROD > 0 ? NPROD : NSHCOPY_;  // waves that issue the copies
   static constexpr int A_INS = A_BYTES / 1024 / NCOPY, B_INS = B_BYTES / 1024 / NCOPY;
   static constexpr int NVM = A_INS + B_INS;    // 1 KiB copies per copying wave per step
   static constexpr int WAVES_PER_EU = (NW + 3) / 4;
@@ -472,15 +478,20 @@ gemm_kernel(GemmArgs g) {
         for (int j = 0; j < FN; ++j) mfma(fa[LB], fb[LB], i, j);
     }
   } else {
-    // Every wave also issues 1/8 of the copies, spread over the MFMAs that
-    // precede each step's barrier (the other wave on the SIMD keeps the matrix
-    // pipe busy while a copy holds this one up).
+    // The copying waves (all 8, or the first NCOPY) also issue their share of
+    // the copies, spread over the MFMAs that precede each step's barrier (the
+    // other wave on the SIMD keeps the matrix pipe busy while a copy holds this
+    // one up).  A wave that issues none waits on an empty vmcnt.
+    constexpr bool ALL_COPY = C::NCOPY == C::NCONS;
+    const bool copier = ALL_COPY || wave < C::NCOPY;
     Copier<C, AK, BKC> cp;
     cp.init(g, m0, n0, wave, lane, smem);
+    if (copier) {
 #pragma unroll
-    for (int p = 0; p < PREF; ++p)
+      for (int p = 0; p < PREF; ++p)
 #pragma unroll
-      for (int u = 0; u < NVM; ++u) cp.issue(p, u);
+        for (int u = 0; u < NVM; ++u) cp.issue(p, u);
+    }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step 0 landed
     __syncthreads();
     constexpr int PRE_MF = FM * FN * (NS - 1) + FM_HALF * FN;   // MFMAs before the barrier
@@ -499,7 +510,10 @@ gemm_kernel(GemmArgs g) {
             const int t = s * FM * FN + i * FN + j;
 #pragma unroll
             for (int u = 0; u < NVM; ++u)
-              if ((u * PRE_MF) / NVM == t) cp.issue(kt + PREF, u);
+              if ((u * PRE_MF) / NVM == t) {
+                if constexpr (ALL_COPY) cp.issue(kt + PREF, u);
+                else if (copier) cp.issue(kt + PREF, u);
+              }
           }
       }
       __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step kt+1 landed
@@ -525,6 +539,7 @@ using T128x256 = Cfg<128, 256, 4, 2>;
 using T128x128 = Cfg<128, 128, 4, 2>;
 using T256x384 = Cfg<256, 384, 0, 2>;
 using T384x256 = Cfg<384, 256, 0, 4>;
+using T192x384 = Cfg<192, 384, 0, 2, 6>;  // 36 KiB per K step: 6 copying waves x 6 copies
 
 template <class C, bool AK, bool BKC, int EPI, typename E>
 const char* kname() {
@@ -567,7 +582,7 @@ struct TileChoice { int bm, bn; };
 
 TileChoice choose_tile(int M, int N) {
   static const struct { int bm, bn; double eff; } cand[] = {
-      {256, 384, 1.12}, {384, 256, 1.12}, {256, 192, 1.00}, {192, 256, 1.00},
+      {256, 384, 1.12}, {384, 256, 1.12}, {192, 384, 1.06}, {256, 192, 1.00}, {192, 256, 1.00},
       {256, 128, 0.92}, {128, 256, 0.92}, {128, 128, 0.75}};
   double best = 1e300;
   TileChoice pick = {256, 192};
@@ -585,6 +600,7 @@ hipError_t launch_shape(const GemmArgs& g, hipStream_t s, const char** name) {
   const TileChoice t = choose_tile(g.M, g.N);
   if (t.bm == 256 && t.bn == 384) return launch_tile<T256x384, AK, BKC, EPI, E>(g, s, name);
   if (t.bm == 384 && t.bn == 256) return launch_tile<T384x256, AK, BKC, EPI, E>(g, s, name);
+  if (t.bm == 192 && t.bn == 384) return launch_tile<T192x384, AK, BKC, EPI, E>(g, s, name);
   if (t.bm == 256 && t.bn == 192) return launch_tile<T256x192, AK, BKC, EPI, E>(g, s, name);
   if (t.bm == 192 && t.bn == 256) return launch_tile<T192x256, AK, BKC, EPI, E>(g, s, name);
   if (t.bm == 256 && t.bn == 128) return launch_tile<T256x128, AK, BKC, EPI, E>(g, s, name);

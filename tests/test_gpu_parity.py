@@ -276,6 +276,30 @@ def test_linears_edges(dtype):
         _rel("row.db", f64(gr["db"]), rr["db"], tol)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+def test_weight_grad_192x384_tile_ragged(dtype):
+    """A weight gradient whose shape selects the 192 x 384 tile (six copying
+    waves), with every edge ragged: dW [1496 x 12000] = X^T dY over T = 520
+    (M = 7 x 192 + 152, N = 31 x 384 + 96, K = 16 x 32 + 8)."""
+    dt = DTS[dtype]
+    T, K, N = 520, 1496, 12000
+    print(f"weight grad 192x384 T{T} K{K} N{N} {dt}", flush=True)
+    g = synth.seeded(T + K + N)
+    X = synth.randn(g, (T, K), 1.0, dt)
+    W = synth.randn(g, (K, N), 0.05, dt)
+    dY = synth.randn(g, (T, N), 1.0, dt)
+    tps.trace_start()
+    gc = tps.column_linear_bwd(dev(X), dev(W), dev(dY), tp_size=1)
+    torch.cuda.synchronize()
+    names = [k["name"] for k in tps.trace_stop()]
+    print("  kernels:", names, flush=True)
+    assert any(n.endswith("_tn_f32_192x384") for n in names), names
+    rc = oracle.linear_bwd(f64(X), f64(W), f64(dY))
+    _rel("dW", f64(gc["dW"]), rc["dW"], TOL[dtype])
+    _rel("dX", f64(gc["dX"]), rc["dX"], TOL[dtype])
+    _rel("db", f64(gc["db"]), rc["db"], TOL[dtype])
+
+
 # ---------------------------------------------------------------------------
 # Properties
 # ---------------------------------------------------------------------------
