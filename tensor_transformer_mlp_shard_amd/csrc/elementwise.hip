@@ -29,7 +29,18 @@ __global__ void __launch_bounds__(CS_THREADS) colsum_partial_kernel(const void* 
   const int64_t r1 = min(T, r0 + rows_per_chunk);
   float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (col < N) {
-    for (int64_t r = r0 + wave; r < r1; r += 4) {
+    // Rows r0 + wave, + 4, + 8, ... in that order; four loads in flight.
+    int64_t r = r0 + wave;
+    for (; r + 12 < r1; r += 16) {
+      float v[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load8<E>(in, (r + 4 * u) * N + col, v[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] += v[u][e];
+    }
+    for (; r < r1; r += 4) {
       float v[8];
       load8<E>(in, r * N + col, v);
 #pragma unroll
