@@ -19,8 +19,9 @@ fp64 CPU oracle timed on a bounded sample of the same workload, and, outside
 the step, the same step in fp16, core attention on the rank's local heads (175B
 shape: 4 sequences of 2048 tokens, 12 heads of 128, causal) forward and
 backward, the selective
-recompute forms of the MLP backward, and the sequence-parallel edge steps
-(LayerNorm, bias + dropout + residual) in GB/s.
+recompute forms of the MLP backward, the sequence-parallel edge steps
+(LayerNorm, bias + dropout + residual) in GB/s, and, for context, the step's
+12 matrix products through the vendor library (torch.mm -> hipBLASLt).
 """
 from __future__ import annotations
 
@@ -144,6 +145,37 @@ class CoreAttention:
     def step(self):
         self.fwd()
         self.bwd()
+
+
+def measure_vendor_gemms(torch, shard, steps, warmup):
+    """The step's 12 matrix products through torch.mm (hipBLASLt on ROCm), bf16
+    in and out, on the same resident tensors: context for the hand-written
+    kernels, not a measurement of this library (no epilogues, no bias
+    gradients, bf16 instead of fp32 weight-gradient outputs)."""
+    X, A, B, dY = shard.X, shard.A, shard.B, shard.dY
+    H, Z = shard.fwd_out["H"], shard.fwd_out["Z"]
+    Xa, Wq, dQ, O, Wo, dYa = shard.Xa, shard.Wq, shard.dQ, shard.O, shard.Wo, shard.dYa
+    prods = [(X, A), (H, B), (dY, B.t()), (H.t(), dY), (X.t(), Z), (Z, A.t()),
+             (Xa, Wq), (dQ, Wq.t()), (Xa.t(), dQ), (O, Wo), (dYa, Wo.t()), (O.t(), dYa)]
+    outs = [torch.empty((a.shape[0], b.shape[1]), dtype=a.dtype, device=a.device) for a, b in prods]
+    flops = sum(2.0 * a.shape[0] * a.shape[1] * b.shape[1] for a, b in prods)
+
+    def run():
+        for (a, b), c in zip(prods, outs):
+            torch.mm(a, b, out=c)
+
+    ms, _ = time_steps(torch, run, steps, warmup)
+    names = ["fc1", "fc2", "mlp_dH", "mlp_dB", "mlp_dA", "mlp_dX", "qkv", "qkv_dX", "qkv_dW", "oproj", "oproj_dX",
+             "oproj_dW"]
+    each = []
+    for name, (a, b), c in zip(names, prods, outs):
+        pms, _ = time_steps(torch, lambda a=a, b=b, c=c: torch.mm(a, b, out=c), steps, 3)
+        f = 2.0 * a.shape[0] * a.shape[1] * b.shape[1]
+        each.append({"gemm": name, "m_n_k": [a.shape[0], b.shape[1], a.shape[1]], "ms": round(pms, 4),
+                     "tflops": round(f / (pms * 1e-3) / 1e12, 1)})
+    return {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1), "flop": flops, "per_product": each,
+            "note": "the step's 12 products via torch.mm (hipBLASLt), bf16 in/out, no epilogues or bias "
+                    "gradients: vendor-library context, not this library"}
 
 
 def measure_core_attention(torch, device, steps, warmup):
@@ -435,6 +467,7 @@ def main():
         out["sp_edge"] = measure_sp_edge(torch, device, min(args.steps, 50), min(args.warmup, 10))
         out["selective_recompute"] = measure_recompute(torch, shard, min(args.steps, 50), min(args.warmup, 10))
         out["core_attention"] = measure_core_attention(torch, device, min(args.steps, 50), min(args.warmup, 10))
+        out["vendor_gemms"] = measure_vendor_gemms(torch, shard, min(args.steps, 50), min(args.warmup, 10))
     if not args.no_cpu_baseline and args.part == "all":
         out["cpu_baseline"] = cpu_baseline(shard, args.cpu_frac)
     print(json.dumps(out), flush=True)
