@@ -107,22 +107,26 @@ def attention_head_fwd(q, k, v, causal: bool = True):
     return O, lse, P
 
 
-def attention_head_bwd(q, k, v, dO, causal: bool = True):
+def attention_head_bwd(q, k, v, dO, causal: bool = True, o=None, return_ds: bool = False):
     """Gradients of sum(dO * O) for one head of one sequence.
 
     With P the forward's probabilities and s the scaled scores:
-      dV = P^T dO;  dP = dO V^T;  ds = P * (dP - rowsum(P * dP));
+      dV = P^T dO;  dP = dO V^T;  ds = P * (dP - D);  D = rowsum(P * dP);
       dQ = ds K / sqrt(d);  dK = ds^T Q / sqrt(d).
-    (rowsum(P * dP) equals rowsum(dO * O); the softmax Jacobian.)"""
+    D equals rowsum(dO * O) (the softmax Jacobian).  The IO-aware backward
+    takes D from the output the forward stored; passing that output as `o`
+    gives the gradients of that formulation, D = rowsum(dO * o) (equal to the
+    default when `o` is the exact output).  return_ds: also return ds [S x S]."""
     q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
     d = q.shape[1]
     _, _, P = attention_head_fwd(q, k, v, causal)
     dV = P.T @ dO
     dP = dO @ v.T
-    ds = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+    D = np.sum(P * dP, axis=1, keepdims=True) if o is None else np.sum(dO * _f64(o), axis=1, keepdims=True)
+    ds = P * (dP - D)
     dQ = (ds @ k) / math.sqrt(d)
     dK = (ds.T @ q) / math.sqrt(d)
-    return dQ, dK, dV
+    return (dQ, dK, dV, ds) if return_ds else (dQ, dK, dV)
 
 
 def core_attention_fwd(QKV, seq: int, heads_local: int, d: int, causal: bool = True):
@@ -142,11 +146,14 @@ def core_attention_fwd(QKV, seq: int, heads_local: int, d: int, causal: bool = T
     return merge_heads(O), lse
 
 
-def core_attention_bwd(QKV, dO, seq: int, heads_local: int, d: int, causal: bool = True):
-    """dQKV [T x 3*Hl*d] (same [Q | K | V] layout as the input) of sum(dO * O)."""
+def core_attention_bwd(QKV, dO, seq: int, heads_local: int, d: int, causal: bool = True, O=None):
+    """dQKV [T x 3*Hl*d] (same [Q | K | V] layout as the input) of sum(dO * O).
+    O [T x Hl*d], if given, is the stored forward output the D term is taken
+    from (see attention_head_bwd)."""
     Q, K, V = split_qkv(QKV, heads_local, d)
     Hl, T, _ = Q.shape
     dO3 = _f64(dO).reshape(T, Hl, d).transpose(1, 0, 2)
+    O3 = None if O is None else _f64(O).reshape(T, Hl, d).transpose(1, 0, 2)
     if seq < 1 or T % seq != 0:
         raise ValueError(f"T={T} is not a whole number of sequences of length {seq}")
     dQ = np.zeros_like(Q)
@@ -155,5 +162,6 @@ def core_attention_bwd(QKV, dO, seq: int, heads_local: int, d: int, causal: bool
     for h in range(Hl):
         for b0 in range(0, T, seq):
             sl = slice(b0, b0 + seq)
-            dQ[h, sl], dK[h, sl], dV[h, sl] = attention_head_bwd(Q[h, sl], K[h, sl], V[h, sl], dO3[h, sl], causal)
+            dQ[h, sl], dK[h, sl], dV[h, sl] = attention_head_bwd(Q[h, sl], K[h, sl], V[h, sl], dO3[h, sl], causal,
+                                                                 None if O3 is None else O3[h, sl])
     return np.concatenate([merge_heads(dQ), merge_heads(dK), merge_heads(dV)], axis=1)

@@ -189,6 +189,28 @@ def test_backward_rowsum_identity():
     np.testing.assert_allclose(np.sum(P * dP, 1), np.sum(dO * O, 1), rtol=1e-12, atol=1e-12)
 
 
+def test_backward_with_stored_output():
+    """The stored-output form of the backward (D from the given O) equals the
+    default when O is the exact forward output, and with a perturbed O only
+    dQ and dK move, by exactly ds = -P * delta(D) through K and Q."""
+    rng = np.random.default_rng(10)
+    S, B, Hl, d = 6, 2, 2, 4
+    QKV = _qkv(rng, S * B, Hl, d)
+    dO = rng.standard_normal((S * B, Hl * d))
+    O, _ = oracle.core_attention_fwd(QKV, S, Hl, d, True)
+    base = oracle.core_attention_bwd(QKV, dO, S, Hl, d, True)
+    np.testing.assert_allclose(oracle.core_attention_bwd(QKV, dO, S, Hl, d, True, O=O), base, rtol=1e-12, atol=1e-12)
+    Op = O + 1e-3 * rng.standard_normal(O.shape)
+    got = oracle.core_attention_bwd(QKV, dO, S, Hl, d, True, O=Op)
+    w = Hl * d
+    np.testing.assert_array_equal(got[:, 2 * w:], base[:, 2 * w:])        # dV does not use D
+    # one head of one sequence by hand: dQ moves by -(P * dD) K / sqrt(d)
+    q, k = QKV[:S, :d], QKV[:S, w:w + d]
+    _, _, P = oracle.attention_head_fwd(q, k, QKV[:S, 2 * w:2 * w + d], True)
+    dD = np.sum(dO[:S, :d] * (Op[:S, :d] - O[:S, :d]), axis=1, keepdims=True)
+    np.testing.assert_allclose(got[:S, :d] - base[:S, :d], -(P * dD) @ k / np.sqrt(d), rtol=1e-9, atol=1e-12)
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 def _pins_pass():
@@ -243,15 +265,15 @@ def test_planted_head_layout_mistake_is_caught(monkeypatch):
 def test_planted_backward_mistakes_are_caught(monkeypatch):
     orig = att.attention_head_bwd
 
-    def no_rowsum(q, k, v, dO, causal=True):
+    def no_rowsum(q, k, v, dO, causal=True, o=None):
         q, k, v, dO = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dO))
         d = q.shape[1]
         _, _, P = att.attention_head_fwd(q, k, v, causal)
         ds = P * (dO @ v.T)
         return (ds @ k) / math.sqrt(d), (ds.T @ q) / math.sqrt(d), P.T @ dO
 
-    def untransposed_dv(q, k, v, dO, causal=True):
-        dQ, dK, _ = orig(q, k, v, dO, causal)
+    def untransposed_dv(q, k, v, dO, causal=True, o=None):
+        dQ, dK, _ = orig(q, k, v, dO, causal, o)
         _, _, P = att.attention_head_fwd(q, k, v, causal)
         return dQ, dK, P @ np.asarray(dO, dtype=np.float64)
 
