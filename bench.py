@@ -294,7 +294,7 @@ def roofline_from_trace(tps, torch, fn, steps):
 
 def _source_hash():
     h = hashlib.sha256()
-    for name in ("gemm_bf16.hip", "gemm.h", "common.h", "lds_dma.h"):
+    for name in ("gemm_bf16.hip", "gemm.h", "common.h", "lds_dma.h", "gelu.h"):
         with open(os.path.join(ROOT, "tensor_transformer_mlp_shard_amd", "csrc", name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -9,8 +9,10 @@
 // row.  Pass 2 adds the partial rows of every column in a fixed order.  There
 // are no atomics, so the result is bitwise reproducible.
 //
-// Bias + GeLU.  H = GeLU(Z + b) with 8 elements per lane (16-byte bf16 loads).
+// Bias + GeLU.  H = GeLU(Z + b) with 8 elements per lane (16-byte bf16 loads),
+// the same GeLU evaluation as the GEMM epilogue (gelu.h).
 #include "elem.h"
+#include "gelu.h"
 #include "side.h"
 
 namespace tps {
@@ -101,7 +103,7 @@ __global__ void __launch_bounds__(256) bias_gelu_kernel(const void* Z, const voi
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float x = z[e] + bb[e];
-    h[e] = 0.5f * x * (1.0f + erff(x * 0.7071067811865475f));
+    h[e] = gelu_f(x);
   }
   store8<E>(H, row * N + c, h);
 }

@@ -43,6 +43,7 @@
 // outside the matrix read zero and stores outside it are skipped.  Feature
 // dimensions are multiples of 8, so a 16-byte vector is entirely inside or
 // entirely outside.
+#include "gelu.h"
 #include "gemm.h"
 #include "lds_dma.h"
 
@@ -52,16 +53,6 @@ namespace tps {
 namespace {
 
 constexpr int KT = 32;        // K step per LDS stage
-
-__device__ __forceinline__ float gelu_f(float z) {
-  return 0.5f * z * (1.0f + erff(z * 0.7071067811865475f));
-}
-
-__device__ __forceinline__ float gelu_grad_f(float z) {
-  const float cdf = 0.5f * (1.0f + erff(z * 0.7071067811865475f));
-  const float pdf = 0.3989422804014327f * expf(-0.5f * z * z);
-  return cdf + z * pdf;
-}
 
 // The two 16-bit element types: operand vectors and the matching MFMA.
 template <typename E> struct Vec;
