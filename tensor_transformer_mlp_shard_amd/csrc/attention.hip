@@ -17,7 +17,11 @@
 // the score accumulators hold them (per lane half: 4 keys, skip 4, 4 keys) and
 // the V^T operand is read from LDS with transposing reads in that same order.
 // The O^T accumulator again has one query per lane, so the rescale by
-// exp(m_old - m_new) is a per-lane multiply.
+// exp(m_old - m_new) is a per-lane multiply.  K runs one block ahead of V:
+// while a block's probabilities are formed, the next block's scores are
+// computed, so the vector work sits between MFMAs of the same wave.  The
+// running maximum a lane's probabilities are taken against moves only when a
+// block exceeds it by more than 2^8 (RESCALE_LOG2), so the rescale is rare.
 #include "attention.h"
 
 #include <cmath>
@@ -39,10 +43,9 @@ struct Shape {
   static constexpr int CH = D / 8;                      // 16-byte chunks per K/V row
   static constexpr int ROW_BYTES = D * 2;
   static constexpr int BLOCK_BYTES = BKEYS * ROW_BYTES;  // one K (or V) block
-  static constexpr int LOADS = 2 * BKEYS * CH / NT;     // 16-byte loads per thread per K+V block
   static constexpr int KS = D / 16;                     // 16-wide d slices of a score product
   static constexpr int DT = D / 32;                     // 32-row d tiles of O^T
-  static_assert(LOADS % 2 == 0 && (LOADS / 2) * NT == BKEYS * CH, "whole K and V loads per thread");
+  static_assert(BLOCK_BYTES % (1024 * AW) == 0, "whole 1 KiB copies per wave per block");
 };
 
 // LDS layout of a block (rows = keys or queries, D bf16 each): 16-byte chunk c
