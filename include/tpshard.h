@@ -323,7 +323,12 @@ int tp_unscale_check_finite(float* grads, int64_t n, float inv_scale, int32_t* f
  * matching call: T, d_in, d_out = (T, K, N) for the linears, (T, h, F) for the
  * MLP and its recompute form, (T, N, unused) for the bias gradient, (T, heads, head_dim) for the
  * attention backward (dtype TP_BF16), (rows, h, unused) for the LayerNorm and
- * bias-dropout-add backwards.  Returns 0 for invalid arguments.
+ * bias-dropout-add backwards.  Returns 0 for invalid arguments.  In the linear
+ * and MLP backwards it holds the bias-gradient partials: with 16-bit storage
+ * most weight-gradient tile shapes add the columns of dY while dY passes
+ * through the GEMM and leave one fp32 row per row of tiles; otherwise a
+ * column-sum pass over dY leaves its own partial rows.  The MLP backward also
+ * keeps dZ there (and the recompute form H and Z).
  */
 size_t tp_workspace_size(int32_t op, int64_t T, int64_t d_in, int64_t d_out, int32_t tp_size,
                          int32_t dtype);

@@ -127,6 +127,28 @@ GemmArgs make_args(const void* A, int64_t lda, const void* B, int64_t ldb, int64
 
 size_t colsum_ws_bytes(int64_t T, int64_t N) { return round_up((size_t)colsum_chunks(T, N) * (size_t)N * 4); }
 
+// Workspace of a bias gradient db = sum_t dY [N] that goes with a weight
+// gradient dW = X^T dY [M x N].  On the 16-bit path the weight-gradient GEMM
+// adds dY's columns while dY passes through it (GemmArgs::colsum) and leaves
+// one partial row per row of tiles; the fp32 path runs the column-sum pass.
+bool db_fused(int32_t dtype, int64_t M, int64_t N) {
+  return dtype != TP_FP32 && gemm16_colsum_rows((int)M, (int)N) > 0;
+}
+
+size_t db_ws_bytes(int32_t dtype, int64_t T, int64_t M, int64_t N) {
+  if (!db_fused(dtype, M, N)) return colsum_ws_bytes(T, N);
+  return round_up((size_t)gemm16_colsum_rows((int)M, (int)N) * (size_t)N * 4);
+}
+
+// db (+)= sum_t dY after the weight-gradient GEMM g (dW = X^T dY, B = dY) has
+// run, with g.colsum = part where db_fused (its partial rows are added here),
+// else by the column-sum pass over dY.
+hipError_t bias_grad_after_wgrad(const GemmArgs& g, const void* dY, float* db, float* part, int accumulate,
+                                 int64_t T, int32_t dtype, hipStream_t s) {
+  if (!db_fused(dtype, g.M, g.N)) return colsum(dY, elem_of(dtype), db, part, accumulate, T, g.N, s);
+  return sum_partials(part, db, g.N, gemm16_colsum_rows(g.M, g.N), accumulate, "colsum_finalize", s);
+}
+
 // Shape checks shared by the attention entry points; fills p on success.
 int check_attention(int64_t T, int64_t seq, int64_t heads, int64_t head_dim, int32_t tp_size, int32_t causal,
                     int32_t dtype, AttnProblem& p) {
@@ -215,27 +237,28 @@ size_t tp_workspace_size(int32_t op, int64_t T, int64_t d_in, int64_t d_out, int
       if (d_in < 1 || d_in > kMaxDim) return 0;
       return colsum_ws_bytes(T, d_in);
     case TP_OP_COLUMN_LINEAR_BWD:
-      if (tp_size < 1 || d_out < 1 || d_out > kMaxDim || d_out % tp_size) return 0;
-      return colsum_ws_bytes(T, d_out / tp_size);
+      // db_i with dW_i = X^T dY_i [K x N/p]
+      if (tp_size < 1 || d_in < 1 || d_out < 1 || d_in > kMaxDim || d_out > kMaxDim || d_out % tp_size) return 0;
+      return db_ws_bytes(dtype, T, d_in, d_out / tp_size);
     case TP_OP_ROW_LINEAR_BWD:
-      if (d_out < 1 || d_out > kMaxDim) return 0;
-      return colsum_ws_bytes(T, d_out);
+      // db with dW_i = X_i^T dY [K/p x N]
+      if (tp_size < 1 || d_in < 1 || d_out < 1 || d_in > kMaxDim || d_out > kMaxDim || d_in % tp_size) return 0;
+      return db_ws_bytes(dtype, T, d_in / tp_size, d_out);
     case TP_OP_MLP_SHARD_BWD: {
+      // dZ [T x f], then the partials of db2 (with dB_i [f x h]) or db1 (with dA_i [h x f]), one at a time
       if (tp_size < 1 || d_in < 1 || d_out < 1 || d_in > kMaxDim || d_out > kMaxDim || d_out % tp_size) return 0;
       const int64_t f = d_out / tp_size;
       const size_t dz = round_up((size_t)T * (size_t)f * elsize(dtype));
-      const size_t cs = colsum_ws_bytes(T, f) > colsum_ws_bytes(T, d_in) ? colsum_ws_bytes(T, f)
-                                                                          : colsum_ws_bytes(T, d_in);
-      return dz + cs;
+      const size_t c2 = db_ws_bytes(dtype, T, f, d_in), c1 = db_ws_bytes(dtype, T, d_in, f);
+      return dz + (c2 > c1 ? c2 : c1);
     }
     case TP_OP_MLP_SHARD_BWD_RECOMPUTE: {
-      // dZ, H and (when Z is not saved) Z [T x f], then the column-sum partials
+      // dZ, H and (when Z is not saved) Z [T x f], then the bias-gradient partials as above
       if (tp_size < 1 || d_in < 1 || d_out < 1 || d_in > kMaxDim || d_out > kMaxDim || d_out % tp_size) return 0;
       const int64_t f = d_out / tp_size;
       const size_t act = round_up((size_t)T * (size_t)f * elsize(dtype));
-      const size_t cs = colsum_ws_bytes(T, f) > colsum_ws_bytes(T, d_in) ? colsum_ws_bytes(T, f)
-                                                                          : colsum_ws_bytes(T, d_in);
-      return 3 * act + cs;
+      const size_t c2 = db_ws_bytes(dtype, T, f, d_in), c1 = db_ws_bytes(dtype, T, d_in, f);
+      return 3 * act + (c2 > c1 ? c2 : c1);
     }
     case TP_OP_LAYERNORM_BWD:
       // dgamma and dbeta partial rows of every workgroup (d_in = h)
@@ -330,20 +353,21 @@ static int mlp_bwd_gemms(const void* X, const void* A_i, const void* B_i, const 
   g1.aux = Z_i;
   g1.ldaux = f;
   HIP_TRY(gemm(dtype, g1, true, true, EPI_DGELU, s));
-  // dB_i = H_i^T dY                       [f x h], contraction over T
+  // dB_i = H_i^T dY                       [f x h], contraction over T; db2 = sum_t dY
   GemmArgs g2 = make_args(H_i, f, dY, h, f, h, T, dB_i, h);
   g2.accumulate = accumulate;
+  if (db2 && db_fused(dtype, f, h)) g2.colsum = part;
   HIP_TRY(gemm(dtype, g2, false, false, EPI_F32, s));
-  // dA_i = X^T dZ                         [h x f], contraction over T
+  if (db2) HIP_TRY(bias_grad_after_wgrad(g2, dY, db2, part, accumulate, T, dtype, s));
+  // dA_i = X^T dZ                         [h x f], contraction over T; db1_i = sum_t dZ
   GemmArgs g3 = make_args(X, h, dZ, f, h, f, T, dA_i, f);
   g3.accumulate = accumulate;
+  if (db1_i && db_fused(dtype, h, f)) g3.colsum = part;
   HIP_TRY(gemm(dtype, g3, false, false, EPI_F32, s));
+  if (db1_i) HIP_TRY(bias_grad_after_wgrad(g3, dZ, db1_i, part, accumulate, T, dtype, s));
   // dX_i = dZ A_i^T                       [T x h], contraction over f
   GemmArgs g4 = make_args(dZ, f, A_i, f, T, h, f, dX_i, h);
   HIP_TRY(gemm(dtype, g4, true, true, EPI_STORE, s));
-  // db1_i = sum_t dZ, db2 = sum_t dY
-  if (db1_i) HIP_TRY(colsum(dZ, elem_of(dtype), db1_i, part, accumulate, T, f, s));
-  if (db2) HIP_TRY(colsum(dY, elem_of(dtype), db2, part, accumulate, T, h, s));
   return TP_OK;
 }
 
@@ -439,11 +463,12 @@ int tp_column_linear_bwd(const void* X, const void* W_i, const void* dY_i, void*
   // dX = dY_i W_i^T  [T x K], contraction over n
   GemmArgs g1 = make_args(dY_i, n, W_i, n, T, K, n, dX_partial, K);
   HIP_TRY(gemm(dtype, g1, true, true, EPI_STORE, s));
-  // dW_i = X^T dY_i  [K x n], contraction over T
+  // dW_i = X^T dY_i  [K x n], contraction over T; db_i = sum_t dY_i
   GemmArgs g2 = make_args(X, K, dY_i, n, K, n, T, dW_i, n);
   g2.accumulate = accumulate;
+  if (db_i && db_fused(dtype, K, n)) g2.colsum = (float*)workspace;
   HIP_TRY(gemm(dtype, g2, false, false, EPI_F32, s));
-  if (db_i) HIP_TRY(colsum(dY_i, elem_of(dtype), db_i, (float*)workspace, accumulate, T, n, s));
+  if (db_i) HIP_TRY(bias_grad_after_wgrad(g2, dY_i, db_i, (float*)workspace, accumulate, T, dtype, s));
   return TP_OK;
 }
 
@@ -468,11 +493,12 @@ int tp_row_linear_bwd(const void* X_i, const void* W_i, const void* dY, void* dX
   // dX_i = dY W_i^T  [T x k], contraction over N
   GemmArgs g1 = make_args(dY, N, W_i, N, T, k, N, dX_i, k);
   HIP_TRY(gemm(dtype, g1, true, true, EPI_STORE, s));
-  // dW_i = X_i^T dY  [k x N], contraction over T
+  // dW_i = X_i^T dY  [k x N], contraction over T; db = sum_t dY
   GemmArgs g2 = make_args(X_i, k, dY, N, k, N, T, dW_i, N);
   g2.accumulate = accumulate;
+  if (db && db_fused(dtype, k, N)) g2.colsum = (float*)workspace;
   HIP_TRY(gemm(dtype, g2, false, false, EPI_F32, s));
-  if (db) HIP_TRY(colsum(dY, elem_of(dtype), db, (float*)workspace, accumulate, T, N, s));
+  if (db) HIP_TRY(bias_grad_after_wgrad(g2, dY, db, (float*)workspace, accumulate, T, dtype, s));
   return TP_OK;
 }
 

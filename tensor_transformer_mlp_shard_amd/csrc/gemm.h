@@ -29,6 +29,11 @@ struct GemmArgs {
   const void* aux;    // [M x N] read by EPI_DGELU
   int64_t ldaux;
   int accumulate;     // EPI_F32 only
+  // 16-bit EPI_F32 with B stored [K x N] only, nullable: partial column sums of
+  // B over K, gemm16_colsum_rows(M, N) rows of N floats (row r = the sum over
+  // a subset of K, the rows together cover K once).  Adding the rows gives the
+  // bias gradient that goes with a weight gradient dW = X^T dY (db = sum_t dY).
+  float* colsum;
   int group_m;        // tile rows per group in the tile order (set by the launcher)
 };
 
@@ -37,5 +42,8 @@ struct GemmArgs {
 hipError_t gemm_bf16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s);
 hipError_t gemm_f16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s);
 hipError_t gemm_f32(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s);
+
+// Rows of GemmArgs::colsum written by the 16-bit GEMM for an M x N product.
+int gemm16_colsum_rows(int M, int N);
 
 }  // namespace tps

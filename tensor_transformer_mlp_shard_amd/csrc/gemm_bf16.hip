@@ -39,6 +39,10 @@
 // of C; the epilogue stages them through LDS and writes whole 16-byte runs of
 // rows (and reads GeLU's Z the same way).
 //
+// Bias gradients.  A weight gradient dW = X^T dY can also return the column
+// sums of its B operand dY (db = sum_t dY) from the B panels already in LDS
+// (BColSum), so the gradient is not read from HBM a second time.
+//
 // Edges.  M, N and K may be ragged against the tile (T is arbitrary); loads
 // outside the matrix read zero and stores outside it are skipped.  Feature
 // dimensions are multiples of 8, so a 16-byte vector is entirely inside or
@@ -127,6 +131,9 @@ struct Cfg {
   static constexpr int NVM = A_INS + B_INS;    // 1 KiB copies per copying wave per step
   static constexpr int WAVES_PER_EU = (NW + 3) / 4;
   static constexpr bool DBUF = NPROD > 0;       // double-buffered operands (register budget)
+  // Column sums of B ride along (BColSum) on the tiles whose consumers have
+  // registers to spare; the two biggest tiles are at the 256-register limit.
+  static constexpr bool CSUM = BM * BN < 256 * 384;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "consumer tile must be whole 32x32 blocks");
   static_assert(A_INS * NCOPY * 1024 == A_BYTES && B_INS * NCOPY * 1024 == B_BYTES, "whole copies");
   static_assert(NSTAGE >= 3, "need at least three stages");
@@ -252,6 +259,64 @@ struct Reader {
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
       fb[j] = BKC ? frag_k(sb, wn * C::WN + 32 * j, s) : frag_mn(sb, C::BN * 2, tr_swz_b, wn * C::WN + 32 * j, s);
+  }
+};
+
+// Column sums of B over K, computed alongside a weight gradient whose B
+// operand (stored [K x N]) is the output gradient dY: the sums are the bias
+// gradient db = sum_t dY, so dY is not read a second time.  The tiles_m tiles
+// of a column panel split K between them: tile row tm adds the K steps tm,
+// tm + tiles_m, ... of its B panel, while that step is in LDS anyway.  Lane L
+// of the first BN consumer lanes owns columns 4 (L / 4) .. + 3 of the panel
+// and k-rows j, j + 4, ..., j + 28 (j = L % 4) of a step; its 4 fp32 sums stay
+// in registers over the K loop (4, not 8: the big tiles have no registers to
+// spare).  At the end the 4 lanes of a column quad are added in a fixed order
+// and the tile writes its partial row (row tm); a second pass adds the
+// tiles_m rows in order.
+template <class C, typename E>
+struct BColSum {
+  using V4 = typename Vec<E>::v4;
+  static constexpr int LANES = C::BN;     // one lane per 4 columns and 8 k-rows
+  static_assert(LANES % 64 == 0 && LANES <= 64 * C::NCONS, "column-sum lanes are whole consumer waves");
+  static_assert(KT == 32, "eight k-rows per lane");
+  float s[4];
+  int next;   // next K step this tile adds (wave-uniform)
+  bool on;    // wave-uniform: sums wanted and this wave takes part
+
+  __device__ __forceinline__ void init(const GemmArgs& g, int wave, int tm) {
+    on = g.colsum != nullptr && wave * 64 < LANES;
+    next = tm;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] = 0.0f;
+  }
+  // Add K step kt (in LDS) when it is this tile's.
+  __device__ __forceinline__ void step(const char* smem, int kt, int tiles_m, int wave, int lane) {
+    if (!on || kt != next) return;
+    next += tiles_m;
+    // The address is derived here, inside the branch, rather than hoisted above
+    // the K loop where it would hold registers that the main loop needs.
+    asm volatile("" : "+v"(lane));
+    const int L = wave * 64 + lane, q = L >> 2, j = L & 3;
+    // rows j + 4 u all have row j's chunk swizzle (it depends on the row mod 4)
+    const int off = j * (C::BN * 2) + (((q >> 1) ^ mn_swz<C::BN>(j)) * 16) + (q & 1) * 8;
+    const char* sb = smem + (kt % C::NSTAGE) * C::STAGE + C::A_BYTES + off;
+    V4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *(const V4*)(sb + u * 4 * C::BN * 2);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] += (float)v[u][e];
+  }
+  // Add the 4 lanes of each column quad and write the tile's partial row.
+  __device__ __forceinline__ void finish(const GemmArgs& g, int tm, int n0, int wave, int lane) {
+    if (!on) return;
+#pragma unroll
+    for (int m = 1; m < 4; m <<= 1)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] += __shfl_xor(s[e], m);
+    const int n = n0 + 4 * ((wave * 64 + lane) >> 2);
+    if ((lane & 3) == 0 && n < g.N) *(f32x4*)(g.colsum + (int64_t)tm * g.N + n) = f32x4{s[0], s[1], s[2], s[3]};
   }
 };
 
@@ -431,6 +496,9 @@ gemm_kernel(GemmArgs g) {
   // ------------------------------------------------------------ consumer wave
   Reader<C, AK, BKC, E> rd;
   rd.init(wave, lane);
+  constexpr bool CS = C::CSUM && !BKC && EPI == EPI_F32;   // B stored [K x N]: its column sums can ride along
+  BColSum<C, E> cs;
+  if constexpr (CS) cs.init(g, wave, tm);
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -463,6 +531,7 @@ gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) mfma(fa[LB], fb[LB], i, j);
       if constexpr (AK && BKC) __builtin_amdgcn_s_setprio(0);
+      if constexpr (CS) cs.step(smem, kt, tiles_m, wave, lane);
       __syncthreads();
       rd.load(smem, kt + 1, 0, fa[LB ^ 1], fb[LB ^ 1]);
 #pragma unroll
@@ -520,6 +589,7 @@ gemm_kernel(GemmArgs g) {
           }
       }
       __builtin_amdgcn_s_setprio(0);
+      if constexpr (CS) cs.step(smem, kt, tiles_m, wave, lane);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step kt+1 landed
       __syncthreads();
 #pragma unroll
@@ -530,6 +600,7 @@ gemm_kernel(GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no copy into this workgroup's LDS outlives it
   }
 
+  if constexpr (CS) cs.finish(g, tm, n0, wave, lane);
   __syncthreads();  // every consumer is done with the ring (producer copies have drained)
   epilogue<C, EPI, E>(g, acc, m0, n0, wave, lane, smem);
 }
@@ -620,10 +691,13 @@ hipError_t gemm16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hi
   const double out_bytes = (epi == EPI_F32 ? 4.0 * (g.accumulate ? 2 : 1) : 2.0) * g.M * (double)g.N;
   info.bytes = 2.0 * ((double)g.M * g.K + (double)g.K * g.N) + out_bytes +
                ((epi == EPI_BIAS_GELU && g.C2) ? 2.0 * g.M * (double)g.N : 0.0) +
-               (epi == EPI_DGELU ? 2.0 * g.M * (double)g.N : 0.0);
+               (epi == EPI_DGELU ? 2.0 * g.M * (double)g.N : 0.0) +
+               (g.colsum ? 4.0 * g.N * (double)gemm16_colsum_rows(g.M, g.N) : 0.0);
   // Instantiated layout / epilogue pairs: forward (NN), data gradient (NT) and
   // weight gradient (TN).
   hipError_t e = hipErrorInvalidValue;
+  // column sums: B stored [K x N], fp32 out, a tile that carries them
+  if (g.colsum != nullptr && (b_kcontig || epi != EPI_F32 || gemm16_colsum_rows(g.M, g.N) == 0)) return e;
   trace_begin(s);
   if (a_kcontig && !b_kcontig && epi == EPI_STORE) e = launch_shape<true, false, EPI_STORE, E>(g, s, &info.name);
   else if (a_kcontig && !b_kcontig && epi == EPI_BIAS_GELU)
@@ -643,6 +717,12 @@ hipError_t gemm_bf16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi,
 
 hipError_t gemm_f16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s) {
   return gemm16<f16>(g, a_kcontig, b_kcontig, epi, s);
+}
+
+int gemm16_colsum_rows(int M, int N) {
+  const TileChoice t = choose_tile(M, N);
+  if (t.bm * t.bn >= 256 * 384) return 0;   // that tile does not carry the column sums (Cfg::CSUM)
+  return (M + t.bm - 1) / t.bm;
 }
 
 }  // namespace tps

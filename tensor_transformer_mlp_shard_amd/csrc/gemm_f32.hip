@@ -110,6 +110,7 @@ hipError_t gemm_f32(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, 
   info.flops = 2.0 * g.M * (double)g.N * g.K;
   info.bytes = 4.0 * ((double)g.M * g.K + (double)g.K * g.N + (double)g.M * g.N);
   hipError_t e = hipErrorInvalidValue;
+  if (g.colsum != nullptr) return e;  // column sums ride on the 16-bit kernels only
   trace_begin(s);
   if (a_kcontig && !b_kcontig && epi == EPI_STORE) e = launch<true, false, EPI_STORE>(g, s);
   else if (a_kcontig && !b_kcontig && epi == EPI_BIAS_GELU) e = launch<true, false, EPI_BIAS_GELU>(g, s);
