@@ -18,9 +18,11 @@
 //  * "split" kernels (tiles up to 256 x 192): 8 consumer waves (2 per SIMD) and
 //    4 producer waves that only issue the copies;
 //  * "shared" kernels (256 x 384, 384 x 256, 192 x 384): 8 waves, each a
-//    consumer of a 128 x 96 (96 x 128, 96 x 96) sub-tile; all 8 (six for
-//    192 x 384, whose 36 KiB per step do not split eight ways) also issue the
-//    copies.  The biggest tile moves 29% fewer bytes per FLOP from L2 and
+//    consumer of a 128 x 96 (96 x 128, 96 x 96) sub-tile; all 8 also issue
+//    the copies, except in 192 x 384, whose 36 KiB per step do not split
+//    eight ways: there waves 0-3, one per SIMD, issue 9 copies each (six
+//    copying waves would put 12 copies per step on two SIMDs and 6 on the
+//    others, and the per-step barrier waits for the busiest).  The biggest tile moves 29% fewer bytes per FLOP from L2 and
 //    reads 31% fewer operand bytes from LDS than 256 x 192, which matters
 //    because the chip runs at its power limit and data movement lowers the
 //    clock; 192 x 384 sits in between and fills whole waves of 256 tiles
@@ -114,8 +116,9 @@ __device__ __forceinline__ int mn_swz(int r) {
 
 
 // Kernel shape: tile, waves and their roles, LDS ring.  NSHCOPY_ (shared
-// kernels only): how many of the 8 waves issue the copies, when a K step's
-// 1 KiB copies do not divide evenly over all 8.
+// kernels only): how many of the 8 waves issue the copies (waves 0 .. NSHCOPY_-1;
+// a workgroup's waves go to the four SIMDs in turn), when a K step's 1 KiB
+// copies do not divide evenly over all 8.
 template <int BM_, int BN_, int NPROD_, int CM_, int NSHCOPY_ = 8>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_;
@@ -614,7 +617,7 @@ using T128x256 = Cfg<128, 256, 4, 2>;
 using T128x128 = Cfg<128, 128, 4, 2>;
 using T256x384 = Cfg<256, 384, 0, 2>;
 using T384x256 = Cfg<384, 256, 0, 4>;
-using T192x384 = Cfg<192, 384, 0, 2, 6>;  // 36 KiB per K step: 6 copying waves x 6 copies
+using T192x384 = Cfg<192, 384, 0, 2, 4>;  // 36 KiB per K step: 4 copying waves (one per SIMD) x 9 copies
 
 template <class C, bool AK, bool BKC, int EPI, typename E>
 const char* kname() {
