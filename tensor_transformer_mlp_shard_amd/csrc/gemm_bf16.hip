@@ -654,11 +654,13 @@ hipError_t launch_tile(const GemmArgs& g_in, hipStream_t s, const char** name) {
   GemmArgs g = g_in;
   const int tiles_m = (g.M + C::BM - 1) / C::BM, tiles_n = (g.N + C::BN - 1) / C::BN;
   g.group_m = choose_group_m(tiles_m, C::BM, C::BN);
-  // Measured exception: the 192 x 384 weight-gradient tile (both operands
-  // M/N-contiguous) runs 2% faster with twice the height the estimate picks
-  // (longer contiguous runs of each token row per K step); the other
-  // kernels ran 1-3% slower with either half or twice the estimate.
+  // Measured exceptions to the estimate: the 192 x 384 weight-gradient tile
+  // (both operands M/N-contiguous) runs 2% faster with twice the height
+  // (longer contiguous runs of each token row per K step), the 256 x 384
+  // data-gradient tile (both K-contiguous) 0.6-0.9% faster with half; the
+  // other kernels ran 1-3% slower with either.
   if (!AK && !BKC && C::BM == 192 && 2 * g.group_m <= tiles_m) g.group_m *= 2;
+  if (AK && BKC && C::BM == 256 && C::BN == 384 && g.group_m > 1) g.group_m /= 2;
   hipLaunchKernelGGL((gemm_kernel<C, AK, BKC, EPI, E>), dim3(tiles_m * tiles_n), dim3(C::NT), 0, s, g);
   return hipGetLastError();
 }
