@@ -278,7 +278,7 @@ def test_linears_edges(dtype):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
 def test_weight_grad_192x384_tile_ragged(dtype):
-    """A weight gradient whose shape selects the 192 x 384 tile (six copying
+    """A weight gradient whose shape selects the 192 x 384 tile (four copying
     waves), with every edge ragged: dW [1496 x 12000] = X^T dY over T = 520
     (M = 7 x 192 + 152, N = 31 x 384 + 96, K = 16 x 32 + 8)."""
     dt = DTS[dtype]
@@ -298,6 +298,47 @@ def test_weight_grad_192x384_tile_ragged(dtype):
     _rel("dW", f64(gc["dW"]), rc["dW"], TOL[dtype])
     _rel("dX", f64(gc["dX"]), rc["dX"], TOL[dtype])
     _rel("db", f64(gc["db"]), rc["db"], 1e-5)   # dY exact in the storage type: fp32-summation error only
+
+
+# (T, K_in, N_out) of a column linear whose forward (NN, T x N_out), data
+# gradient (NT, T x K_in) and weight gradient (TN, K_in x N_out) select the
+# big shared tiles named after each shape; every edge is ragged (T is odd or
+# not a multiple of 64, the feature sizes are multiples of 8 but not of 32).
+BIG_TILES = [
+    (2179, 6136, 8184, ("nn_store_256x384", "nt_store_192x384", "tn_f32_384x256")),
+    (2179, 10232, 2040, ("nt_store_256x384", "tn_f32_256x384")),
+    (3000, 8184, 3080, ("nt_store_384x256", "tn_f32_192x384")),
+    (3000, 2040, 8184, ("nn_store_384x256", "tn_f32_192x384")),
+    (2100, 3080, 6136, ("nn_store_192x384", "tn_f32_256x384")),
+]
+
+
+@pytest.mark.parametrize("shape", BIG_TILES, ids=[f"T{s[0]}_K{s[1]}_N{s[2]}" for s in BIG_TILES])
+def test_big_tiles_ragged(shape):
+    """The 256 x 384, 384 x 256 and 192 x 384 kernels on all three operand
+    layouts with ragged M, N and K, whole tensors against the oracle (bias in
+    the forward, fused or separate bias gradient in the backward)."""
+    T, K, N, want = shape
+    print(f"big tiles T{T} K{K} N{N}", flush=True)
+    g = synth.seeded(T + 3 * K + 7 * N)
+    X = synth.randn(g, (T, K), 1.0, "bf16")
+    W = synth.randn(g, (K, N), 0.02, "bf16")
+    b = synth.randn(g, (N,), 0.02, "bf16")
+    dY = synth.randn(g, (T, N), 1.0, "bf16")
+    tps.trace_start()
+    y = tps.column_linear(dev(X), dev(W), dev(b), tp_size=1)
+    gc = tps.column_linear_bwd(dev(X), dev(W), dev(dY), tp_size=1)
+    torch.cuda.synchronize()
+    names = [k["name"] for k in tps.trace_stop()]
+    print("  kernels:", names, flush=True)
+    for w in want:
+        assert any(n.endswith(w) for n in names), (w, names)
+    x, w_, dy = f64(X), f64(W), f64(dY)
+    _rel("Y", f64(y), oracle.column_linear_fwd(x, w_, f64(b)), 5e-3)
+    rc = oracle.linear_bwd(x, w_, dy)
+    _rel("dX", f64(gc["dX"]), rc["dX"], 5e-3)
+    _rel("dW", f64(gc["dW"]), rc["dW"], 5e-3)
+    _rel("db", f64(gc["db"]), rc["db"], 1e-5)   # dY exact in bf16: fp32-summation error only
 
 
 # (T, K, N) of dW = X^T dY [K x N] over T tokens: T = 40 has two K steps, so
