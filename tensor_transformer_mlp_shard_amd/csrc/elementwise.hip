@@ -60,31 +60,49 @@ __global__ void __launch_bounds__(CS_THREADS) colsum_partial_kernel(const void* 
   }
 }
 
-// Pass 2: a workgroup owns 64 columns (one per lane); wave w adds the partial
-// rows w, w+4, ... in that order (loads issued 8 at a time, added in order),
-// and the four wave sums are added in a fixed order.
-__global__ void __launch_bounds__(256) colsum_finalize_kernel(const float* part, float* out, int64_t N,
-                                                              int chunks, int accumulate) {
-  __shared__ float red[4][64];
+// Pass 2: a workgroup owns 64 columns (one per lane) of one of up to two
+// (partial rows, output) pairs (blockIdx.y picks the pair).  Its 16 waves split
+// the partial rows: wave w adds rows w, w + 16, w + 32, ... in that order, with
+// up to 16 loads in flight before the adds (one round trip for 256 rows); the
+// 16 wave sums are then added in a fixed order.
+constexpr int FIN_WAVES = 16;
+
+__global__ void __launch_bounds__(64 * FIN_WAVES) colsum_finalize_kernel(const float* part, float* out,
+                                                                        const float* part2, float* out2, int64_t N,
+                                                                        int chunks, int accumulate) {
+  __shared__ float red[FIN_WAVES][64];
+  if (blockIdx.y == 1) {
+    part = part2;
+    out = out2;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t n = (int64_t)blockIdx.x * 64 + lane;
   float t = 0.0f;
   if (n < N) {
     int c = wave;
-    for (; c + 28 < chunks; c += 32) {
-      float v[8];
+    for (; c + FIN_WAVES * 15 < chunks; c += FIN_WAVES * 16) {
+      float v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(c + 4 * u) * N + n];
+      for (int u = 0; u < 16; ++u) v[u] = part[(int64_t)(c + FIN_WAVES * u) * N + n];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) t += v[u];
+      for (int u = 0; u < 16; ++u) t += v[u];
     }
-    for (; c < chunks; c += 4) t += part[(int64_t)c * N + n];
+    for (; c + FIN_WAVES * 3 < chunks; c += FIN_WAVES * 4) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = part[(int64_t)(c + FIN_WAVES * u) * N + n];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) t += v[u];
+    }
+    for (; c < chunks; c += FIN_WAVES) t += part[(int64_t)c * N + n];
   }
   red[wave][lane] = t;
   __syncthreads();
   if (wave == 0 && n < N) {
-    const float s = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
-    out[n] = accumulate ? out[n] + s : s;
+    float sum = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < FIN_WAVES; ++w) sum += red[w][lane];
+    out[n] = accumulate ? out[n] + sum : sum;
   }
 }
 
@@ -173,18 +191,19 @@ hipError_t colsum(const void* in, Elem el, float* out, float* ws, int accumulate
   if (e != hipSuccess) return e;
   LaunchInfo info2{"colsum_finalize", 0.0, 4.0 * chunks * (double)N + 4.0 * (accumulate ? 2 : 1) * N};
   trace_begin(s);
-  hipLaunchKernelGGL(colsum_finalize_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, s,
-                     (const float*)ws, out, N, chunks, accumulate);
+  hipLaunchKernelGGL(colsum_finalize_kernel, dim3((unsigned)((N + 63) / 64)), dim3(64 * FIN_WAVES), 0, s,
+                     (const float*)ws, out, (const float*)nullptr, (float*)nullptr, N, chunks, accumulate);
   trace_end(s, info2);
   return hipGetLastError();
 }
 
 hipError_t sum_partials(const float* part, float* out, int64_t N, int chunks, int accumulate, const char* name,
-                        hipStream_t s) {
-  LaunchInfo info{name, 0.0, 4.0 * chunks * (double)N + 4.0 * (accumulate ? 2 : 1) * N};
+                        hipStream_t s, const float* part2, float* out2) {
+  const int pairs = out2 != nullptr ? 2 : 1;
+  LaunchInfo info{name, 0.0, pairs * (4.0 * chunks * (double)N + 4.0 * (accumulate ? 2 : 1) * N)};
   trace_begin(s);
-  hipLaunchKernelGGL(colsum_finalize_kernel, dim3((unsigned)((N + 63) / 64)), dim3(256), 0, s, part, out, N, chunks,
-                     accumulate);
+  hipLaunchKernelGGL(colsum_finalize_kernel, dim3((unsigned)((N + 63) / 64), (unsigned)pairs), dim3(64 * FIN_WAVES),
+                     0, s, part, out, part2, out2, N, chunks, accumulate);
   trace_end(s, info);
   return hipGetLastError();
 }

@@ -12,9 +12,10 @@ int colsum_chunks(int64_t T, int64_t N);
 hipError_t colsum(const void* in, Elem el, float* out, float* ws, int accumulate,
                   int64_t T, int64_t N, hipStream_t s);
 
-// out[n] (+)= sum over c < chunks of part[c * N + n], in a fixed order (elementwise.hip).
+// out[n] (+)= sum over c < chunks of part[c * N + n], in a fixed order (elementwise.hip);
+// with out2 given, the same for (part2, out2) in the same launch.
 hipError_t sum_partials(const float* part, float* out, int64_t N, int chunks, int accumulate, const char* name,
-                        hipStream_t s);
+                        hipStream_t s, const float* part2 = nullptr, float* out2 = nullptr);
 
 // H = GeLU(Z + b) elementwise (elementwise.hip).
 hipError_t bias_gelu(const void* Z, const void* b, void* H, Elem el, int64_t T, int64_t N, hipStream_t s);

@@ -234,8 +234,11 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
-    const uint32_t hi0 = __umulhi(0xD2511F53u, x0), lo0 = 0xD2511F53u * x0;
-    const uint32_t hi1 = __umulhi(0xCD9E8D57u, x2), lo1 = 0xCD9E8D57u * x2;
+    // One 32 x 32 -> 64-bit multiply per product (v_mad_u64_u32) instead of
+    // separate high and low halves.
+    const uint64_t p0 = (uint64_t)0xD2511F53u * x0, p1 = (uint64_t)0xCD9E8D57u * x2;
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
     const uint32_t n0 = hi1 ^ x1 ^ k0, n2 = hi0 ^ x3 ^ k1;
     x0 = n0;
     x1 = lo1;
@@ -335,9 +338,9 @@ hipError_t layernorm_bwd(const void* X, const void* gamma, const float* mean, co
   trace_end(s, info);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = sum_partials(ws, dgamma, h, chunks, accumulate, "layernorm_bwd_finalize", s);
-  if (e != hipSuccess || dbeta == nullptr) return e;
-  return sum_partials(ws + (int64_t)chunks * h, dbeta, h, chunks, accumulate, "layernorm_bwd_finalize", s);
+  // dgamma and dbeta (when wanted) from their partial rows in one launch.
+  return sum_partials(ws, dgamma, h, chunks, accumulate, "layernorm_bwd_finalize", s,
+                      dbeta != nullptr ? ws + (int64_t)chunks * h : nullptr, dbeta);
 }
 
 hipError_t bias_dropout_add_fwd(const void* Y, const void* b, const void* residual, void* out, int64_t rows,
