@@ -313,32 +313,36 @@ BIG_TILES = [
 ]
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
 @pytest.mark.parametrize("shape", BIG_TILES, ids=[f"T{s[0]}_K{s[1]}_N{s[2]}" for s in BIG_TILES])
-def test_big_tiles_ragged(shape):
+def test_big_tiles_ragged(shape, dtype):
     """The 256 x 384, 384 x 256 and 192 x 384 kernels on all three operand
     layouts with ragged M, N and K, whole tensors against the oracle (bias in
     the forward, fused or separate bias gradient in the backward)."""
     T, K, N, want = shape
-    print(f"big tiles T{T} K{K} N{N}", flush=True)
+    dt = DTS[dtype]
+    print(f"big tiles T{T} K{K} N{N} {dt}", flush=True)
     g = synth.seeded(T + 3 * K + 7 * N)
-    X = synth.randn(g, (T, K), 1.0, "bf16")
-    W = synth.randn(g, (K, N), 0.02, "bf16")
-    b = synth.randn(g, (N,), 0.02, "bf16")
-    dY = synth.randn(g, (T, N), 1.0, "bf16")
+    X = synth.randn(g, (T, K), 1.0, dt)
+    W = synth.randn(g, (K, N), 0.02, dt)
+    b = synth.randn(g, (N,), 0.02, dt)
+    dY = synth.randn(g, (T, N), 1.0, dt)
     tps.trace_start()
     y = tps.column_linear(dev(X), dev(W), dev(b), tp_size=1)
     gc = tps.column_linear_bwd(dev(X), dev(W), dev(dY), tp_size=1)
     torch.cuda.synchronize()
     names = [k["name"] for k in tps.trace_stop()]
     print("  kernels:", names, flush=True)
+    prefix = "gemm_bf16_" if dtype == torch.bfloat16 else "gemm_f16_"
     for w in want:
-        assert any(n.endswith(w) for n in names), (w, names)
+        assert any(n == prefix + w for n in names), (w, names)
     x, w_, dy = f64(X), f64(W), f64(dY)
-    _rel("Y", f64(y), oracle.column_linear_fwd(x, w_, f64(b)), 5e-3)
+    tol = TOL[dtype]
+    _rel("Y", f64(y), oracle.column_linear_fwd(x, w_, f64(b)), tol)
     rc = oracle.linear_bwd(x, w_, dy)
-    _rel("dX", f64(gc["dX"]), rc["dX"], 5e-3)
-    _rel("dW", f64(gc["dW"]), rc["dW"], 5e-3)
-    _rel("db", f64(gc["db"]), rc["db"], 1e-5)   # dY exact in bf16: fp32-summation error only
+    _rel("dX", f64(gc["dX"]), rc["dX"], tol)
+    _rel("dW", f64(gc["dW"]), rc["dW"], tol)
+    _rel("db", f64(gc["db"]), rc["db"], 1e-5)   # dY exact in the storage type: fp32-summation error only
 
 
 # (T, K, N) of dW = X^T dY [K x N] over T tokens: T = 40 has two K steps, so
