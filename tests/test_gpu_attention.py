@@ -56,6 +56,9 @@ CASES = [  # (T, seq, heads, head_dim, tp, causal, sigma)
     (384, 128, 4, 128, 2, True, 2.0),
     (520, 260, 2, 64, 1, False, 1.5),
     (1024, 512, 2, 128, 1, True, 1.0),
+    # longer ragged causal sequences (partial last query and key blocks)
+    (1200, 600, 2, 128, 1, True, 1.0),
+    (2200, 1100, 4, 64, 2, True, 1.0),
 ]
 
 
