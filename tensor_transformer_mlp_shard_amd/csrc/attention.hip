@@ -364,8 +364,9 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(FwdArgs a) {
 // With P the forward's probabilities (recomputed from the saved log-sum-exp),
 // dP = dO V^T and Dt = rowsum(dO * O) = rowsum(P * dP):
 //   dV = P^T dO,  dS = P * (dP - Dt),  dK = dS^T Q / sqrt(D),  dQ = dS K / sqrt(D).
-// Three kernels, no atomics (bitwise reproducible):
-//  * attn_bwd_dot: Dt for every (token, head);
+// Two kernels, no atomics (bitwise reproducible), dQ first:
+//  * attn_bwd_dq (below) also forms Dt for its queries from the dO rows it
+//    holds and the matching O rows, and writes it for attn_bwd_dkdv;
 //  * attn_bwd_dkdv: a workgroup owns 128 keys (32 per wave, one per lane
 //    column); K and V of its keys stay in registers; queries (Q and dO rows)
 //    are copied HBM -> LDS directly in double-buffered blocks of 64.  Scores are computed as S[query][key] so each lane
@@ -390,28 +391,6 @@ struct BwdArgs {
 };
 
 constexpr float LOG2E = 1.4426950408889634f;
-
-// Dt[h, t] = sum_d dO[t, h, d] * O[t, h, d]; D/8 lanes per (token, head) row.
-template <int D>
-__global__ void __launch_bounds__(NT) attn_bwd_dot_kernel(BwdArgs a) {
-  constexpr int LPR = D / 8;  // lanes per row
-  const int64_t row = ((int64_t)blockIdx.x * NT + threadIdx.x) / LPR;   // token * Hl + head
-  const int part = threadIdx.x % LPR;
-  float s = 0.0f;
-  if (row < a.T * a.Hl) {
-    const bf16x8 o = *(const bf16x8*)(a.o + row * D + part * 8);
-    const bf16x8 g = *(const bf16x8*)(a.dout + row * D + part * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s += (float)o[e] * (float)g[e];
-  }
-#pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) s += __shfl_xor(s, m);
-  if (row < a.T * a.Hl && part == 0) {
-    const int64_t t = row / a.Hl;
-    const int h = (int)(row % a.Hl);
-    a.dt[(int64_t)h * a.T + t] = s;
-  }
-}
 
 template <int D>
 __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
@@ -662,7 +641,22 @@ __global__ void __launch_bounds__(NT, 2) attn_bwd_dq_kernel(BwdArgs a) {
     gf[s] = qvalid ? *(const bf16x8*)(dobase + (int64_t)qi * ldo + 16 * s + 8 * hh) : bf16x8{};
   }
   const float lse2 = qvalid ? a.lse[(int64_t)h * a.T + row0 + qi] * LOG2E : INFINITY;
-  const float dti = qvalid ? a.dt[(int64_t)h * a.T + row0 + qi] : 0.0f;
+  // Dt = rowsum(dO * O) for this lane's query: this lane holds half of the dO
+  // row (d = 16 s + 8 hh + 0..7), lane ^ 32 the other half; the two partial
+  // sums are added (the same value in both lanes: fp32 addition commutes) and
+  // written for the dK/dV kernel.
+  float dti = 0.0f;
+  {
+    const bf16* orow = a.o + (row0 + qi) * ldo + (int64_t)h * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < SH::KS; ++s) {
+      const bf16x8 ov = qvalid ? *(const bf16x8*)(orow + 16 * s) : bf16x8{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dti += (float)gf[s][e] * (float)ov[e];
+    }
+    dti += other_half(dti, (lane ^ 32) * 4);
+    if (qvalid && hh == 0) a.dt[(int64_t)h * a.T + row0 + qi] = dti;
+  }
   const int g16 = lane >> 4, i16 = lane & 15;
   KvReadOffsets<D> ro;  // row reads of K / V (.k), transposing reads of K^T (.va, .vb)
   ro.init(l32, hh, 4 * (g16 >> 1) + (i16 >> 2), 16 * (g16 & 1) + 4 * (i16 & 3));
@@ -825,29 +819,23 @@ hipError_t attention_bwd(const bf16* qkv, const bf16* o, const float* lse, const
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p.D));
   const double el = 2.0 * p.T * p.Hl * p.D;   // bytes of one [T x Hl*D] bf16 tensor
   const bool d128 = p.D == 128;
-  const dim3 grid_dot((unsigned)((p.T * p.Hl * (p.D / 8) + NT - 1) / NT));
-  LaunchInfo i0{d128 ? "attn_bwd_dot_d128" : "attn_bwd_dot_d64", 0.0, 2.0 * el + 4.0 * p.T * p.Hl};
-  trace_begin(s);
-  if (d128) hipLaunchKernelGGL(attn_bwd_dot_kernel<128>, grid_dot, dim3(NT), 0, s, a);
-  else hipLaunchKernelGGL(attn_bwd_dot_kernel<64>, grid_dot, dim3(NT), 0, s, a);
-  trace_end(s, i0);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const double f = attention_fwd_flops(p);   // 2 products per allowed pair
   const dim3 grid((unsigned)((int64_t)a.nb * a.B * a.Hl));
-  // dK, dV: S, dP, dV, dK (4 products); dQ: S^T, dP^T, dQ (3 products)
+  // dQ: S^T, dP^T, dQ (3 products), and Dt for dK/dV (reads O as well);
+  // dK, dV: S, dP, dV, dK (4 products)
+  LaunchInfo i2{d128 ? "attn_bwd_dq_d128" : "attn_bwd_dq_d64", 1.5 * f,
+                4.0 * el + 4.0 * p.T * p.Hl + el};
+  trace_begin(s);
+  if (d128) hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, grid, dim3(NT), 0, s, a);
+  else hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, grid, dim3(NT), 0, s, a);
+  trace_end(s, i2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   LaunchInfo i1{d128 ? "attn_bwd_dkdv_d128" : "attn_bwd_dkdv_d64", 2.0 * f, 3.0 * el + 4.0 * 2 * p.T * p.Hl + 2.0 * el};
   trace_begin(s);
   if (d128) hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, grid, dim3(NT), 0, s, a);
   else hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, grid, dim3(NT), 0, s, a);
   trace_end(s, i1);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  LaunchInfo i2{d128 ? "attn_bwd_dq_d128" : "attn_bwd_dq_d64", 1.5 * f, 3.0 * el + 4.0 * 2 * p.T * p.Hl + el};
-  trace_begin(s);
-  if (d128) hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, grid, dim3(NT), 0, s, a);
-  else hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, grid, dim3(NT), 0, s, a);
-  trace_end(s, i2);
   return hipGetLastError();
 }
 
