@@ -21,7 +21,7 @@ Sources (the web pages this method is described on):
   matrix 12288 x 36864 in 8 shards of 12288 x 4608 (so each rank's shard holds
   a third of its width for each of Q, K and V).
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * Scaled dot-product attention per head with the causal mask of a GPT
   decoder: O = softmax(Q K^T / sqrt(d) + M) V, M[i, j] = -inf for j > i.

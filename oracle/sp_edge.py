@@ -24,7 +24,7 @@ Sources:
   Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11): a
   10-round bijection of a 128-bit counter under a 64-bit key.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * LayerNorm over the hidden dimension with learned gain and bias:
   y = (x - mean) / sqrt(var + eps) * gamma + beta, var the biased variance;

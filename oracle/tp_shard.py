@@ -22,7 +22,7 @@ Sources (the web pages this method is described on):
   same Transformer placement.  "案例拆解：175B 的张量并行": the 175B QKV matrix
   12288 x 36864 cut into 8 shards of 12288 x 4608.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * GeLU is the exact one, GeLU(z) = z * Phi(z) with Phi the standard normal CDF
   (the pages only say "GeLU").
