@@ -239,6 +239,37 @@ def test_mlp_edges(shape, dtype):
     check_mlp_full(d["X"], d["A"], d["b1"], d["B"], d["dY"], p, dtype)
 
 
+def _random_shapes(n, seed):
+    """n seeded (T, h, f, p) draws: T from three ranges (tiny, one to a few
+    tiles, several thousand), h and f any multiple of 8 up to 4096, p in
+    {1, 2, 4, 8}; kept to shapes the oracle finishes in well under a second."""
+    import random
+
+    rng = random.Random(seed)
+    out = []
+    while len(out) < n:
+        T = rng.choice([rng.randint(1, 64), rng.randint(65, 900), rng.randint(900, 3000)])
+        h, p, f = 8 * rng.randint(1, 512), rng.choice([1, 2, 4, 8]), 8 * rng.randint(1, 512)
+        if 6 * T * h * f <= 4e10:
+            out.append((T, h, f, p))
+    return out
+
+
+RANDOM_SHAPES = _random_shapes(10, 20261203)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("shape", RANDOM_SHAPES, ids=[f"T{s[0]}_h{s[1]}_f{s[2]}_p{s[3]}" for s in RANDOM_SHAPES])
+def test_mlp_random_shapes(shape, dtype):
+    """A fixed-seed sweep of shapes nobody picked by hand (ragged everywhere),
+    MLP shard forward and backward, whole tensors against the oracle."""
+    T, h, f, p = shape
+    dt = DTS[dtype]
+    d = synth.mlp_inputs(T, h, f * p, p, dt, 0.05, seed=T + 3 * h + 5 * f, full=False)
+    print(f"random {shape} {dt}", flush=True)
+    check_mlp_full(d["X"], d["A"], d["b1"], d["B"], d["dY"], p, dtype)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32], ids=["bf16", "fp16", "fp32"])
 def test_linears_edges(dtype):
     dt = DTS[dtype]
