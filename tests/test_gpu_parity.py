@@ -272,39 +272,72 @@ def test_mlp_random_shapes(shape, dtype):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32], ids=["bf16", "fp16", "fp32"])
 def test_linears_edges(dtype):
+    for T, K, N, p in [(5, 48, 96, 2), (133, 288, 544, 4), (300, 1024, 264, 1)]:
+        _check_linears(T, K, N, p, dtype)
+
+
+def _check_linears(T, K, N, p, dtype):
+    """Column linear (plain and bias + GeLU) and row linear with bias, forward
+    and backward, whole tensors against the oracle."""
     dt = DTS[dtype]
     tol = TOL[dtype]
-    for T, K, N, p in [(5, 48, 96, 2), (133, 288, 544, 4), (300, 1024, 264, 1)]:
-        print(f"linears T{T} K{K} N{N} p{p} {dt}", flush=True)
-        g = synth.seeded(T + K + N)
-        X = synth.randn(g, (T, K), 1.0, dt)
-        W = synth.randn(g, (K, N // p), 0.05, dt)
-        b = synth.randn(g, (N // p,), 0.05, dt)
-        dY = synth.randn(g, (T, N // p), 1.0, dt)
-        Xi = synth.randn(g, (T, K // p), 1.0, dt)
-        Wr = synth.randn(g, (K // p, N), 0.05, dt)
-        br = synth.randn(g, (N,), 0.05, dt)
-        dYr = synth.randn(g, (T, N), 1.0, dt)
-        y = tps.column_linear(dev(X), dev(W), dev(b), tp_size=p)
-        yg, zg = tps.column_linear(dev(X), dev(W), dev(b), tp_size=p, act="gelu", save_z=True)
-        gc = tps.column_linear_bwd(dev(X), dev(W), dev(dY), tp_size=p)
-        yr = tps.row_linear(dev(Xi), dev(Wr), dev(br), tp_size=p)
-        gr = tps.row_linear_bwd(dev(Xi), dev(Wr), dev(dYr), tp_size=p)
-        torch.cuda.synchronize()
-        zr, yr_ref = oracle.column_linear_fwd(f64(X), f64(W), f64(b))
-        _rel("col.Y", f64(y), yr_ref, tol)
-        zg_ref, yg_ref = oracle.column_linear_fwd(f64(X), f64(W), f64(b), act="gelu")
-        _rel("col.Zg", f64(zg), zg_ref, tol)
-        _rel("col.Yg", f64(yg), yg_ref, tol)
-        rc = oracle.linear_bwd(f64(X), f64(W), f64(dY))
-        _rel("col.dX", f64(gc["dX"]), rc["dX"], tol)
-        _rel("col.dW", f64(gc["dW"]), rc["dW"], tol)
-        _rel("col.db", f64(gc["db"]), rc["db"], tol)
-        _rel("row.Y", f64(yr), oracle.row_linear_fwd(f64(Xi), f64(Wr), f64(br)), tol)
-        rr = oracle.linear_bwd(f64(Xi), f64(Wr), f64(dYr))
-        _rel("row.dX", f64(gr["dX"]), rr["dX"], tol)
-        _rel("row.dW", f64(gr["dW"]), rr["dW"], tol)
-        _rel("row.db", f64(gr["db"]), rr["db"], tol)
+    print(f"linears T{T} K{K} N{N} p{p} {dt}", flush=True)
+    g = synth.seeded(T + K + N)
+    X = synth.randn(g, (T, K), 1.0, dt)
+    W = synth.randn(g, (K, N // p), 0.05, dt)
+    b = synth.randn(g, (N // p,), 0.05, dt)
+    dY = synth.randn(g, (T, N // p), 1.0, dt)
+    Xi = synth.randn(g, (T, K // p), 1.0, dt)
+    Wr = synth.randn(g, (K // p, N), 0.05, dt)
+    br = synth.randn(g, (N,), 0.05, dt)
+    dYr = synth.randn(g, (T, N), 1.0, dt)
+    y = tps.column_linear(dev(X), dev(W), dev(b), tp_size=p)
+    yg, zg = tps.column_linear(dev(X), dev(W), dev(b), tp_size=p, act="gelu", save_z=True)
+    gc = tps.column_linear_bwd(dev(X), dev(W), dev(dY), tp_size=p)
+    yr = tps.row_linear(dev(Xi), dev(Wr), dev(br), tp_size=p)
+    gr = tps.row_linear_bwd(dev(Xi), dev(Wr), dev(dYr), tp_size=p)
+    torch.cuda.synchronize()
+    zr, yr_ref = oracle.column_linear_fwd(f64(X), f64(W), f64(b))
+    _rel("col.Y", f64(y), yr_ref, tol)
+    zg_ref, yg_ref = oracle.column_linear_fwd(f64(X), f64(W), f64(b), act="gelu")
+    _rel("col.Zg", f64(zg), zg_ref, tol)
+    _rel("col.Yg", f64(yg), yg_ref, tol)
+    rc = oracle.linear_bwd(f64(X), f64(W), f64(dY))
+    _rel("col.dX", f64(gc["dX"]), rc["dX"], tol)
+    _rel("col.dW", f64(gc["dW"]), rc["dW"], tol)
+    _rel("col.db", f64(gc["db"]), rc["db"], tol)
+    _rel("row.Y", f64(yr), oracle.row_linear_fwd(f64(Xi), f64(Wr), f64(br)), tol)
+    rr = oracle.linear_bwd(f64(Xi), f64(Wr), f64(dYr))
+    _rel("row.dX", f64(gr["dX"]), rr["dX"], tol)
+    _rel("row.dW", f64(gr["dW"]), rr["dW"], tol)
+    _rel("row.db", f64(gr["db"]), rr["db"], tol)
+
+
+def _random_linear_shapes(n, seed):
+    """n seeded (T, K, N, p) draws, K and N multiples of 8 p (each rank's
+    share a multiple of 8), T from three ranges; oracle work kept small."""
+    import random
+
+    rng = random.Random(seed)
+    out = []
+    while len(out) < n:
+        T = rng.choice([rng.randint(1, 64), rng.randint(65, 900), rng.randint(900, 3000)])
+        p = rng.choice([1, 2, 4, 8])
+        K, N = 8 * p * rng.randint(1, 4096 // (8 * p)), 8 * p * rng.randint(1, 4096 // (8 * p))
+        if 8 * T * K * N // p <= 4e10:
+            out.append((T, K, N, p))
+    return out
+
+
+RANDOM_LINEARS = _random_linear_shapes(8, 31415)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("shape", RANDOM_LINEARS, ids=[f"T{s[0]}_K{s[1]}_N{s[2]}_p{s[3]}" for s in RANDOM_LINEARS])
+def test_linears_random_shapes(shape, dtype):
+    """A fixed-seed sweep of column and row linear shapes (ragged T, any
+    feature sizes the ABI accepts), forward and backward against the oracle."""
+    _check_linears(*shape, dtype)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
