@@ -75,6 +75,43 @@ def test_attention_fwd_small(T, seq, heads, d, tp, causal, sigma):
     _lse(f64(lse), lse_ref)
 
 
+def _random_attention_cases(n, seed):
+    """n seeded (T, seq, heads, d, tp, causal, sigma) draws: sequence lengths
+    1-1400 (ragged against the 64-key and 128-query blocks), 1-3 sequences,
+    1-4 local heads at p in {1, 2}, head dim 64 or 128, both masks."""
+    import random
+
+    rng = random.Random(seed)
+    out = []
+    for _ in range(n):
+        seq = rng.choice([rng.randint(1, 200), rng.randint(200, 1400)])
+        B, hl, tp = rng.randint(1, 3), rng.randint(1, 4), rng.choice([1, 2])
+        out.append((B * seq, seq, hl * tp, rng.choice([64, 128]), tp, rng.random() < 0.7, 1.0))
+    return out
+
+
+RANDOM_CASES = _random_attention_cases(8, 271828)
+
+
+@pytest.mark.parametrize("T,seq,heads,d,tp,causal,sigma", RANDOM_CASES,
+                         ids=[f"T{c[0]}_S{c[1]}_H{c[2]}_d{c[3]}_p{c[4]}_{'causal' if c[5] else 'full'}"
+                              for c in RANDOM_CASES])
+def test_attention_random_shapes(T, seq, heads, d, tp, causal, sigma):
+    """A fixed-seed sweep of attention shapes nobody picked by hand: forward (O,
+    lse) and backward (dQ, dK, dV), whole tensors against the oracle."""
+    hl = heads // tp
+    x = synth.core_attn_inputs(T, hl, d, "bf16", sigma, seed=T * 11 + d + heads)
+    print(f"random case T={T} S={seq} Hl={hl} d={d} causal={causal}", flush=True)
+    O, lse = tps.attention_fwd(x["QKV"].to(DEV), seq=seq, heads=heads, head_dim=d, tp_size=tp, causal=causal)
+    torch.cuda.synchronize()
+    O_ref, lse_ref = oracle.core_attention_fwd(f64(x["QKV"]), seq, hl, d, causal)
+    _rel("O", f64(O), O_ref)
+    _lse(f64(lse), lse_ref)
+    got = _bwd_case(x, T, seq, heads, d, tp, causal)
+    ref = oracle.core_attention_bwd(f64(x["QKV"]), f64(x["dO"]), seq, hl, d, causal)
+    _rel_blocks(got, ref, hl * d)
+
+
 def _sampled_pairs(w, n):
     rng = np.random.default_rng(w.seed)
     B = w.T // w.seq
