@@ -357,7 +357,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frac", type=int, default=1, help="oracle sample = 1/N of the tokens")
-    ap.add_argument("--part", choices=["all", "mlp", "attn", "core_attn"], default="all",
+    ap.add_argument("--part", choices=["all", "mlp", "attn", "core_attn", "sp_edge"], default="all",
                     help="run only one part (for profiling runs)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the measurements outside the step (selective recompute, core attention, "
@@ -391,6 +391,9 @@ def main():
     if args.part == "core_attn":
         print(json.dumps({"core_attention": measure_core_attention(torch, device, args.steps, args.warmup)}),
               flush=True)
+        return
+    if args.part == "sp_edge":
+        print(json.dumps({"sp_edge": measure_sp_edge(torch, device, args.steps, args.warmup)}), flush=True)
         return
     shard = Shard(device)
     fn = {"all": shard.step, "mlp": shard.mlp_step, "attn": shard.attn_step}[args.part]
