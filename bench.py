@@ -233,6 +233,42 @@ def measure_sp_edge(torch, device, steps, warmup):
             "ms_per_step": round(ms, 4), "kernels": kern}
 
 
+def measure_side(torch, device, steps, warmup):
+    """The HBM-bound side kernels on the 175B MLP shard's shapes: the replicated
+    row-parallel bias gradient db2 = sum_t dY over dY [2048 x 12288] (column-sum
+    pass + fixed-order finalize) and the unfused H = GeLU(Z + b1) over
+    Z [2048 x 6144] that the fused fc1 epilogue replaces: GB/s of algorithmic
+    traffic per kernel."""
+    import tensor_transformer_mlp_shard_amd as tps
+    from tensor_transformer_mlp_shard_amd import _native, synth
+
+    w = synth.WORKLOADS["gpt175b_mlp_tp8"]
+    f = w.F // w.tp
+    g = synth.seeded(w.seed + 7)
+    dY = synth.randn(g, (w.T, w.h), 1.0, "bf16").to(device)
+    Z = synth.randn(g, (w.T, f), 1.0, "bf16").to(device)
+    b1 = synth.randn(g, (f,), 0.02, "bf16").to(device)
+    ws = torch.empty(tps.workspace_size(_native.TP_OP_BIAS_GRAD, w.T, w.h, 0, 1, torch.bfloat16), dtype=torch.uint8,
+                     device=device)
+
+    def step():
+        tps.bias_grad(dY, workspace=ws)
+        tps.bias_gelu(Z, b1)
+
+    ms, _ = time_steps(torch, step, steps, warmup)
+    tps.trace_start(4096)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kern = [{"name": k["name"], "launches_per_step": k["launches"] // steps,
+             "us_per_step": round(1e3 * k["total_ms"] / steps, 2),
+             "gbs": round(k["bytes"] / (k["total_ms"] * 1e-3) / 1e9, 1),
+             "frac_hbm": round(k["bytes"] / (k["total_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
+            for k in tps.trace_stop()]
+    return {"workload": f"db2 = sum_t dY over {w.T} x {w.h} and GeLU(Z + b1) over {w.T} x {f}, bf16",
+            "ms_per_step": round(ms, 4), "kernels": kern}
+
+
 def measure_recompute(torch, shard, steps, warmup):
     """MLP shard fwd+bwd with all activations saved against the two selective
     recompute forms: Z kept (H recomputed by an elementwise GeLU) and nothing
@@ -357,7 +393,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frac", type=int, default=1, help="oracle sample = 1/N of the tokens")
-    ap.add_argument("--part", choices=["all", "mlp", "attn", "core_attn", "sp_edge"], default="all",
+    ap.add_argument("--part", choices=["all", "mlp", "attn", "core_attn", "sp_edge", "side"], default="all",
                     help="run only one part (for profiling runs)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the measurements outside the step (selective recompute, core attention, "
@@ -394,6 +430,9 @@ def main():
         return
     if args.part == "sp_edge":
         print(json.dumps({"sp_edge": measure_sp_edge(torch, device, args.steps, args.warmup)}), flush=True)
+        return
+    if args.part == "side":
+        print(json.dumps({"side_kernels": measure_side(torch, device, args.steps, args.warmup)}), flush=True)
         return
     shard = Shard(device)
     fn = {"all": shard.step, "mlp": shard.mlp_step, "attn": shard.attn_step}[args.part]
@@ -468,6 +507,7 @@ def main():
                             "note": "the same step with IEEE-half storage (fp16 matrix-core instruction)"}
         del sh16
         out["sp_edge"] = measure_sp_edge(torch, device, min(args.steps, 50), min(args.warmup, 10))
+        out["side_kernels"] = measure_side(torch, device, min(args.steps, 50), min(args.warmup, 10))
         out["selective_recompute"] = measure_recompute(torch, shard, min(args.steps, 50), min(args.warmup, 10))
         out["core_attention"] = measure_core_attention(torch, device, min(args.steps, 50), min(args.warmup, 10))
         out["vendor_gemms"] = measure_vendor_gemms(torch, shard, min(args.steps, 50), min(args.warmup, 10))
