@@ -40,6 +40,12 @@ def _rel(name, got, ref, tol=TOL):
     assert e <= tol, f"{name}: rel_fro {e:.3e} > {tol:g}"
 
 
+def _bf16_ulp(x):
+    """Spacing of bf16 numbers at |x| (8 significant bits): 2^(floor(log2|x|) - 7)."""
+    a = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
 def _lse(got, ref):
     e = float(np.max(np.abs(got - ref)))
     print(f"  lse    max_abs={e:.3e} (tol {LSE_TOL:g})", flush=True)
@@ -216,15 +222,22 @@ def test_attention_growing_scores(d, step, causal):
     block rescales O) or by less (probabilities above 1 accumulate against a
     stale maximum between rescales).  O and lse against the oracle at the
     usual bounds; dK and dV against the exact gradient at the usual bound.
+
     dQ = dS K / sqrt(d) is ill-conditioned here: each row of dS sums to zero
     and K's rows share a large common component, so dQ is a small remainder
-    of large terms.  The bf16 rounding of the stored O alone moves it 3-15%
-    from the exact gradient (measured on the CPU, everything else exact).  It
-    is therefore checked element by element against the oracle's stored-O
-    form (D = rowsum(dO * O) with the O the forward returned), within 2^-6 of
-    the magnitude sum (|dS| |K|) / sqrt(d) of the terms it adds: the kernel
-    rounds dS to bf16 (relative 2^-9) before its MFMA, and P and dP - D carry
-    fp32 rounding of the recomputed scores."""
+    of large terms, and the 16-bit rounding of the stored O alone moves it
+    3-15% from the exact gradient.  The IO-aware backward takes the softmax
+    Jacobian term D = rowsum(dO * O) from the O the forward stored (the
+    stored-output reading of the backward).  The reference is therefore the
+    oracle's backward with that term taken from the oracle's exact O rounded
+    to nearest-even bf16 -- nothing in it comes from the kernels.  dQ is
+    compared element by element within
+      2^-6 (|dS| |K|) / sqrt(d)  +  (P * dD) |K| / sqrt(d),
+    where the first term covers the kernel's rounding of dS to bf16 (relative
+    2^-9) and the fp32 rounding of the recomputed scores, and the second one
+    bf16 ulp of freedom in each stored O element (the kernel's fp32 O may round
+    to either neighbour of the exact value): dD_t = sum_i |dO_ti| ulp(O_ti),
+    and a change dD_t of D moves dQ_t by -(P_t. dD_t) K / sqrt(d)."""
     T, hl = 512, 2
     g = synth.seeded(int(step) * 100 + d + int(causal))
     u = torch.randn(d, generator=g)
@@ -254,12 +267,18 @@ def test_attention_growing_scores(d, step, causal):
     _rel("dK", got[:, w:2 * w], exact[:, w:2 * w])
     _rel("dV", got[:, 2 * w:], exact[:, 2 * w:])
     Q3, K3, V3 = oracle.split_qkv(f64(qkv), hl, d)
-    dO3, O3 = (f64(t).reshape(T, hl, d).transpose(1, 0, 2) for t in (dO, O))
+    dO3 = f64(dO).reshape(T, hl, d).transpose(1, 0, 2)
+    # the stored O of the reading above: the oracle's exact O, rounded RNE to bf16
+    O_st = torch.from_numpy(O_ref).to(torch.bfloat16).to(torch.float64).numpy()
+    O3 = O_st.reshape(T, hl, d).transpose(1, 0, 2)
     worst = 0.0
     for h in range(hl):
         dq_ref, _, _, ds = oracle.attention_head_bwd(Q3[h], K3[h], V3[h], dO3[h], causal, o=O3[h], return_ds=True)
-        scale = np.abs(ds) @ np.abs(K3[h]) / np.sqrt(d)
+        _, _, P = oracle.attention_head_fwd(Q3[h], K3[h], V3[h], causal)
+        absK = np.abs(K3[h])
+        dD = np.sum(np.abs(dO3[h]) * _bf16_ulp(O3[h]), axis=1, keepdims=True)
+        bound = (2 ** -6 * (np.abs(ds) @ absK) + (P * dD) @ absK) / np.sqrt(d)
         err = np.abs(got[:, h * d:(h + 1) * d] - dq_ref)
-        worst = max(worst, float(np.max(err / (scale + 1e-6 * scale.max()))))
-    print(f"  dQ     max |err| / (|dS||K|/sqrt(d)) = {worst:.3e} (bound {2**-6:.3e})", flush=True)
-    assert worst <= 2 ** -6
+        worst = max(worst, float(np.max(err / (bound + 1e-6 * bound.max()))))
+    print(f"  dQ     max |err| / bound = {worst:.3e} (must be <= 1)", flush=True)
+    assert worst <= 1.0

@@ -410,3 +410,133 @@ def test_planted_erf_scale_mistake_is_caught(monkeypatch):
                         lambda z: 0.5 * (1.0 + oracle.tp_shard._erf(np.asarray(z, dtype=np.float64))))  # missing /sqrt2
     with pytest.raises(AssertionError):
         test_normal_table_values()
+
+
+# ---------------------------------------------------------------------------
+# The unfused bias + GeLU step and the row-parallel output bias
+# ([TUT] "融合优化技术": bias + GeLU; [TUT] "张量并行原理": the row-parallel
+# partial, with the output bias added on one rank only)
+# ---------------------------------------------------------------------------
+def _bf_bias_gelu(Z, b):
+    """H[t][n] = GeLU(Z[t][n] + b[n]) by Python loops and math.erf."""
+    return [[_bf_gelu(Z[t][n] + b[n]) for n in range(len(b))] for t in range(len(Z))]
+
+
+def _bf_row_linear(X_i, W_i, b):
+    """Y[t][n] = (b[n] if b else 0) + sum_k X_i[t][k] W_i[k][n] by Python loops."""
+    T, k, N = len(X_i), len(W_i), len(W_i[0])
+    return [[(b[n] if b is not None else 0.0) + sum(X_i[t][j] * W_i[j][n] for j in range(k)) for n in range(N)]
+            for t in range(T)]
+
+
+# Non-square shapes, so that a bias broadcast along the wrong axis either fails
+# to broadcast or lands on the wrong elements.
+_BIAS_SHAPES = [(1, 1), (1, 5), (4, 1), (3, 7), (7, 3), (5, 8)]
+
+
+def _bias_gelu_err(seed=11):
+    rng = _rng(seed)
+    worst = 0.0
+    for T, N in _BIAS_SHAPES:
+        Z = rng.standard_normal((T, N)) * 1.5
+        b = rng.standard_normal(N)
+        ref = _bf_bias_gelu(Z.tolist(), b.tolist())
+        worst = max(worst, float(np.max(np.abs(np.asarray(ref) - oracle.bias_gelu(Z, b)))))
+    return worst
+
+
+def test_bias_gelu_bruteforce():
+    assert _bias_gelu_err() <= 1e-14
+
+
+def test_bias_gelu_against_torch_float64():
+    rng = _rng(12)
+    Z = rng.standard_normal((37, 53)) * 2.0
+    b = rng.standard_normal(53)
+    ref = torch.nn.functional.gelu(torch.from_numpy(Z) + torch.from_numpy(b)[None, :], approximate="none")
+    assert oracle.rel_fro(oracle.bias_gelu(Z, b), ref.numpy()) <= 1e-14
+
+
+def test_bias_gelu_special_cases():
+    # b = -Z row by row gives GeLU(0) = 0; Z = 0 gives GeLU(b) on every row
+    b = np.array([-1.0, 0.0, 1.0, 2.5])
+    np.testing.assert_array_equal(oracle.bias_gelu(-np.tile(b, (3, 1)), b), np.zeros((3, 4)))
+    H = oracle.bias_gelu(np.zeros((2, 4)), b)
+    table = {float(r[0]): float(r[1]) for r in _read_table("normal_table.txt")}
+    for j, x in enumerate(b):
+        if round(float(x), 2) in table:
+            assert abs(H[0, j] - x * table[round(float(x), 2)]) <= 6e-5 * max(1.0, abs(x))
+    np.testing.assert_array_equal(H[0], H[1])
+
+
+def _row_linear_bias_err(seed=13):
+    rng = _rng(seed)
+    worst = 0.0
+    for T, k, N in [(1, 1, 1), (2, 3, 5), (5, 8, 3), (4, 6, 9)]:
+        X_i = rng.standard_normal((T, k))
+        W_i = rng.standard_normal((k, N))
+        b = rng.standard_normal(N)
+        for bias in (b, None):
+            ref = _bf_row_linear(X_i.tolist(), W_i.tolist(), None if bias is None else bias.tolist())
+            got = oracle.row_linear_fwd(X_i, W_i, bias)
+            worst = max(worst, float(np.max(np.abs(np.asarray(ref) - got))))
+    return worst
+
+
+def test_row_linear_bias_bruteforce():
+    assert _row_linear_bias_err() <= 1e-13
+
+
+def test_row_linear_bias_once_gives_full_layer():
+    """Summing the ranks' partials, with the output bias passed on one rank only,
+    gives the unsharded layer X W + b (torch float64 as the second library)."""
+    rng = _rng(14)
+    T, K, N, p = 9, 24, 10, 4
+    X = rng.standard_normal((T, K))
+    W = rng.standard_normal((K, N))
+    b = rng.standard_normal(N)
+    full = (torch.from_numpy(X) @ torch.from_numpy(W) + torch.from_numpy(b)[None, :]).numpy()
+    for owner in range(p):
+        s = sum(oracle.row_linear_fwd(oracle.column_shard(X, p, i), oracle.row_shard(W, p, i),
+                                      b if i == owner else None) for i in range(p))
+        assert oracle.rel_fro(s, full) <= 1e-13
+    # adding it on every rank counts it p times
+    s_all = sum(oracle.row_linear_fwd(oracle.column_shard(X, p, i), oracle.row_shard(W, p, i), b) for i in range(p))
+    assert oracle.rel_fro(s_all, full) > 1e-3
+
+
+def test_planted_bias_gelu_dropped_bias_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle.tp_shard, "bias_gelu", lambda Z, b: oracle.gelu(np.asarray(Z, dtype=np.float64)))
+    monkeypatch.setattr(oracle, "bias_gelu", oracle.tp_shard.bias_gelu)
+    assert _bias_gelu_err() > 1e-3
+
+
+def test_planted_bias_gelu_wrong_axis_is_caught(monkeypatch):
+    def wrong_axis(Z, b):
+        Z = np.asarray(Z, dtype=np.float64)
+        b = np.asarray(b, dtype=np.float64)
+        # bias indexed by the row instead of the column (cycled so that it always broadcasts)
+        return oracle.gelu(Z + np.resize(b, Z.shape[0])[:, None])
+
+    monkeypatch.setattr(oracle.tp_shard, "bias_gelu", wrong_axis)
+    monkeypatch.setattr(oracle, "bias_gelu", wrong_axis)
+    assert _bias_gelu_err() > 1e-3
+
+
+def test_planted_row_linear_dropped_bias_is_caught(monkeypatch):
+    orig = oracle.tp_shard.row_linear_fwd
+    monkeypatch.setattr(oracle.tp_shard, "row_linear_fwd", lambda X_i, W_i, b=None: orig(X_i, W_i, None))
+    monkeypatch.setattr(oracle, "row_linear_fwd", oracle.tp_shard.row_linear_fwd)
+    assert _row_linear_bias_err() > 1e-3
+
+
+def test_planted_row_linear_wrong_axis_is_caught(monkeypatch):
+    def wrong_axis(X_i, W_i, b=None):
+        Y = np.asarray(X_i, dtype=np.float64) @ np.asarray(W_i, dtype=np.float64)
+        if b is not None:
+            Y = Y + np.resize(np.asarray(b, dtype=np.float64), Y.shape[0])[:, None]
+        return Y
+
+    monkeypatch.setattr(oracle.tp_shard, "row_linear_fwd", wrong_axis)
+    monkeypatch.setattr(oracle, "row_linear_fwd", wrong_axis)
+    assert _row_linear_bias_err() > 1e-3
