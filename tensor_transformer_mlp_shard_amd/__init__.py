@@ -42,11 +42,15 @@ def _dtype_code(t: torch.Tensor) -> int:
     return _DT[t.dtype]
 
 
+def _require_gpu(name, t):
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+
+
 def _check(name, t, shape, dtype, device):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on a GPU device")
+    _require_gpu(name, t)
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if tuple(t.shape) != tuple(shape):
@@ -55,6 +59,20 @@ def _check(name, t, shape, dtype, device):
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _out(out, key, shape, dtype, device):
+    """out[key] checked like an input (shape, dtype, device, contiguity), or a
+    new tensor when the caller gave none."""
+    t = out.get(key)
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _check(f"out[{key}]", t, shape, dtype, device)
+    return t
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
 
 
 def _ptr(t):
@@ -72,8 +90,9 @@ def workspace_size(op: int, T: int, d_in: int, d_out: int, tp_size: int, dtype: 
 def _workspace(op, T, d_in, d_out, tp_size, dtype, device, given):
     need = workspace_size(op, T, d_in, d_out, tp_size, dtype)
     if given is not None:
-        if given.device != device or given.numel() * given.element_size() < need:
-            raise ValueError(f"workspace needs {need} bytes on {device}")
+        if (given.device != device or not given.is_contiguous()
+                or given.numel() * given.element_size() < need):
+            raise ValueError(f"workspace needs {need} contiguous bytes on {device}")
         return given
     return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
 
@@ -130,15 +149,9 @@ def mlp_shard_fwd(x, a_i, b1_i, b_i, *, tp_size: int, save_z: bool = True, out=N
     if b1_i is not None:
         _check("b1_i", b1_i, (f,), dt, dev)
     out = out or {}
-    z = out.get("Z") if save_z else None
-    if save_z and z is None:
-        z = torch.empty((T, f), dtype=dt, device=dev)
-    hh = out.get("H")
-    if hh is None:
-        hh = torch.empty((T, f), dtype=dt, device=dev)
-    y = out.get("Y")
-    if y is None:
-        y = torch.empty((T, h), dtype=dt, device=dev)
+    z = _out(out, "Z", (T, f), dt, dev) if save_z else None
+    hh = _out(out, "H", (T, f), dt, dev)
+    y = _out(out, "Y", (T, h), dt, dev)
     st = _native.lib().tp_mlp_shard_fwd(_ptr(x), _ptr(a_i), _ptr(b1_i), _ptr(b_i), _ptr(z), _ptr(hh), _ptr(y),
                                         T, h, f * tp_size, tp_size, _dtype_code(x), _stream(dev))
     _native.check(st, "tp_mlp_shard_fwd")
@@ -193,14 +206,14 @@ def mlp_shard_bwd(x, a_i, b_i, z_i, h_i, dy, *, tp_size: int, want_db1: bool = T
         ws = _workspace(_native.TP_OP_MLP_SHARD_BWD_RECOMPUTE, T, h, f * tp_size, tp_size, dt, dev, workspace)
         st = _native.lib().tp_mlp_shard_bwd_recompute(
             _ptr(x), _ptr(a_i), _ptr(b1_i), _ptr(b_i), _ptr(z_i), _ptr(dy), _ptr(dX), _ptr(dA), _ptr(db1),
-            _ptr(dB), _ptr(db2), _ptr(ws), ws.numel(), int(accumulate), T, h, f * tp_size, tp_size,
+            _ptr(dB), _ptr(db2), _ptr(ws), _nbytes(ws), int(accumulate), T, h, f * tp_size, tp_size,
             _dtype_code(x), _stream(dev))
         _native.check(st, "tp_mlp_shard_bwd_recompute")
     else:
         ws = _workspace(_native.TP_OP_MLP_SHARD_BWD, T, h, f * tp_size, tp_size, dt, dev, workspace)
         st = _native.lib().tp_mlp_shard_bwd(
             _ptr(x), _ptr(a_i), _ptr(b_i), _ptr(z_i), _ptr(h_i), _ptr(dy), _ptr(dX), _ptr(dA), _ptr(db1),
-            _ptr(dB), _ptr(db2), _ptr(ws), ws.numel(), int(accumulate), T, h, f * tp_size, tp_size,
+            _ptr(dB), _ptr(db2), _ptr(ws), _nbytes(ws), int(accumulate), T, h, f * tp_size, tp_size,
             _dtype_code(x), _stream(dev))
         _native.check(st, "tp_mlp_shard_bwd")
     return {"dX": dX, "dA": dA, "db1": db1, "dB": dB, "db2": db2}
@@ -227,7 +240,7 @@ def _linear_bwd(fn_name, op, x, w, dy, T, K, N, tp_size, dx_shape, want_db, accu
     db = get("db", (dy.shape[1],), torch.float32) if want_db else None
     ws = _workspace(op, T, K, N, tp_size, dt, dev, workspace) if want_db else None
     fn = getattr(_native.lib(), fn_name)
-    st = fn(_ptr(x), _ptr(w), _ptr(dy), _ptr(dX), _ptr(dW), _ptr(db), _ptr(ws), 0 if ws is None else ws.numel(),
+    st = fn(_ptr(x), _ptr(w), _ptr(dy), _ptr(dX), _ptr(dW), _ptr(db), _ptr(ws), 0 if ws is None else _nbytes(ws),
             int(accumulate), T, K, N, tp_size, _dtype_code(x), _stream(dev))
     _native.check(st, fn_name)
     return {"dX": dX, "dW": dW, "db": db}
@@ -264,9 +277,11 @@ def bias_grad(dy, *, accumulate_into=None, workspace=None):
     T, N = dy.shape
     dev = dy.device
     _check("dy", dy, (T, N), dy.dtype, dev)
+    if accumulate_into is not None:
+        _check("accumulate_into", accumulate_into, (N,), torch.float32, dev)
     db = accumulate_into if accumulate_into is not None else torch.empty((N,), dtype=torch.float32, device=dev)
     ws = _workspace(_native.TP_OP_BIAS_GRAD, T, N, 0, 1, dy.dtype, dev, workspace)
-    st = _native.lib().tp_bias_grad(_ptr(dy), _ptr(db), _ptr(ws), ws.numel(), int(accumulate_into is not None),
+    st = _native.lib().tp_bias_grad(_ptr(dy), _ptr(db), _ptr(ws), _nbytes(ws), int(accumulate_into is not None),
                                     T, N, _dtype_code(dy), _stream(dev))
     _native.check(st, "tp_bias_grad")
     return db
@@ -313,16 +328,9 @@ def attention_bwd(qkv, o, lse, dout, *, seq: int, heads: int, head_dim: int, tp_
     _check("dout", dout, (T, w), torch.bfloat16, dev)
     dq = out if out is not None else torch.empty((T, 3 * w), dtype=torch.bfloat16, device=dev)
     _check("out", dq, (T, 3 * w), torch.bfloat16, dev)
-    need = int(_native.lib().tp_workspace_size(_native.TP_OP_ATTENTION_BWD, T, heads, head_dim, tp_size,
-                                               _native.TP_BF16))
-    if workspace is not None:
-        if workspace.device != dev or workspace.numel() * workspace.element_size() < need:
-            raise ValueError(f"workspace needs {need} bytes on {dev}")
-        ws = workspace
-    else:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    ws = _workspace(_native.TP_OP_ATTENTION_BWD, T, heads, head_dim, tp_size, torch.bfloat16, dev, workspace)
     st = _native.lib().tp_attention_bwd(_ptr(qkv), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(ws),
-                                        ws.numel() * ws.element_size(), T, seq, heads, head_dim, tp_size,
+                                        _nbytes(ws), T, seq, heads, head_dim, tp_size,
                                         int(causal), _native.TP_BF16, _stream(dev))
     _native.check(st, "tp_attention_bwd")
     return dq
@@ -365,12 +373,12 @@ def layernorm_bwd(x, gamma, mean, rstd, dy, *, want_dbeta: bool = True, accumula
         _check(f"out[{k}]", t, shape, dtype, dev)
         return t
 
-    dX = out.get("dX") if out.get("dX") is not None else torch.empty_like(x)
+    dX = _out(out, "dX", (rows, h), dt, dev)
     dg = get("dgamma", (h,), torch.float32)
     db = get("dbeta", (h,), torch.float32) if want_dbeta else None
     ws = _workspace(_native.TP_OP_LAYERNORM_BWD, rows, h, 0, 1, dt, dev, workspace)
     st = _native.lib().tp_layernorm_bwd(_ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dy), _ptr(dX), _ptr(dg),
-                                        _ptr(db), _ptr(ws), ws.numel(), int(accumulate), rows, h, _dtype_code(x),
+                                        _ptr(db), _ptr(ws), _nbytes(ws), int(accumulate), rows, h, _dtype_code(x),
                                         _stream(dev))
     _native.check(st, "tp_layernorm_bwd")
     return {"dX": dX, "dgamma": dg, "dbeta": db}
@@ -399,11 +407,14 @@ def bias_dropout_add_bwd(dout, *, p: float, seed: int, offset: int = 0, want_db:
     dev, dt = dout.device, dout.dtype
     _check("dout", dout, (rows, h), dt, dev)
     dY = out if out is not None else torch.empty_like(dout)
+    _check("out", dY, (rows, h), dt, dev)
+    if accumulate_into is not None:
+        _check("accumulate_into", accumulate_into, (h,), torch.float32, dev)
     db = accumulate_into if accumulate_into is not None else (
         torch.empty((h,), dtype=torch.float32, device=dev) if want_db else None)
     ws = _workspace(_native.TP_OP_BIAS_DROPOUT_ADD_BWD, rows, h, 0, 1, dt, dev, workspace) if db is not None else None
     st = _native.lib().tp_bias_dropout_add_bwd(_ptr(dout), _ptr(dY), _ptr(db), _ptr(ws),
-                                               ws.numel() if ws is not None else 0, int(accumulate_into is not None),
+                                               _nbytes(ws) if ws is not None else 0, int(accumulate_into is not None),
                                                rows, h, float(p), int(seed), int(offset), _dtype_code(dout),
                                                _stream(dev))
     _native.check(st, "tp_bias_dropout_add_bwd")

@@ -55,6 +55,26 @@ int check_elems(std::initializer_list<std::pair<int64_t, int64_t>> mats) {
   return TP_OK;
 }
 
+// A launch of `workgroups` workgroups of `threads` work-items each must stay
+// within the 32-bit dispatch size (at most 2^32 - 1 work-items in x); sizes the
+// other limits admit but one launch cannot cover are rejected up front.
+constexpr int64_t kMaxWorkItems = (int64_t(1) << 32) - 1;
+int check_launch(int64_t workgroups, int64_t threads) {
+  return workgroups * threads > kMaxWorkItems ? TP_ERR_DIM : TP_OK;
+}
+// The elementwise passes (bias + GeLU, bias + dropout + residual, dropout
+// backward) run one work-item per 8 elements in 256-wide workgroups.
+int check_elementwise_launch(int64_t elems) { return check_launch((elems / 8 + 255) / 256, 256); }
+
+// Every GEMM launch (M x N outputs) of an entry point, for the dispatch size.
+int check_gemms(int32_t dtype, std::initializer_list<std::pair<int64_t, int64_t>> mn) {
+  for (const auto& p : mn) {
+    const int64_t w = dtype == TP_FP32 ? gemm_f32_work_items(p.first, p.second) : gemm16_work_items(p.first, p.second);
+    if (w > kMaxWorkItems) return TP_ERR_DIM;
+  }
+  return TP_OK;
+}
+
 int check_feature(std::initializer_list<int64_t> dims) {
   for (int64_t d : dims) {
     if (d > kMaxFeature) return TP_ERR_DIM;
@@ -160,8 +180,8 @@ int check_attention(int64_t T, int64_t seq, int64_t heads, int64_t head_dim, int
   if (tp_size < 1 || heads % tp_size != 0) return TP_ERR_TP_DIVISIBILITY;
   const int64_t hl = heads / tp_size;
   if (3 * hl * head_dim > kMaxFeature) return TP_ERR_DIM;
-  const int64_t workgroups = (seq + 127) / 128 * (T / seq) * hl;  // one per 128 queries of a (sequence, head)
-  if (workgroups > 0x7fffffff) return TP_ERR_DIM;
+  // one workgroup of kAttnThreads per 128 queries (or keys) of a (sequence, head)
+  TP_TRY(check_launch((seq + 127) / 128 * (T / seq) * hl, kAttnThreads));
   p.T = T;
   p.S = (int)seq;
   p.Hl = (int)hl;
@@ -289,6 +309,7 @@ int tp_column_linear(const void* X, const void* W_i, const void* b_i, void* Y_i,
   const int64_t n = N / tp_size;
   TP_TRY(check_feature({K, n}));
   TP_TRY(check_elems({{T, K}, {K, n}, {T, n}}));
+  TP_TRY(check_gemms(dtype, {{T, n}}));
   TP_TRY(check_ptrs_aligned({X, W_i, b_i, Y_i, Z_i}));
   const int64_t es = elsize(dtype);
   TP_TRY(check_alias({{X, T * K * es}, {W_i, K * n * es}, {b_i, n * es}},
@@ -311,6 +332,7 @@ int tp_row_linear(const void* X_i, const void* W_i, const void* b, void* Y_i, in
   const int64_t k = K / tp_size;
   TP_TRY(check_feature({k, N}));
   TP_TRY(check_elems({{T, k}, {k, N}, {T, N}}));
+  TP_TRY(check_gemms(dtype, {{T, N}}));
   TP_TRY(check_ptrs_aligned({X_i, W_i, b, Y_i}));
   const int64_t es = elsize(dtype);
   TP_TRY(check_alias({{X_i, T * k * es}, {W_i, k * N * es}, {b, N * es}}, {{Y_i, T * N * es}}));
@@ -329,6 +351,7 @@ int tp_mlp_shard_fwd(const void* X, const void* A_i, const void* b1_i, const voi
   const int64_t f = F / tp_size;
   TP_TRY(check_feature({h, f}));
   TP_TRY(check_elems({{T, h}, {h, f}, {T, f}}));
+  TP_TRY(check_gemms(dtype, {{T, f}, {T, h}}));
   TP_TRY(check_ptrs_aligned({X, A_i, b1_i, B_i, Z_i, H_i, Y_i}));
   const int64_t es = elsize(dtype);
   TP_TRY(check_alias({{X, T * h * es}, {A_i, h * f * es}, {b1_i, f * es}, {B_i, f * h * es}},
@@ -383,6 +406,7 @@ int tp_mlp_shard_bwd(const void* X, const void* A_i, const void* B_i, const void
   const int64_t f = F / tp_size;
   TP_TRY(check_feature({h, f}));
   TP_TRY(check_elems({{T, h}, {h, f}, {T, f}}));
+  TP_TRY(check_gemms(dtype, {{T, f}, {f, h}, {h, f}, {T, h}}));
   TP_TRY(check_ptrs_aligned({X, A_i, B_i, Z_i, H_i, dY, dX_i, dA_i, db1_i, dB_i, db2, workspace}));
   const size_t need = tp_workspace_size(TP_OP_MLP_SHARD_BWD, T, h, F, tp_size, dtype);
   if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
@@ -409,6 +433,8 @@ int tp_mlp_shard_bwd_recompute(const void* X, const void* A_i, const void* b1_i,
   const int64_t f = F / tp_size;
   TP_TRY(check_feature({h, f}));
   TP_TRY(check_elems({{T, h}, {h, f}, {T, f}}));
+  TP_TRY(check_gemms(dtype, {{T, f}, {f, h}, {h, f}, {T, h}}));
+  if (Z_i) TP_TRY(check_elementwise_launch(T * f));   // H = GeLU(Z) pass
   TP_TRY(check_ptrs_aligned({X, A_i, b1_i, B_i, Z_i, dY, dX_i, dA_i, db1_i, dB_i, db2, workspace}));
   const size_t need = tp_workspace_size(TP_OP_MLP_SHARD_BWD_RECOMPUTE, T, h, F, tp_size, dtype);
   if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
@@ -452,6 +478,7 @@ int tp_column_linear_bwd(const void* X, const void* W_i, const void* dY_i, void*
   const int64_t n = N / tp_size;
   TP_TRY(check_feature({K, n}));
   TP_TRY(check_elems({{T, K}, {K, n}, {T, n}}));
+  TP_TRY(check_gemms(dtype, {{T, K}, {K, n}}));
   TP_TRY(check_ptrs_aligned({X, W_i, dY_i, dX_partial, dW_i, db_i, workspace}));
   const size_t need = db_i ? tp_workspace_size(TP_OP_COLUMN_LINEAR_BWD, T, K, N, tp_size, dtype) : 0;
   if (db_i && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
@@ -483,6 +510,7 @@ int tp_row_linear_bwd(const void* X_i, const void* W_i, const void* dY, void* dX
   const int64_t k = K / tp_size;
   TP_TRY(check_feature({k, N}));
   TP_TRY(check_elems({{T, k}, {k, N}, {T, N}}));
+  TP_TRY(check_gemms(dtype, {{T, k}, {k, N}}));
   TP_TRY(check_ptrs_aligned({X_i, W_i, dY, dX_i, dW_i, db, workspace}));
   const size_t need = db ? tp_workspace_size(TP_OP_ROW_LINEAR_BWD, T, K, N, tp_size, dtype) : 0;
   if (db && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
@@ -524,6 +552,7 @@ int tp_bias_gelu(const void* Z, const void* b, void* H, int64_t T, int64_t N, in
   TP_TRY(check_dims({T, N}));
   TP_TRY(check_feature({N}));
   TP_TRY(check_elems({{T, N}}));
+  TP_TRY(check_elementwise_launch(T * N));
   TP_TRY(check_ptrs_aligned({Z, b, H}));
   const int64_t es = elsize(dtype);
   TP_TRY(check_alias({{Z, T * N * es}, {b, N * es}}, {{H, T * N * es}}));
@@ -584,6 +613,7 @@ int tp_layernorm_fwd(const void* X, const void* gamma, const void* beta, void* Y
   if ((mean == nullptr) != (rstd == nullptr)) return TP_ERR_ARG;
   if (!(eps >= 0.0f) || !std::isfinite(eps)) return TP_ERR_ARG;
   TP_TRY(check_rows_h(rows, h));
+  TP_TRY(check_launch(rows, layernorm_fwd_threads()));   // one workgroup per row
   TP_TRY(check_ptrs_aligned({X, gamma, beta, Y, mean, rstd}));
   const int64_t es = elsize(dtype);
   TP_TRY(check_alias({{X, rows * h * es}, {gamma, h * es}, {beta, beta ? h * es : 0}},
@@ -619,6 +649,7 @@ int tp_bias_dropout_add_fwd(const void* Y, const void* b, const void* residual, 
   uint64_t thr;
   float scale;
   TP_TRY(dropout_params(p_drop, offset, thr, scale));
+  TP_TRY(check_elementwise_launch(rows * h));
   TP_TRY(check_ptrs_aligned({Y, b, residual, out}));
   const int64_t es = elsize(dtype);
   TP_TRY(check_alias({{Y, rows * h * es}, {b, b ? h * es : 0}, {residual, rows * h * es}}, {{out, rows * h * es}}));
@@ -637,6 +668,7 @@ int tp_bias_dropout_add_bwd(const void* dOut, void* dY, float* db, void* workspa
   uint64_t thr;
   float scale;
   TP_TRY(dropout_params(p_drop, offset, thr, scale));
+  TP_TRY(check_elementwise_launch(rows * h));
   TP_TRY(check_ptrs_aligned({dOut, dY, db, workspace}));
   const size_t need = db ? tp_workspace_size(TP_OP_BIAS_DROPOUT_ADD_BWD, rows, h, 0, 1, dtype) : 0;
   if (db && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;

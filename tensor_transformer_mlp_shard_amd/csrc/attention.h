@@ -5,6 +5,9 @@
 
 namespace tps {
 
+// Work-items per workgroup of every attention kernel.
+constexpr int kAttnThreads = 256;
+
 // One rank's attention problem.  qkv is [T x 3*Hl*D] bf16 (columns [Q | K | V],
 // head-major inside each block), T = B * S tokens in sequences of S.
 struct AttnProblem {

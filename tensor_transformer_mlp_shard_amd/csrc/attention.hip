@@ -37,6 +37,7 @@ constexpr int QW = 32;           // queries per wave
 constexpr int BQ = AW * QW;      // queries per workgroup
 constexpr int BKEYS = 64;        // keys per LDS block
 constexpr int NT = AW * 64;      // threads per workgroup
+static_assert(NT == kAttnThreads, "the launch-size check assumes kAttnThreads work-items per workgroup");
 
 template <int D>
 struct Shape {

@@ -43,6 +43,11 @@ hipError_t gemm_bf16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi,
 hipError_t gemm_f16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s);
 hipError_t gemm_f32(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s);
 
+// Work-items of the launch gemm_bf16 / gemm_f16 (resp. gemm_f32) makes for an
+// M x N product: every launch must stay within the 32-bit dispatch size.
+int64_t gemm16_work_items(int64_t M, int64_t N);
+int64_t gemm_f32_work_items(int64_t M, int64_t N);
+
 // Rows of GemmArgs::colsum written by the 16-bit GEMM for an M x N product.
 int gemm16_colsum_rows(int M, int N);
 

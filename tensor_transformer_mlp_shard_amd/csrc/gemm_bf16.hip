@@ -737,6 +737,19 @@ hipError_t gemm_f16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, 
   return gemm16<f16>(g, a_kcontig, b_kcontig, epi, s);
 }
 
+int64_t gemm16_work_items(int64_t M, int64_t N) {
+  const TileChoice t = choose_tile((int)M, (int)N);
+  int64_t threads = T128x128::NT;
+  if (t.bm == 256 && t.bn == 384) threads = T256x384::NT;
+  else if (t.bm == 384 && t.bn == 256) threads = T384x256::NT;
+  else if (t.bm == 192 && t.bn == 384) threads = T192x384::NT;
+  else if (t.bm == 256 && t.bn == 192) threads = T256x192::NT;
+  else if (t.bm == 192 && t.bn == 256) threads = T192x256::NT;
+  else if (t.bm == 256 && t.bn == 128) threads = T256x128::NT;
+  else if (t.bm == 128 && t.bn == 256) threads = T128x256::NT;
+  return (M + t.bm - 1) / t.bm * ((N + t.bn - 1) / t.bn) * threads;
+}
+
 int gemm16_colsum_rows(int M, int N) {
   const TileChoice t = choose_tile(M, N);
   if (t.bm * t.bn >= 256 * 384) return 0;   // that tile does not carry the column sums (Cfg::CSUM)

@@ -29,7 +29,9 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
   const float* __restrict__ B = (const float*)g.B;
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
-  const int m0 = blockIdx.y * TB, n0 = blockIdx.x * TB;
+  // one flat grid over the tiles (a second grid dimension would cap M at 65536 tiles)
+  const int tiles_n = (g.N + TB - 1) / TB;
+  const int m0 = (int)(blockIdx.x / tiles_n) * TB, n0 = (int)(blockIdx.x % tiles_n) * TB;
 
   float acc[4][4];
 #pragma unroll
@@ -97,12 +99,14 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
 
 template <bool AK, bool BKC, int EPI>
 hipError_t launch(const GemmArgs& g, hipStream_t s) {
-  const dim3 grid((g.N + TB - 1) / TB, (g.M + TB - 1) / TB);
+  const dim3 grid((unsigned)(((int64_t)g.N + TB - 1) / TB * (((int64_t)g.M + TB - 1) / TB)));
   hipLaunchKernelGGL((gemm_f32_kernel<AK, BKC, EPI>), grid, dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
 }  // namespace
+
+int64_t gemm_f32_work_items(int64_t M, int64_t N) { return (M + TB - 1) / TB * ((N + TB - 1) / TB) * 256; }
 
 hipError_t gemm_f32(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s) {
   LaunchInfo info;

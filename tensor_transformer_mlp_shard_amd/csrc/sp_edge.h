@@ -6,6 +6,9 @@
 
 namespace tps {
 
+// Work-items of the LayerNorm forward's one workgroup per row.
+int layernorm_fwd_threads();
+
 // Workgroups (and partial rows of the parameter gradients) of the LayerNorm backward.
 int layernorm_bwd_chunks(int64_t rows);
 

@@ -297,6 +297,8 @@ __global__ void __launch_bounds__(256) dropout_bwd_kernel(const void* dOut, void
 
 }  // namespace
 
+int layernorm_fwd_threads() { return LN_T; }
+
 int layernorm_bwd_chunks(int64_t rows) {
   int64_t c = (rows + 3) / 4;   // about 4 rows per workgroup, one workgroup per CU at most
   if (c > 256) c = 256;

@@ -254,3 +254,34 @@ def test_unscale_check_validation(lib):
     assert f(G, 16, ctypes.c_float(float("nan")), F, S) == -9
     assert f(P(0x1000004), 16, ctypes.c_float(0.5), F, S) == -4
     assert f(G, 16, ctypes.c_float(0.5), P(0x1000008), S) == -6        # flag inside the buffer
+
+
+# Addresses far apart, so that no overlap check fires before the size checks.
+FAR = [P((i + 1) << 40) for i in range(12)]
+
+
+def test_launch_size_limits(lib):
+    """Sizes inside the dimension and element limits whose launch would pass
+    the 32-bit dispatch size (2^32 - 1 work-items) are rejected with
+    TP_ERR_DIM before anything is enqueued."""
+    X, W, B, Y, Z, R = FAR[:6]
+    # elementwise passes: one work-item per 8 elements -> T*N = 2^36 needs 2^33
+    assert lib.tp_bias_gelu(X, B, Y, 1 << 20, 1 << 16, 0, S) == -2
+    assert lib.tp_bias_dropout_add_fwd(X, B, R, Y, 1 << 20, 1 << 16, 0.1, 1, 0, 0, S) == -2
+    assert lib.tp_bias_dropout_add_bwd(X, Y, None, None, 0, 0, 1 << 20, 1 << 16, 0.1, 1, 0, 0, S) == -2
+    # LayerNorm forward: one 256-wide workgroup per row -> 2^24 rows need 2^32
+    assert lib.tp_layernorm_fwd(X, W, B, Y, Z, R, 1 << 24, 8, 1e-5, 0, S) == -2
+    # attention: one 256-wide workgroup per 128 queries of a (sequence, head):
+    # 2^18 sequences of 128 tokens x 1024 local heads of 64 -> 2^36 work-items
+    assert lib.tp_attention_fwd(X, Y, Z, 1 << 25, 128, 1024, 64, 1, 1, 0, S) == -2
+    # fp32 GEMM: 64 x 64 tiles of 256 work-items; 2^30 tokens x 64 outputs -> 2^32
+    assert lib.tp_column_linear(X, W, None, Y, None, 1 << 30, 8, 64, 1, 0, 1, S) == -2
+    assert lib.tp_row_linear(X, W, None, Y, 1 << 30, 8, 64, 1, 1, S) == -2
+    assert lib.tp_mlp_shard_fwd(X, W, None, B, None, Z, Y, 1 << 30, 8, 64, 1, 1, S) == -2
+    ws = FAR[11]
+    need = lib.tp_workspace_size(_native.TP_OP_COLUMN_LINEAR_BWD, 1 << 30, 8, 64, 1, 1)
+    assert need > 0
+    assert lib.tp_column_linear_bwd(X, W, B, Y, Z, None, ws, need, 0, 1 << 30, 64, 8, 1, 1, S) == -2
+    assert lib.tp_row_linear_bwd(X, W, B, Y, Z, None, ws, need, 0, 1 << 30, 8, 64, 1, 1, S) == -2
+    assert lib.tp_mlp_shard_bwd(X, W, B, Z, R, FAR[6], FAR[7], FAR[8], None, FAR[9], None, ws, 1 << 62, 0,
+                                1 << 30, 8, 64, 1, 1, S) == -2
