@@ -109,6 +109,70 @@ class Shard:
         self.attn_step()
 
 
+class MLPConfig:
+    """One rank's MLP shard of a workload in the table (rank 0's contiguous
+    column block of A and b1 and row block of B when the unsharded weights are
+    drawn), device-resident, with preallocated outputs and workspace; one step
+    is the forward and the backward (dX, dA, db1, dB, db2)."""
+
+    def __init__(self, device, name: str):
+        import torch
+
+        import tensor_transformer_mlp_shard_amd as tps
+        from tensor_transformer_mlp_shard_amd import _native, synth
+
+        self.tps = tps
+        w = synth.WORKLOADS[name]
+        self.w = w
+        d = synth.inputs_for(w)
+        f = w.f
+        if w.full:   # rank 0's shard of the unsharded weights
+            d["A"], d["b1"], d["B"] = d["A"][:, :f].contiguous(), d["b1"][:f].contiguous(), d["B"][:f].contiguous()
+        self.X, self.A, self.b1, self.B, self.dY = (d[k].to(device) for k in ("X", "A", "b1", "B", "dY"))
+        dt = self.X.dtype
+        e = lambda shape, t: torch.empty(shape, dtype=t, device=device)  # noqa: E731
+        T, h = w.T, w.h
+        self.fwd_out = {"Z": e((T, f), dt), "H": e((T, f), dt), "Y": e((T, h), dt)}
+        fp = torch.float32
+        self.bwd_out = {"dX": e((T, h), dt), "dA": e((h, f), fp), "dB": e((f, h), fp), "db1": e((f,), fp),
+                        "db2": e((h,), fp)}
+        self.ws = e((tps.workspace_size(_native.TP_OP_MLP_SHARD_BWD, T, h, w.F, w.tp, dt),), torch.uint8)
+        self.flops = _flops_mlp(T, h, f)
+
+    def step(self):
+        o = self.fwd_out
+        self.tps.mlp_shard_fwd(self.X, self.A, self.b1, self.B, tp_size=self.w.tp, out=o)
+        self.tps.mlp_shard_bwd(self.X, self.A, self.B, o["Z"], o["H"], self.dY, tp_size=self.w.tp, want_db2=True,
+                               out=self.bwd_out, workspace=self.ws)
+
+
+def measure_configs(torch, device, shard, steps, warmup):
+    """Forward + backward of every workload in the table, each on its own:
+    the tiny fp32 check-path shard, the GPT h=1024 TP=2 and 1.3B TP=1 MLP
+    shards, and the two 175B TP=8 parts of the step (MLP shard, attention
+    linears).  TFLOP/s and % of the bf16 peak from the median step."""
+    out = {}
+    for key, name in (("tiny_tp2_fp32", "tiny_tp2_fp32"), ("gpt_h1024_tp2_mlp", "gpt_h1024_tp2"),
+                      ("gpt_1p3b_tp1_mlp", "gpt_1p3b_tp1")):
+        c = MLPConfig(device, name)
+        st = time_stats(torch, c.step, steps, warmup)
+        w = c.w
+        out[key] = {"workload": f"{w.note}: X[{w.T}x{w.h}], A_i[{w.h}x{w.f}], B_i[{w.f}x{w.h}], fwd+bwd",
+                    "dtype": w.dtype, "flop": c.flops, **_rates(c.flops, st)}
+        if w.dtype == "fp32":
+            out[key]["note"] = "fp32 check path (FMA kernel, not the matrix cores): latency-bound, parity only"
+        del c
+    st = time_stats(torch, shard.mlp_step, steps, warmup)
+    out["gpt175b_mlp_tp8"] = {"workload": "175B MLP shard at TP=8: X[2048x12288], A_i[12288x6144], "
+                                          "B_i[6144x12288], fwd+bwd", "dtype": "bf16", "flop": shard.flops_mlp,
+                              **_rates(shard.flops_mlp, st)}
+    st = time_stats(torch, shard.attn_step, steps, warmup)
+    out["gpt175b_attn_tp8"] = {"workload": "175B attention linears at TP=8, T=8192: QKV 12288->4608 (bias), "
+                                           "out-proj 1536->12288, fwd+bwd", "dtype": "bf16",
+                               "flop": shard.flops_attn, **_rates(shard.flops_attn, st)}
+    return out
+
+
 class CoreAttention:
     """Core attention on the rank's local heads, 175B shape at TP=8: 4 sequences
     of 2048 tokens, 12 local heads of 128, causal; forward and backward."""
@@ -184,9 +248,7 @@ def measure_core_attention(torch, device, steps, warmup):
            "flop_fwd": ca.flops_fwd, "flop_bwd": ca.flops_bwd}
     for name, fn, fl in (("fwd", ca.fwd, ca.flops_fwd), ("bwd", ca.bwd, ca.flops_bwd),
                          ("fwd_bwd", ca.step, ca.flops_fwd + ca.flops_bwd)):
-        ms, _ = time_steps(torch, fn, steps, warmup)
-        out[name] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
-                     "pct_peak": round(100 * fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2)}
+        out[name] = _rates(fl, time_stats(torch, fn, steps, warmup))
     ca.tps.trace_start(4096)
     for _ in range(steps):
         ca.step()
@@ -269,11 +331,14 @@ def measure_side(torch, device, steps, warmup):
             "ms_per_step": round(ms, 4), "kernels": kern}
 
 
-def measure_recompute(torch, shard, steps, warmup):
+def measure_recompute(torch, shard, steps, warmup, pairs=6):
     """MLP shard fwd+bwd with all activations saved against the two selective
     recompute forms: Z kept (H recomputed by an elementwise GeLU) and nothing
-    kept (Z and H recomputed by the fc1 GEMM).  Reports the time overhead and
-    the activation bytes each form keeps between forward and backward."""
+    kept (Z and H recomputed by the fc1 GEMM).  The three forms run in turn,
+    `pairs` rounds of `steps` steps each, so that each overhead is a paired
+    difference against the baseline round next to it; reported as the median
+    and the range over the rounds, with the activation bytes each form keeps
+    between forward and backward."""
     tps = shard.tps
     wm = shard.wm
     p = wm.tp
@@ -291,29 +356,63 @@ def measure_recompute(torch, shard, steps, warmup):
         tps.mlp_shard_bwd(shard.X, shard.A, shard.B, None, None, shard.dY, tp_size=p, want_db2=True,
                           out=shard.bwd_out, workspace=ws, recompute=True, b1_i=shard.b1)
 
+    forms = (("saved_Z_and_H", shard.mlp_step), ("saved_Z_recompute_H", keep_z),
+             ("saved_none_recompute_fc1", keep_none))
+    for _, fn in forms:
+        for _ in range(warmup):
+            fn()
+    ms = {name: [] for name, _ in forms}
+    for _ in range(pairs):
+        for name, fn in forms:
+            ms[name].append(time_stats(torch, fn, steps, 2)["mean"])
+    base = ms["saved_Z_and_H"]
     act = wm.T * wm.f * 2
-    base, _ = time_steps(torch, shard.mlp_step, steps, warmup)
-    out = {"saved_Z_and_H": {"ms": round(base, 4), "kept_bytes": 2 * act}}
-    for name, fn, kept in (("saved_Z_recompute_H", keep_z, act), ("saved_none_recompute_fc1", keep_none, 0)):
-        ms, _ = time_steps(torch, fn, steps, warmup)
-        out[name] = {"ms": round(ms, 4), "kept_bytes": kept, "overhead_pct": round(100 * (ms / base - 1), 2)}
+    med = lambda v: sorted(v)[len(v) // 2] if len(v) % 2 else 0.5 * sum(sorted(v)[len(v) // 2 - 1:len(v) // 2 + 1])  # noqa: E731,E501
+    out = {"rounds": pairs, "steps_per_round": steps,
+           "saved_Z_and_H": {"ms_median": round(med(base), 4), "ms_range": [round(min(base), 4), round(max(base), 4)],
+                             "kept_bytes": 2 * act}}
+    for name, kept in (("saved_Z_recompute_H", act), ("saved_none_recompute_fc1", 0)):
+        ov = [100.0 * (a / b - 1.0) for a, b in zip(ms[name], base)]
+        out[name] = {"ms_median": round(med(ms[name]), 4), "kept_bytes": kept,
+                     "overhead_pct_median": round(med(ov), 2),
+                     "overhead_pct_range": [round(min(ov), 2), round(max(ov), 2)]}
     return out
 
 
-def time_steps(torch, fn, steps, warmup):
+def time_stats(torch, fn, steps, warmup):
+    """Run `warmup` untimed calls, then exactly `steps` timed ones between two
+    synchronisations.  HIP events on the current stream bracket every call, so
+    besides the mean over the whole region (total time / steps) the median and
+    minimum per-call times are known.  Returns dict(mean, median, min, wall)
+    in ms per call."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    start.record()
-    for _ in range(steps):
+    ev[0].record()
+    for i in range(steps):
         fn()
-    stop.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return start.elapsed_time(stop) / steps, wall * 1e3 / steps
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    mid = steps // 2
+    median = per[mid] if steps % 2 else 0.5 * (per[mid - 1] + per[mid])
+    return {"mean": ev[0].elapsed_time(ev[steps]) / steps, "median": median, "min": per[0],
+            "wall": wall * 1e3 / steps}
+
+
+def time_steps(torch, fn, steps, warmup):
+    st = time_stats(torch, fn, steps, warmup)
+    return st["mean"], st["wall"]
+
+
+def _rates(flop, st):
+    """TFLOP/s and % of the bf16 peak from the median, plus mean / median / min ms."""
+    tf = flop / (st["median"] * 1e-3) / 1e12
+    return {"ms_mean": round(st["mean"], 4), "ms_median": round(st["median"], 4), "ms_min": round(st["min"], 4),
+            "tflops": round(tf, 1), "pct_peak": round(100 * tf / BF16_PEAK_TFLOPS, 2)}
 
 
 def roofline_from_trace(tps, torch, fn, steps):
@@ -438,14 +537,12 @@ def main():
     fn = {"all": shard.step, "mlp": shard.mlp_step, "attn": shard.attn_step}[args.part]
     flops = {"all": shard.flops_mlp + shard.flops_attn, "mlp": shard.flops_mlp, "attn": shard.flops_attn}[args.part]
 
-    ms, wall_ms = time_steps(torch, fn, args.steps, args.warmup)
+    st = time_stats(torch, fn, args.steps, args.warmup)
+    ms, wall_ms = st["mean"], st["wall"]
     value = flops / (ms * 1e-3) / 1e12
-    parts = {}
+    configs = {}
     if args.part == "all":
-        for name, f_, fl in (("mlp", shard.mlp_step, shard.flops_mlp), ("attn", shard.attn_step, shard.flops_attn)):
-            pms, _ = time_steps(torch, f_, args.steps, 2)
-            parts[name] = {"ms": round(pms, 4), "tflops": round(fl / (pms * 1e-3) / 1e12, 1),
-                           "pct_peak": round(100 * fl / (pms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2)}
+        configs = measure_configs(torch, device, shard, min(args.steps, 50), min(args.warmup, 20))
 
     dom, kernels = roofline_from_trace(shard.tps, torch, fn, args.steps)
     avg_ms = dom["total_ms"] / dom["launches"]
@@ -479,6 +576,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(st["median"], 4),
+        "ms_per_step_min": round(st["min"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -493,7 +592,7 @@ def main():
         },
         "pct_of_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
         "wall_ms_per_step": round(wall_ms, 4),
-        "parts": parts,
+        "configs": configs,
         "roofline": roof,
         "mfma_probe": {"tflops": round(probe["tflops"], 1), "clock_ghz": round(probe["clock_ghz_mean"], 3),
                        "mfma_busy": round(probe["mfma_busy"], 3), "compute_units": probe["compute_units"],
