@@ -79,7 +79,9 @@ enum {
   TP_ERR_ALIAS = -6,            /* an output overlaps an input or another output */
   TP_ERR_WORKSPACE = -7,        /* workspace NULL or smaller than tp_workspace_size() */
   TP_ERR_HIP = -8,              /* a HIP runtime call or kernel launch failed */
-  TP_ERR_ARG = -9               /* other invalid argument (flag value, unexpected pointer) */
+  TP_ERR_ARG = -9,              /* other invalid argument (flag value, unexpected pointer) */
+  TP_ERR_SCRATCH = -10          /* more scratch needed than tp_noalloc_scratch_bytes() (the
+                                   allocation-free entry point only) */
 };
 
 /* Operation codes for tp_workspace_size(). */
@@ -155,6 +157,32 @@ int tp_mlp_shard_bwd(const void* X, const void* A_i, const void* B_i, const void
                      float* dB_i, float* db2, void* workspace, size_t workspace_bytes,
                      int32_t accumulate, int64_t T, int64_t h, int64_t F, int32_t tp_size,
                      int32_t dtype, void* stream);
+
+/*
+ * MLP shard backward that allocates nothing and takes no workspace, for callers
+ * that cannot allocate device memory or hand out scratch: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, outputs, kernels and results (bitwise) as tp_mlp_shard_bwd,
+ * without workspace / workspace_bytes: the scratch (dZ, then the bias-gradient
+ * partials) lives in a static device array of tp_noalloc_scratch_bytes()
+ * (96 MiB) that the library holds on each GPU it runs on until the process
+ * ends.  A problem whose scratch, tp_workspace_size(TP_OP_MLP_SHARD_BWD, ...),
+ * exceeds that size is rejected with TP_ERR_SCRATCH before anything is
+ * enqueued (the 175B TP=8 shard needs 26 MiB, the 1.3B TP=1 MLP 64.3 MiB in
+ * 16-bit storage).  No hipMalloc, hipFree or allocating library routine is
+ * called; the first call on a GPU looks the array's device address up once.
+ * Every call on a GPU uses that GPU's one array: calls that overlap in time on
+ * one GPU (different streams, or different host threads without ordering)
+ * race on it and must not be issued.  The array keeps the last call's
+ * contents; nothing in it needs to start at zero.
+ */
+int tp_mlp_shard_bwd_noalloc(const void* X, const void* A_i, const void* B_i, const void* Z_i,
+                             const void* H_i, const void* dY, void* dX_i, float* dA_i, float* db1_i,
+                             float* dB_i, float* db2, int32_t accumulate, int64_t T, int64_t h, int64_t F,
+                             int32_t tp_size, int32_t dtype, void* stream);
+
+/* Bytes of the static scratch array of tp_mlp_shard_bwd_noalloc. */
+size_t tp_noalloc_scratch_bytes(void);
 
 /*
  * MLP shard backward with selective activation recompute ([TUT] "融合优化技术"

@@ -26,6 +26,7 @@ __all__ = [
     "row_linear_bwd", "bias_grad", "bias_gelu", "workspace_size", "trace_start", "trace_stop",
     "attention_fwd", "attention_bwd", "layernorm_fwd", "layernorm_bwd", "bias_dropout_add_fwd",
     "bias_dropout_add_bwd", "unscale_check_finite", "mfma_probe", "library_path", "NativeLibraryMissing",
+    "mlp_shard_bwd_noalloc", "noalloc_scratch_bytes",
 ]
 
 _DT = {torch.bfloat16: _native.TP_BF16, torch.float32: _native.TP_FP32, torch.float16: _native.TP_FP16}
@@ -217,6 +218,41 @@ def mlp_shard_bwd(x, a_i, b_i, z_i, h_i, dy, *, tp_size: int, want_db1: bool = T
             _dtype_code(x), _stream(dev))
         _native.check(st, "tp_mlp_shard_bwd")
     return {"dX": dX, "dA": dA, "db1": db1, "dB": dB, "db2": db2}
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the static device scratch of mlp_shard_bwd_noalloc."""
+    return int(_native.lib().tp_noalloc_scratch_bytes())
+
+
+def mlp_shard_bwd_noalloc(x, a_i, b_i, z_i, h_i, dy, *, tp_size: int, out, want_db1: bool = True,
+                          want_db2: bool = False, accumulate: bool = False):
+    """MLP shard backward through tp_mlp_shard_bwd_noalloc: the same results as
+    mlp_shard_bwd with its scratch in the library's static device array, for
+    callers that cannot allocate.  Nothing is allocated here either: ``out``
+    must hold "dX", "dA", "dB" (and "db1" / "db2" when wanted).  Calls that
+    overlap on one GPU race on that array."""
+    T, h = x.shape
+    f = a_i.shape[1]
+    dt = x.dtype
+    dev = x.device
+    for name, t, shp in (("x", x, (T, h)), ("a_i", a_i, (h, f)), ("b_i", b_i, (f, h)), ("z_i", z_i, (T, f)),
+                         ("h_i", h_i, (T, f)), ("dy", dy, (T, h))):
+        _check(name, t, shp, dt, dev)
+    need = [("dX", (T, h), dt), ("dA", (h, f), torch.float32), ("dB", (f, h), torch.float32)]
+    need += [("db1", (f,), torch.float32)] if want_db1 else []
+    need += [("db2", (h,), torch.float32)] if want_db2 else []
+    for k, shp, tdt in need:
+        if out.get(k) is None:
+            raise ValueError(f"mlp_shard_bwd_noalloc allocates nothing: out[{k!r}] is required")
+        _check(f"out[{k}]", out[k], shp, tdt, dev)
+    db1 = out["db1"] if want_db1 else None
+    db2 = out["db2"] if want_db2 else None
+    st = _native.lib().tp_mlp_shard_bwd_noalloc(
+        _ptr(x), _ptr(a_i), _ptr(b_i), _ptr(z_i), _ptr(h_i), _ptr(dy), _ptr(out["dX"]), _ptr(out["dA"]), _ptr(db1),
+        _ptr(out["dB"]), _ptr(db2), int(accumulate), T, h, f * tp_size, tp_size, _dtype_code(x), _stream(dev))
+    _native.check(st, "tp_mlp_shard_bwd_noalloc")
+    return out
 
 
 def _linear_bwd(fn_name, op, x, w, dy, T, K, N, tp_size, dx_shape, want_db, accumulate, out, workspace):

@@ -14,7 +14,7 @@ TP_OP_ATTENTION_BWD, TP_OP_MLP_SHARD_BWD_RECOMPUTE, TP_OP_LAYERNORM_BWD, TP_OP_B
 STATUS = {
     0: "TP_OK", -1: "TP_ERR_NULLPTR", -2: "TP_ERR_DIM", -3: "TP_ERR_TP_DIVISIBILITY",
     -4: "TP_ERR_ALIGNMENT", -5: "TP_ERR_DTYPE", -6: "TP_ERR_ALIAS", -7: "TP_ERR_WORKSPACE",
-    -8: "TP_ERR_HIP", -9: "TP_ERR_ARG",
+    -8: "TP_ERR_HIP", -9: "TP_ERR_ARG", -10: "TP_ERR_SCRATCH",
 }
 
 _p = ctypes.c_void_p
@@ -32,6 +32,9 @@ PROTOTYPES = {
                                 _i64, _i64, _i64, _i32, _i32, _p]),
     "tp_mlp_shard_bwd_recompute": (_i32, [_p, _p, _p, _p, _p, _p, _p, _fp, _fp, _fp, _fp, _p, _sz, _i32,
                                           _i64, _i64, _i64, _i32, _i32, _p]),
+    "tp_mlp_shard_bwd_noalloc": (_i32, [_p, _p, _p, _p, _p, _p, _p, _fp, _fp, _fp, _fp, _i32,
+                                        _i64, _i64, _i64, _i32, _i32, _p]),
+    "tp_noalloc_scratch_bytes": (_sz, []),
     "tp_column_linear_bwd": (_i32, [_p, _p, _p, _p, _fp, _fp, _p, _sz, _i32, _i64, _i64, _i64, _i32, _i32, _p]),
     "tp_row_linear_bwd": (_i32, [_p, _p, _p, _p, _fp, _fp, _p, _sz, _i32, _i64, _i64, _i64, _i32, _i32, _p]),
     "tp_bias_grad": (_i32, [_p, _fp, _p, _sz, _i32, _i64, _i64, _i32, _p]),

@@ -228,6 +228,33 @@ void trace_end(hipStream_t stream, const LaunchInfo& info) {
   }
 }
 
+// Scratch of the allocation-free MLP backward (tp_mlp_shard_bwd_noalloc): a
+// static device array, one instance per GPU, loaded with the code object and
+// held until the process ends.  Host code never uses its name as an address
+// (on the host it names a stand-in object); it uses the device address that
+// hipGetSymbolAddress returns for the current GPU, looked up once per device.
+constexpr size_t kNoallocScratchBytes = size_t(96) << 20;
+__device__ __align__(256) char scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device address of the current GPU's scratch array, or nullptr on a HIP error.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace tps
 
 using namespace tps;
@@ -246,6 +273,7 @@ const char* tp_status_string(int status) {
     case TP_ERR_WORKSPACE: return "workspace missing or too small";
     case TP_ERR_HIP: return "HIP runtime or kernel launch error";
     case TP_ERR_ARG: return "invalid argument";
+    case TP_ERR_SCRATCH: return "the problem needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -394,10 +422,12 @@ static int mlp_bwd_gemms(const void* X, const void* A_i, const void* B_i, const 
   return TP_OK;
 }
 
-int tp_mlp_shard_bwd(const void* X, const void* A_i, const void* B_i, const void* Z_i, const void* H_i,
-                     const void* dY, void* dX_i, float* dA_i, float* db1_i, float* dB_i, float* db2,
-                     void* workspace, size_t workspace_bytes, int32_t accumulate, int64_t T, int64_t h, int64_t F,
-                     int32_t tp_size, int32_t dtype, void* stream) {
+// Argument checks of the MLP backward that do not depend on where its scratch
+// lives; on success *need holds the scratch bytes the call uses.
+static int mlp_bwd_check(const void* X, const void* A_i, const void* B_i, const void* Z_i, const void* H_i,
+                         const void* dY, void* dX_i, float* dA_i, float* db1_i, float* dB_i, float* db2,
+                         int32_t accumulate, int64_t T, int64_t h, int64_t F, int32_t tp_size, int32_t dtype,
+                         size_t* need) {
   TP_TRY(check_dtype(dtype));
   if (accumulate != 0 && accumulate != 1) return TP_ERR_ARG;
   TP_TRY(check_nonnull({X, A_i, B_i, Z_i, H_i, dY, dX_i, dA_i, dB_i}));
@@ -407,18 +437,63 @@ int tp_mlp_shard_bwd(const void* X, const void* A_i, const void* B_i, const void
   TP_TRY(check_feature({h, f}));
   TP_TRY(check_elems({{T, h}, {h, f}, {T, f}}));
   TP_TRY(check_gemms(dtype, {{T, f}, {f, h}, {h, f}, {T, h}}));
-  TP_TRY(check_ptrs_aligned({X, A_i, B_i, Z_i, H_i, dY, dX_i, dA_i, db1_i, dB_i, db2, workspace}));
-  const size_t need = tp_workspace_size(TP_OP_MLP_SHARD_BWD, T, h, F, tp_size, dtype);
-  if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
+  TP_TRY(check_ptrs_aligned({X, A_i, B_i, Z_i, H_i, dY, dX_i, dA_i, db1_i, dB_i, db2}));
+  *need = tp_workspace_size(TP_OP_MLP_SHARD_BWD, T, h, F, tp_size, dtype);
   const int64_t es = elsize(dtype);
   TP_TRY(check_alias({{X, T * h * es}, {A_i, h * f * es}, {B_i, f * h * es}, {Z_i, T * f * es},
                       {H_i, T * f * es}, {dY, T * h * es}},
                      {{dX_i, T * h * es}, {dA_i, h * f * 4}, {db1_i, db1_i ? f * 4 : 0}, {dB_i, f * h * 4},
-                      {db2, db2 ? h * 4 : 0}, {workspace, (int64_t)need}}));
-  char* ws = (char*)workspace;
-  float* part = (float*)(ws + round_up((size_t)T * (size_t)f * es));
+                      {db2, db2 ? h * 4 : 0}}));
+  return TP_OK;
+}
+
+// The MLP backward on validated arguments, with its scratch (dZ, then the
+// column-sum partials) at `ws`.
+static int mlp_bwd_run(const void* X, const void* A_i, const void* B_i, const void* Z_i, const void* H_i,
+                       const void* dY, void* dX_i, float* dA_i, float* db1_i, float* dB_i, float* db2, char* ws,
+                       int32_t accumulate, int64_t T, int64_t h, int64_t F, int32_t tp_size, int32_t dtype,
+                       hipStream_t s) {
+  const int64_t f = F / tp_size;
+  float* part = (float*)(ws + round_up((size_t)T * (size_t)f * elsize(dtype)));
   return mlp_bwd_gemms(X, A_i, B_i, Z_i, H_i, dY, dX_i, dA_i, db1_i, dB_i, db2, ws, part, accumulate, T, h, f,
-                       dtype, (hipStream_t)stream);
+                       dtype, s);
+}
+
+int tp_mlp_shard_bwd(const void* X, const void* A_i, const void* B_i, const void* Z_i, const void* H_i,
+                     const void* dY, void* dX_i, float* dA_i, float* db1_i, float* dB_i, float* db2,
+                     void* workspace, size_t workspace_bytes, int32_t accumulate, int64_t T, int64_t h, int64_t F,
+                     int32_t tp_size, int32_t dtype, void* stream) {
+  size_t need = 0;
+  TP_TRY(mlp_bwd_check(X, A_i, B_i, Z_i, H_i, dY, dX_i, dA_i, db1_i, dB_i, db2, accumulate, T, h, F, tp_size, dtype,
+                       &need));
+  if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
+  TP_TRY(check_ptrs_aligned({workspace}));
+  const int64_t es = elsize(dtype);
+  const int64_t f = F / tp_size;
+  TP_TRY(check_alias({{X, T * h * es}, {A_i, h * f * es}, {B_i, f * h * es}, {Z_i, T * f * es},
+                      {H_i, T * f * es}, {dY, T * h * es}, {dX_i, T * h * es}, {dA_i, h * f * 4},
+                      {db1_i, db1_i ? f * 4 : 0}, {dB_i, f * h * 4}, {db2, db2 ? h * 4 : 0}},
+                     {{workspace, (int64_t)need}}));
+  return mlp_bwd_run(X, A_i, B_i, Z_i, H_i, dY, dX_i, dA_i, db1_i, dB_i, db2, (char*)workspace, accumulate, T, h, F,
+                     tp_size, dtype, (hipStream_t)stream);
+}
+
+size_t tp_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+int tp_mlp_shard_bwd_noalloc(const void* X, const void* A_i, const void* B_i, const void* Z_i, const void* H_i,
+                             const void* dY, void* dX_i, float* dA_i, float* db1_i, float* dB_i, float* db2,
+                             int32_t accumulate, int64_t T, int64_t h, int64_t F, int32_t tp_size, int32_t dtype,
+                             void* stream) {
+  size_t need = 0;
+  TP_TRY(mlp_bwd_check(X, A_i, B_i, Z_i, H_i, dY, dX_i, dA_i, db1_i, dB_i, db2, accumulate, T, h, F, tp_size, dtype,
+                       &need));
+  if (need > kNoallocScratchBytes) return TP_ERR_SCRATCH;
+  // Every scratch byte the backward reads (dZ, the column-sum partials) is
+  // written earlier in the same call, so nothing is cleared.
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return TP_ERR_HIP;
+  return mlp_bwd_run(X, A_i, B_i, Z_i, H_i, dY, dX_i, dA_i, db1_i, dB_i, db2, (char*)ws, accumulate, T, h, F,
+                     tp_size, dtype, (hipStream_t)stream);
 }
 
 int tp_mlp_shard_bwd_recompute(const void* X, const void* A_i, const void* b1_i, const void* B_i, const void* Z_i,

@@ -285,3 +285,17 @@ def test_launch_size_limits(lib):
     assert lib.tp_row_linear_bwd(X, W, B, Y, Z, None, ws, need, 0, 1 << 30, 8, 64, 1, 1, S) == -2
     assert lib.tp_mlp_shard_bwd(X, W, B, Z, R, FAR[6], FAR[7], FAR[8], None, FAR[9], None, ws, 1 << 62, 0,
                                 1 << 30, 8, 64, 1, 1, S) == -2
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch(lib):
+    """tp_mlp_shard_bwd_noalloc checks the problem's scratch against its static
+    array before any HIP call (1.3B TP=1 in fp32 needs 130 MiB of 96)."""
+    cap = lib.tp_noalloc_scratch_bytes()
+    assert cap == 96 << 20
+    need = lib.tp_workspace_size(_native.TP_OP_MLP_SHARD_BWD, 4096, 2048, 8192, 1, 1)
+    assert need > cap
+    X, A, B, Z, H, dY, dX, dA, db1, dB = FAR[:10]
+    assert lib.tp_mlp_shard_bwd_noalloc(X, A, B, Z, H, dY, dX, dA, db1, dB, None, 0, 4096, 2048, 8192, 1, 1, S) == -10
+    # the ordinary checks come first
+    assert lib.tp_mlp_shard_bwd_noalloc(X, A, B, Z, H, dY, dX, dA, db1, dB, None, 2, 4096, 2048, 8192, 1, 1, S) == -9
+    assert lib.tp_mlp_shard_bwd_noalloc(X, A, B, Z, H, dY, X, dA, db1, dB, None, 0, 4096, 2048, 8192, 1, 1, S) == -6
