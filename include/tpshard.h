@@ -191,7 +191,8 @@ size_t tp_noalloc_scratch_bytes(void);
  * Same outputs and conventions as tp_mlp_shard_bwd; the forward's saved
  * activations are replaced by:
  *   Z_i non-NULL: only the pre-activation was kept; H_i = GeLU(Z_i) is
- *                 recomputed by one elementwise pass (H_i need not be kept);
+ *                 recomputed in the epilogue of the dZ GEMM, which reads Z_i
+ *                 for GeLU' anyway (H_i need not be kept; no extra pass);
  *   Z_i NULL:     nothing was kept; Z_i and H_i are recomputed by the
  *                 forward's fused fc1 GEMM (X A_i + b1_i, then GeLU), which
  *                 needs b1_i (NULL = no bias) -- bitwise the forward's values.

@@ -396,14 +396,22 @@ int tp_mlp_shard_fwd(const void* X, const void* A_i, const void* b1_i, const voi
 }
 
 // The backward GEMM sequence shared by tp_mlp_shard_bwd and its recompute form.
+// H_make non-null (H_i unused): H = GeLU(Z_i) is formed in the dZ GEMM's
+// epilogue from the Z it reads anyway, written to H_make, and used from there.
 static int mlp_bwd_gemms(const void* X, const void* A_i, const void* B_i, const void* Z_i, const void* H_i, const void* dY,
                   void* dX_i, float* dA_i, float* db1_i, float* dB_i, float* db2, void* dZ, float* part,
-                  int32_t accumulate, int64_t T, int64_t h, int64_t f, int32_t dtype, hipStream_t s) {
+                  int32_t accumulate, int64_t T, int64_t h, int64_t f, int32_t dtype, hipStream_t s,
+                  void* H_make = nullptr) {
   // dZ = (dY B_i^T) * GeLU'(Z_i)          [T x f], contraction over h
   GemmArgs g1 = make_args(dY, h, B_i, h, T, f, h, dZ, f);
   g1.aux = Z_i;
   g1.ldaux = f;
-  HIP_TRY(gemm(dtype, g1, true, true, EPI_DGELU, s));
+  if (H_make) {
+    g1.C2 = H_make;
+    g1.ldc2 = f;
+    H_i = H_make;
+  }
+  HIP_TRY(gemm(dtype, g1, true, true, H_make ? EPI_DGELU_H : EPI_DGELU, s));
   // dB_i = H_i^T dY                       [f x h], contraction over T; db2 = sum_t dY
   GemmArgs g2 = make_args(H_i, f, dY, h, f, h, T, dB_i, h);
   g2.accumulate = accumulate;
@@ -509,7 +517,6 @@ int tp_mlp_shard_bwd_recompute(const void* X, const void* A_i, const void* b1_i,
   TP_TRY(check_feature({h, f}));
   TP_TRY(check_elems({{T, h}, {h, f}, {T, f}}));
   TP_TRY(check_gemms(dtype, {{T, f}, {f, h}, {h, f}, {T, h}}));
-  if (Z_i) TP_TRY(check_elementwise_launch(T * f));   // H = GeLU(Z) pass
   TP_TRY(check_ptrs_aligned({X, A_i, b1_i, B_i, Z_i, dY, dX_i, dA_i, db1_i, dB_i, db2, workspace}));
   const size_t need = tp_workspace_size(TP_OP_MLP_SHARD_BWD_RECOMPUTE, T, h, F, tp_size, dtype);
   if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
@@ -533,13 +540,12 @@ int tp_mlp_shard_bwd_recompute(const void* X, const void* A_i, const void* b1_i,
     g.ldc2 = f;
     HIP_TRY(gemm(dtype, g, true, false, EPI_BIAS_GELU, s));
     Z = Zw;
-  } else {
-    // Z saved (it already holds the bias): H = GeLU(Z)
-    HIP_TRY(bias_gelu(Z_i, nullptr, H, elem_of(dtype), T, f, s));
   }
   float* part = (float*)(ws + 3 * act);
+  // Z saved (it already holds the bias): H = GeLU(Z) comes out of the dZ GEMM's
+  // epilogue, which reads Z anyway; recomputed from X: H is the fc1 output
   return mlp_bwd_gemms(X, A_i, B_i, Z, H, dY, dX_i, dA_i, db1_i, dB_i, db2, dZ, part, accumulate, T, h, f, dtype,
-                       s);
+                       s, Z_i != nullptr ? H : nullptr);
 }
 
 int tp_column_linear_bwd(const void* X, const void* W_i, const void* dY_i, void* dX_partial, float* dW_i,

@@ -10,7 +10,8 @@ enum Epi : int {
   EPI_STORE = 0,      // C (dtype) = acc (+ bias[n])
   EPI_BIAS_GELU = 1,  // z = acc (+ bias[n]); C2 (dtype, optional) = z; C (dtype) = GeLU(z)
   EPI_DGELU = 2,      // C (dtype) = acc * GeLU'(aux[m, n])
-  EPI_F32 = 3         // C (fp32) = acc, or C += acc when accumulate
+  EPI_F32 = 3,        // C (fp32) = acc, or C += acc when accumulate
+  EPI_DGELU_H = 4     // as EPI_DGELU, and C2 (dtype) = GeLU(aux[m, n]) from the same erf evaluation
 };
 
 // One C = op(A)[M x K] * op(B)[K x N] launch plus its epilogue operands.
@@ -23,7 +24,7 @@ struct GemmArgs {
   int M, N, K;
   void* C;            // main output
   int64_t ldc;
-  void* C2;           // second output (pre-activation for EPI_BIAS_GELU), nullable
+  void* C2;           // second output: the pre-activation for EPI_BIAS_GELU (nullable), GeLU(aux) for EPI_DGELU_H
   int64_t ldc2;
   const void* bias;   // [N], dtype of the path, nullable
   const void* aux;    // [M x N] read by EPI_DGELU

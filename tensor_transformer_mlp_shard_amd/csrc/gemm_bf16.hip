@@ -349,14 +349,14 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::FM]
   constexpr int NCH = 32 * CPR;                      // chunks per strip
   constexpr int NIT = (NCH + 63) / 64;
   static_assert(ROWB % 16 == 0, "strip rows are whole 16-byte chunks");
-  static_assert(C::NCONS * 32 * PITCH <= C::NSTAGE * C::STAGE, "strips fit in the ring");
+  static_assert(C::NCONS * 32 * PITCH * (EPI == EPI_DGELU_H ? 2 : 1) <= C::NSTAGE * C::STAGE, "strips fit in the ring");
   char* strip = smem + wave * 32 * PITCH;
   const int l32 = lane & 31, hh = lane >> 5;
   const int wm = wave / C::CN, wn = wave % C::CN;
   const int col0 = n0 + wn * C::WN;
 
   // Strip rows <-> memory, 16-byte chunks (cols past N and rows past M skipped).
-  auto to_mem = [&](void* base, int64_t ld, int row0) {
+  auto to_mem_from = [&](const char* sbase, void* base, int64_t ld, int row0) {
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int c = it * 64 + lane;
@@ -364,7 +364,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::FM]
       const int r = c / CPR, cc = c % CPR;
       const int m = row0 + r, n = col0 + cc * (16 / ES);
       if (m >= g.M || n >= g.N) continue;
-      const char* p = strip + r * PITCH + cc * 16;
+      const char* p = sbase + r * PITCH + cc * 16;
       if (F32) {
         f32x4 v = *(const f32x4*)p;
         float* dst = (float*)base + (int64_t)m * ld + n;
@@ -381,6 +381,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::FM]
       }
     }
   };
+  auto to_mem = [&](void* base, int64_t ld, int row0) { to_mem_from(strip, base, ld, row0); };
   auto from_mem = [&](const void* base, int64_t ld, int row0) {
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
@@ -408,7 +409,34 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::FM]
       to_mem(g.C, g.ldc, row0);
       continue;
     }
-    if (EPI == EPI_DGELU) from_mem(g.aux, g.ldaux, row0);
+    if (EPI == EPI_DGELU || EPI == EPI_DGELU_H) {
+      from_mem(g.aux, g.ldaux, row0);
+      if (EPI == EPI_DGELU_H) {
+        // dZ = acc * GeLU'(Z) over Z in the strip and H = GeLU(Z) into a second
+        // strip (above the first set in the idle ring), from one evaluation of
+        // erf and the Gaussian per element.
+        char* strip2 = smem + (C::NCONS + wave) * 32 * PITCH;
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const V4 zz = *(const V4*)at(j, q);
+            V4 hv, dz;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float z = (float)zz[e];
+              const GeluParts gp = gelu_parts(z);
+              dz[e] = (E)(acc[i][j][4 * q + e] * __builtin_fmaf(z, gp.pdf, gp.cdf));
+              hv[e] = (E)(z * gp.cdf);
+            }
+            *(V4*)at(j, q) = dz;
+            *(V4*)(strip2 + (at(j, q) - strip)) = hv;
+          }
+        to_mem_from(strip2, g.C2, g.ldc2, row0);
+        to_mem(g.C, g.ldc, row0);
+        continue;
+      }
+    }
     // z = acc (+ bias) for run (j, q)
     auto zval = [&](int j, int q, float* z) {
 #pragma unroll
@@ -631,7 +659,7 @@ template <class C, bool AK, bool BKC, int EPI, typename E>
 const char* kname() {
   static const std::string s = std::string("gemm_") + Vec<E>::name + "_" + (AK ? "n" : "t") + (BKC ? "t" : "n") + "_" +
                                (EPI == EPI_STORE ? "store" : EPI == EPI_BIAS_GELU ? "bias_gelu"
-                                : EPI == EPI_DGELU ? "dgelu" : "f32") +
+                                : EPI == EPI_DGELU ? "dgelu" : EPI == EPI_DGELU_H ? "dgelu_h" : "f32") +
                                "_" + std::to_string(C::BM) + "x" + std::to_string(C::BN);
   return s.c_str();
 }
@@ -673,13 +701,14 @@ hipError_t launch_tile(const GemmArgs& g_in, hipStream_t s, const char** name) {
 // grows with the tile (fewer bytes moved per FLOP).
 struct TileChoice { int bm, bn; };
 
-TileChoice choose_tile(int M, int N) {
+TileChoice choose_tile(int M, int N, bool shared_tiles = true) {
   static const struct { int bm, bn; double eff; } cand[] = {
       {256, 384, 1.12}, {384, 256, 1.12}, {192, 384, 1.06}, {256, 192, 1.00}, {192, 256, 1.00},
       {256, 128, 0.92}, {128, 256, 0.92}, {128, 128, 0.75}};
   double best = 1e300;
   TileChoice pick = {256, 192};
   for (const auto& c : cand) {
+    if (!shared_tiles && c.bm * c.bn > 256 * 192) continue;
     const long tiles = (long)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
     const long waves = (tiles + 255) / 256;
     const double t = (double)waves * c.bm * c.bn / c.eff;
@@ -690,10 +719,13 @@ TileChoice choose_tile(int M, int N) {
 
 template <bool AK, bool BKC, int EPI, typename E>
 hipError_t launch_shape(const GemmArgs& g, hipStream_t s, const char** name) {
-  const TileChoice t = choose_tile(g.M, g.N);
-  if (t.bm == 256 && t.bn == 384) return launch_tile<T256x384, AK, BKC, EPI, E>(g, s, name);
-  if (t.bm == 384 && t.bn == 256) return launch_tile<T384x256, AK, BKC, EPI, E>(g, s, name);
-  if (t.bm == 192 && t.bn == 384) return launch_tile<T192x384, AK, BKC, EPI, E>(g, s, name);
+  // GeLU' with H out stages two strips per wave: only the split tiles hold them
+  const TileChoice t = EPI == EPI_DGELU_H ? choose_tile(g.M, g.N, false) : choose_tile(g.M, g.N);
+  if constexpr (EPI != EPI_DGELU_H) {
+    if (t.bm == 256 && t.bn == 384) return launch_tile<T256x384, AK, BKC, EPI, E>(g, s, name);
+    if (t.bm == 384 && t.bn == 256) return launch_tile<T384x256, AK, BKC, EPI, E>(g, s, name);
+    if (t.bm == 192 && t.bn == 384) return launch_tile<T192x384, AK, BKC, EPI, E>(g, s, name);
+  }
   if (t.bm == 256 && t.bn == 192) return launch_tile<T256x192, AK, BKC, EPI, E>(g, s, name);
   if (t.bm == 192 && t.bn == 256) return launch_tile<T192x256, AK, BKC, EPI, E>(g, s, name);
   if (t.bm == 256 && t.bn == 128) return launch_tile<T256x128, AK, BKC, EPI, E>(g, s, name);
@@ -710,6 +742,7 @@ hipError_t gemm16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hi
   info.bytes = 2.0 * ((double)g.M * g.K + (double)g.K * g.N) + out_bytes +
                ((epi == EPI_BIAS_GELU && g.C2) ? 2.0 * g.M * (double)g.N : 0.0) +
                (epi == EPI_DGELU ? 2.0 * g.M * (double)g.N : 0.0) +
+               (epi == EPI_DGELU_H ? 4.0 * g.M * (double)g.N : 0.0) +
                (g.colsum ? 4.0 * g.N * (double)gemm16_colsum_rows(g.M, g.N) : 0.0);
   // Instantiated layout / epilogue pairs: forward (NN), data gradient (NT) and
   // weight gradient (TN).
@@ -722,6 +755,8 @@ hipError_t gemm16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hi
     e = launch_shape<true, false, EPI_BIAS_GELU, E>(g, s, &info.name);
   else if (a_kcontig && b_kcontig && epi == EPI_STORE) e = launch_shape<true, true, EPI_STORE, E>(g, s, &info.name);
   else if (a_kcontig && b_kcontig && epi == EPI_DGELU) e = launch_shape<true, true, EPI_DGELU, E>(g, s, &info.name);
+  else if (a_kcontig && b_kcontig && epi == EPI_DGELU_H && g.C2 != nullptr)
+    e = launch_shape<true, true, EPI_DGELU_H, E>(g, s, &info.name);
   else if (!a_kcontig && !b_kcontig && epi == EPI_F32) e = launch_shape<false, false, EPI_F32, E>(g, s, &info.name);
   trace_end(s, info);
   return e;

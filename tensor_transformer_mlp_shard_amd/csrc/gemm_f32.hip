@@ -91,7 +91,11 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g) {
         if (g.C2 != nullptr) ((float*)g.C2)[(int64_t)m * g.ldc2 + n] = v;
         v = gelu32(v);
       }
-      if (EPI == EPI_DGELU) v *= gelu_grad32(((const float*)g.aux)[(int64_t)m * g.ldaux + n]);
+      if (EPI == EPI_DGELU || EPI == EPI_DGELU_H) {
+        const float z = ((const float*)g.aux)[(int64_t)m * g.ldaux + n];
+        v *= gelu_grad32(z);
+        if (EPI == EPI_DGELU_H) ((float*)g.C2)[(int64_t)m * g.ldc2 + n] = gelu32(z);
+      }
       ((float*)g.C)[(int64_t)m * g.ldc + n] = v;
     }
   }
@@ -120,6 +124,7 @@ hipError_t gemm_f32(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, 
   else if (a_kcontig && !b_kcontig && epi == EPI_BIAS_GELU) e = launch<true, false, EPI_BIAS_GELU>(g, s);
   else if (a_kcontig && b_kcontig && epi == EPI_STORE) e = launch<true, true, EPI_STORE>(g, s);
   else if (a_kcontig && b_kcontig && epi == EPI_DGELU) e = launch<true, true, EPI_DGELU>(g, s);
+  else if (a_kcontig && b_kcontig && epi == EPI_DGELU_H && g.C2 != nullptr) e = launch<true, true, EPI_DGELU_H>(g, s);
   else if (!a_kcontig && !b_kcontig && epi == EPI_F32) e = launch<false, false, EPI_F32>(g, s);
   trace_end(s, info);
   return e;
