@@ -146,6 +146,18 @@ class MLPConfig:
                                out=self.bwd_out, workspace=self.ws)
 
 
+def _kernel_breakdown(tps, torch, fn, steps):
+    """Per-kernel HIP-event times of `steps` calls of fn (the library's trace)."""
+    tps.trace_start(4096)
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return [{"name": k["name"], "launches_per_step": k["launches"] // steps,
+             "us_per_step": round(1e3 * k["total_ms"] / steps, 2),
+             "tflops": round(k["flops"] / (k["total_ms"] * 1e-3) / 1e12, 1) if k["flops"] else None}
+            for k in tps.trace_stop()]
+
+
 def measure_configs(torch, device, shard, steps, warmup):
     """Forward + backward of every workload in the table, each on its own:
     the tiny fp32 check-path shard, the GPT h=1024 TP=2 and 1.3B TP=1 MLP
@@ -161,6 +173,8 @@ def measure_configs(torch, device, shard, steps, warmup):
                     "dtype": w.dtype, "flop": c.flops, **_rates(c.flops, st)}
         if w.dtype == "fp32":
             out[key]["note"] = "fp32 check path (FMA kernel, not the matrix cores): latency-bound, parity only"
+        else:
+            out[key]["kernels"] = _kernel_breakdown(c.tps, torch, c.step, steps)
         del c
     st = time_stats(torch, shard.mlp_step, steps, warmup)
     out["gpt175b_mlp_tp8"] = {"workload": "175B MLP shard at TP=8: X[2048x12288], A_i[12288x6144], "

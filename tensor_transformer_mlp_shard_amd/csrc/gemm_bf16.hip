@@ -17,9 +17,9 @@
 // for tens of cycles, so a SIMD needs a second wave to keep the matrix pipe fed:
 //  * "split" kernels (tiles up to 256 x 192): 8 consumer waves (2 per SIMD) and
 //    4 producer waves that only issue the copies;
-//  * "shared" kernels (256 x 384, 384 x 256, 192 x 384): 8 waves, each a
-//    consumer of a 128 x 96 (96 x 128, 96 x 96) sub-tile; all 8 also issue
-//    the copies, except in 192 x 384, whose 36 KiB per step do not split
+//  * "shared" kernels (256 x 384, 384 x 256, 192 x 384, 256 x 256): 8 waves,
+//    each a consumer of a 128 x 96 (96 x 128, 96 x 96, 128 x 64) sub-tile; all
+//    8 also issue the copies, except in 192 x 384, whose 36 KiB per step do not split
 //    eight ways: there waves 0-3, one per SIMD, issue 9 copies each (six
 //    copying waves would put 12 copies per step on two SIMDs and 6 on the
 //    others, and the per-step barrier waits for the busiest).  The biggest tile moves 29% fewer bytes per FLOP from L2 and
@@ -654,6 +654,7 @@ using T128x128 = Cfg<128, 128, 4, 2>;
 using T256x384 = Cfg<256, 384, 0, 2>;
 using T384x256 = Cfg<384, 256, 0, 4>;
 using T192x384 = Cfg<192, 384, 0, 2, 4>;  // 36 KiB per K step: 4 copying waves (one per SIMD) x 9 copies
+using T256x256 = Cfg<256, 256, 0, 2>;     // 128 x 64 per wave, five 32 KiB stages
 
 template <class C, bool AK, bool BKC, int EPI, typename E>
 const char* kname() {
@@ -698,12 +699,15 @@ hipError_t launch_tile(const GemmArgs& g_in, hipStream_t s, const char** name) {
 
 // Tile shape: the one with the least estimated time, counting whole waves of
 // tiles over the 256 CUs (one workgroup per CU) and a per-tile efficiency that
-// grows with the tile (fewer bytes moved per FLOP).
+// grows with the tile (fewer bytes moved per FLOP).  256 x 256 moves as many
+// bytes per FLOP between L2 and LDS as 192 x 384 and fills whole waves where
+// that one leaves a partial wave (the 1.3B MLP's 4096 x 8192 products with
+// K = 2048 and its weight gradients: +7% and +3% in a same-box A/B).
 struct TileChoice { int bm, bn; };
 
 TileChoice choose_tile(int M, int N, bool shared_tiles = true) {
   static const struct { int bm, bn; double eff; } cand[] = {
-      {256, 384, 1.12}, {384, 256, 1.12}, {192, 384, 1.06}, {256, 192, 1.00}, {192, 256, 1.00},
+      {256, 384, 1.12}, {384, 256, 1.12}, {192, 384, 1.06}, {256, 256, 1.06}, {256, 192, 1.00}, {192, 256, 1.00},
       {256, 128, 0.92}, {128, 256, 0.92}, {128, 128, 0.75}};
   double best = 1e300;
   TileChoice pick = {256, 192};
@@ -725,6 +729,7 @@ hipError_t launch_shape(const GemmArgs& g, hipStream_t s, const char** name) {
     if (t.bm == 256 && t.bn == 384) return launch_tile<T256x384, AK, BKC, EPI, E>(g, s, name);
     if (t.bm == 384 && t.bn == 256) return launch_tile<T384x256, AK, BKC, EPI, E>(g, s, name);
     if (t.bm == 192 && t.bn == 384) return launch_tile<T192x384, AK, BKC, EPI, E>(g, s, name);
+    if (t.bm == 256 && t.bn == 256) return launch_tile<T256x256, AK, BKC, EPI, E>(g, s, name);
   }
   if (t.bm == 256 && t.bn == 192) return launch_tile<T256x192, AK, BKC, EPI, E>(g, s, name);
   if (t.bm == 192 && t.bn == 256) return launch_tile<T192x256, AK, BKC, EPI, E>(g, s, name);
@@ -778,6 +783,7 @@ int64_t gemm16_work_items(int64_t M, int64_t N) {
   if (t.bm == 256 && t.bn == 384) threads = T256x384::NT;
   else if (t.bm == 384 && t.bn == 256) threads = T384x256::NT;
   else if (t.bm == 192 && t.bn == 384) threads = T192x384::NT;
+  else if (t.bm == 256 && t.bn == 256) threads = T256x256::NT;
   else if (t.bm == 256 && t.bn == 192) threads = T256x192::NT;
   else if (t.bm == 192 && t.bn == 256) threads = T192x256::NT;
   else if (t.bm == 256 && t.bn == 128) threads = T256x128::NT;

@@ -366,23 +366,27 @@ def test_weight_grad_192x384_tile_ragged(dtype):
 
 # (T, K_in, N_out) of a column linear whose forward (NN, T x N_out), data
 # gradient (NT, T x K_in) and weight gradient (TN, K_in x N_out) select the
-# big shared tiles named after each shape; every edge is ragged (T is odd or
+# big shared tiles named after each shape -- 256 x 384, 384 x 256, 192 x 384
+# and 256 x 256, each on all three layouts; every edge is ragged (T is odd or
 # not a multiple of 64, the feature sizes are multiples of 8 but not of 32).
 BIG_TILES = [
-    (2179, 6136, 8184, ("nn_store_256x384", "nt_store_192x384", "tn_f32_384x256")),
+    (2179, 6136, 8184, ("nn_store_256x384", "nt_store_256x256", "tn_f32_384x256")),
     (2179, 10232, 2040, ("nt_store_256x384", "tn_f32_256x384")),
-    (3000, 8184, 3080, ("nt_store_384x256", "tn_f32_192x384")),
-    (3000, 2040, 8184, ("nn_store_384x256", "tn_f32_192x384")),
-    (2100, 3080, 6136, ("nn_store_192x384", "tn_f32_256x384")),
+    (3000, 8184, 3080, ("nt_store_384x256", "tn_f32_256x256")),
+    (3000, 2040, 8184, ("nn_store_384x256", "tn_f32_256x256")),
+    (2100, 3080, 6136, ("nn_store_256x256", "tn_f32_256x384")),
+    (2967, 8216, 5432, ("nn_store_192x384",)),
+    (3015, 5816, 7656, ("nt_store_192x384",)),
+    (2912, 6360, 5744, ("tn_f32_192x384",)),
 ]
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
 @pytest.mark.parametrize("shape", BIG_TILES, ids=[f"T{s[0]}_K{s[1]}_N{s[2]}" for s in BIG_TILES])
 def test_big_tiles_ragged(shape, dtype):
-    """The 256 x 384, 384 x 256 and 192 x 384 kernels on all three operand
-    layouts with ragged M, N and K, whole tensors against the oracle (bias in
-    the forward, fused or separate bias gradient in the backward)."""
+    """The 256 x 384, 384 x 256, 192 x 384 and 256 x 256 kernels on all three
+    operand layouts with ragged M, N and K, whole tensors against the oracle
+    (bias in the forward, fused or separate bias gradient in the backward)."""
     T, K, N, want = shape
     dt = DTS[dtype]
     print(f"big tiles T{T} K{K} N{N} {dt}", flush=True)
