@@ -393,6 +393,28 @@ def measure_recompute(torch, shard, steps, warmup, pairs=6):
     return out
 
 
+def run_nt_compare(torch, device, steps):
+    """The step's two hardest data-gradient products, QKV dX (8192 x 12288,
+    K = 4608) and the MLP dH with GeLU' (2048 x 6144, K = 12288), through this
+    library and through torch.mm (hipBLASLt) on the same operands, `steps`
+    times each: a fixed workload for kernel traces and hardware counters."""
+    import tensor_transformer_mlp_shard_amd as tps
+
+    g = torch.Generator(device=device).manual_seed(7)
+    rn = lambda *s, sc=1.0: (torch.randn(*s, device=device, generator=g) * sc).to(torch.bfloat16)  # noqa: E731
+    Xq, Wq, dQ = rn(8192, 12288), rn(12288, 4608, sc=0.006), rn(8192, 4608)
+    X, A, B, Z, H, dY = (rn(2048, 12288), rn(12288, 6144, sc=0.006), rn(6144, 12288, sc=0.006), rn(2048, 6144),
+                         rn(2048, 6144), rn(2048, 12288))
+    out1 = torch.empty(8192, 12288, dtype=torch.bfloat16, device=device)
+    out2 = torch.empty(2048, 6144, dtype=torch.bfloat16, device=device)
+    for _ in range(steps):
+        tps.column_linear_bwd(Xq, Wq, dQ, tp_size=8, want_db=False)
+        torch.mm(dQ, Wq.t(), out=out1)
+        tps.mlp_shard_bwd(X, A, B, Z, H, dY, tp_size=8, want_db1=False)
+        torch.mm(dY, B.t(), out=out2)
+    torch.cuda.synchronize()
+
+
 def time_stats(torch, fn, steps, warmup):
     """Run `warmup` untimed calls, then exactly `steps` timed ones between two
     synchronisations.  HIP events on the current stream bracket every call, so
@@ -506,11 +528,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-frac", type=int, default=1, help="oracle sample = 1/N of the tokens")
-    ap.add_argument("--part", choices=["all", "mlp", "attn", "core_attn", "sp_edge", "side"], default="all",
+    ap.add_argument("--part", choices=["all", "mlp", "attn", "core_attn", "sp_edge", "side", "nt_compare"],
+                    default="all",
                     help="run only one part (for profiling runs)")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the measurements outside the step (selective recompute, core attention, "
-                         "sequence-parallel edge): for profiler runs whose per-kernel averages must be the step's")
+                    help="skip the measurements outside the step (the other workloads, selective recompute, "
+                         "core attention, sequence-parallel edge, ...): for profiler runs whose per-kernel "
+                         "averages must be the step's")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of this many MiB, three times (a known-size "
                          "reference for hardware byte counters)")
@@ -547,6 +571,10 @@ def main():
     if args.part == "side":
         print(json.dumps({"side_kernels": measure_side(torch, device, args.steps, args.warmup)}), flush=True)
         return
+    if args.part == "nt_compare":
+        run_nt_compare(torch, device, args.steps)
+        print(json.dumps({"nt_compare": "done", "steps": args.steps}), flush=True)
+        return
     shard = Shard(device)
     fn = {"all": shard.step, "mlp": shard.mlp_step, "attn": shard.attn_step}[args.part]
     flops = {"all": shard.flops_mlp + shard.flops_attn, "mlp": shard.flops_mlp, "attn": shard.flops_attn}[args.part]
@@ -555,7 +583,7 @@ def main():
     ms, wall_ms = st["mean"], st["wall"]
     value = flops / (ms * 1e-3) / 1e12
     configs = {}
-    if args.part == "all":
+    if args.part == "all" and not args.no_extras:
         configs = measure_configs(torch, device, shard, min(args.steps, 50), min(args.warmup, 20))
 
     dom, kernels = roofline_from_trace(shard.tps, torch, fn, args.steps)
