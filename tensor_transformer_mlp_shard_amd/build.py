@@ -28,11 +28,9 @@ COMMON = [
     "-Wno-unused-command-line-argument",
 ]
 
-# Per-source extra flags.  The attention backward needs more than 256 registers
-# per lane; left to its heuristic the compiler then parks the MFMA accumulators
-# in AGPRs and copies them back and forth around every block (hundreds of
-# v_accvgpr moves per block), so the VGPR form of the MFMA is forced there.
-EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source extra flags (none at present: every kernel fits 256 VGPRs per lane,
+# so the compiler keeps the MFMA accumulators in VGPRs by itself).
+EXTRA: dict = {}
 
 SOURCES = ["gemm_bf16.hip", "gemm_f32.hip", "elementwise.hip", "attention.hip", "sp_edge.hip", "probe.hip", "api.cpp"]
 

@@ -180,8 +180,8 @@ int check_attention(int64_t T, int64_t seq, int64_t heads, int64_t head_dim, int
   if (tp_size < 1 || heads % tp_size != 0) return TP_ERR_TP_DIVISIBILITY;
   const int64_t hl = heads / tp_size;
   if (3 * hl * head_dim > kMaxFeature) return TP_ERR_DIM;
-  // one workgroup of kAttnThreads per 128 queries (or keys) of a (sequence, head)
-  TP_TRY(check_launch((seq + 127) / 128 * (T / seq) * hl, kAttnThreads));
+  // one workgroup of kAttnThreads per 128 queries or per 64 keys of a (sequence, head)
+  TP_TRY(check_launch((seq + 63) / 64 * (T / seq) * hl, kAttnThreads));
   p.T = T;
   p.S = (int)seq;
   p.Hl = (int)hl;

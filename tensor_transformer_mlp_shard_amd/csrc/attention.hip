@@ -64,8 +64,32 @@ __device__ __forceinline__ int kv_slot(int c, int r) {
   return D == 128 ? c ^ (4 * (r & 3) + ((r >> 2) & 3)) : c ^ (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
 }
 
+// The Q / dO blocks of the dK/dV kernel use a second permutation, made for its
+// transposing reads of 16 x 16 operand blocks as well as its row reads (16
+// lanes read chunk c of 16 consecutive rows: f(r) takes 16 distinct values on
+// 16 aligned rows).  A transposing read's 16-lane group covers 4 rows x 32
+// bytes (chunks 2j, 2j + 1), group g rows 4g .. 4g + 3, and the LDS serves
+// groups 0 and 2 together, 1 and 3 together (measured: a permutation that kept
+// each run of 8 rows apart but not rows 0-3 from 8-11 cost 13 M bank-conflict
+// cycles per 175B-shaped launch; this one none), so f(r) / 2 must differ on
+// rows {0-3, 8-11} and on {4-7, 12-15} -- and, for D = 64 (two 128-byte rows
+// per 256-byte bank sweep), among the rows of one parity in those sets.
+//  D = 128: f(r) = 2 ((r mod 4) + 4 x) + (r / 8 mod 2);
+//  D = 64:  f(r) = 2 ((r / 2 mod 2) + 2 x) + (r / 8 mod 2),  x = (r / 4 xor r / 8) mod 2.
+template <int D>
+__device__ __forceinline__ int qd_slot(int c, int r) {
+  const int x = ((r >> 2) ^ (r >> 3)) & 1;
+  return D == 128 ? c ^ (2 * ((r & 3) + 4 * x) + ((r >> 3) & 1)) : c ^ (2 * (((r >> 1) & 1) + 2 * x) + ((r >> 3) & 1));
+}
+
 __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// v_mfma_f32_16x16x32_bf16: A lane l holds row l % 16, k = 8 (l / 16) + 0..7;
+// B lane l holds column l % 16, the same k; D lane l holds column l % 16, rows
+// 4 (l / 16) + 0..3.
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // The value held by lane ^ 32 (xhalf = (lane ^ 32) * 4).
@@ -126,7 +150,7 @@ struct KvReadOffsets {
 // lane i of copy c landing at byte 1024 (wave NI + c) + 16 i, which is chunk
 // slot s of row r; it fetches the chunk that the swizzle puts there.  Rows at
 // or past `rows_left` read as zero through the buffer range check.
-template <int D>
+template <int D, bool QD = false>
 struct BlockCopier {
   static constexpr int NI = Shape<D>::BLOCK_BYTES / 1024 / AW;
   int off[NI];
@@ -135,7 +159,7 @@ struct BlockCopier {
     for (int i = 0; i < NI; ++i) {
       const int q = (wave * NI + i) * 64 + lane;
       const int r = q / Shape<D>::CH, sl = q % Shape<D>::CH;
-      off[i] = r * (int)(ld * 2) + kv_slot<D>(sl, r) * 16;
+      off[i] = r * (int)(ld * 2) + (QD ? qd_slot<D>(sl, r) : kv_slot<D>(sl, r)) * 16;
     }
   }
   // Block starting at `first` (row 0 of the copy); `rows_left` rows from there are data.
@@ -368,10 +392,11 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(FwdArgs a) {
 // Two kernels, no atomics (bitwise reproducible), dQ first:
 //  * attn_bwd_dq (below) also forms Dt for its queries from the dO rows it
 //    holds and the matching O rows, and writes it for attn_bwd_dkdv;
-//  * attn_bwd_dkdv: a workgroup owns 128 keys (32 per wave, one per lane
-//    column); K and V of its keys stay in registers; queries (Q and dO rows)
-//    are copied HBM -> LDS directly in double-buffered blocks of 64.  Scores are computed as S[query][key] so each lane
-//    holds one key's column, and P and dS feed dV^T += dO^T P and
+//  * attn_bwd_dkdv: a workgroup owns 64 keys (16 per wave, one per lane
+//    column of 16 x 16 x 32 MFMAs, two workgroups per CU); K and V of its keys
+//    stay in registers; queries (Q and dO rows) are copied HBM -> LDS directly
+//    in double-buffered blocks of 64.  Scores are computed as S[query][key] so
+//    each lane holds one key's column, and P and dS feed dV^T += dO^T P and
 //    dK^T += Q^T dS from registers (queries in the accumulator order, dO^T and
 //    Q^T read from LDS with transposing reads in that order);
 //  * attn_bwd_dq: a workgroup owns 128 queries (32 per wave, one per lane
@@ -393,16 +418,36 @@ struct BwdArgs {
 
 constexpr float LOG2E = 1.4426950408889634f;
 
+// dK/dV with 16 keys per wave on 16 x 16 x 32 MFMAs.  A workgroup owns 64 keys
+// (4 waves x 16, one key per lane column); with K, V, dK, dV, S and dP of 16
+// keys a wave needs ~200 registers, so two workgroups share each CU and a SIMD
+// runs two waves of different workgroups, whose MFMAs cover each other's
+// softmax arithmetic and waits.  Per 64-query block (Q and dO copied HBM ->
+// LDS directly, double-buffered, in the qd_slot layout):
+//  * S[q][key] and dP[q][key] for 4 blocks of 16 queries (A: Q / dO rows read
+//    from LDS, B: this wave's K / V in registers, k = d);
+//  * P and dS in registers, packed as the B operand of dV^T += dO^T P and
+//    dK^T += Q^T dS over 32-query k blocks: k slot 8 g + e of lane half g is
+//    query 4 g + (e mod 4) + 16 (e / 4) of the k block, the order the score
+//    accumulators hold them, and dO^T / Q^T are read with transposing reads of
+//    rows 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3 in that same order.
+// The query / key pairs each product sums over, and their order, are those of
+// the 32-key kernel's; only the MFMA blocking differs.
 template <int D>
-__global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(NT, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
   using SH = Shape<D>;
   constexpr int QB = 64;                     // queries per LDS block
+  constexpr int KW = 16;                     // keys per wave
+  constexpr int BKW = AW * KW;               // keys per workgroup
   constexpr int BUF = 2 * SH::BLOCK_BYTES;   // one buffer: a Q block, then a dO block
+  constexpr int NS = D / 32;                 // 32-wide d slices: k of S and dP
+  constexpr int NDB = D / 16;                // 16-row d blocks of dK^T and dV^T
+  constexpr int RB = SH::ROW_BYTES;
   __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
   __shared__ __attribute__((aligned(16))) float stat[2][2][QB];  // [buffer][lse * log2(e), Dt]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hh = lane >> 5;
+  const int l16 = lane & 15, g = lane >> 4;
   const int bh = a.B * a.Hl;
   const int kb = (int)(blockIdx.x / bh);           // causal: low key blocks have the most queries
   const int b = (int)(blockIdx.x % bh) / a.Hl, h = (int)(blockIdx.x % bh) % a.Hl;
@@ -413,13 +458,13 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
   const bf16* vbase = qbase + 2LL * a.Hl * D;
   const int64_t ldo = (int64_t)a.Hl * D;
   const bf16* dobase = a.dout + row0 * ldo + (int64_t)h * D;
-  const int kw0 = kb * 128 + wave * 32;           // first key of this wave
-  const int kj = kw0 + l32;                       // this lane's key
+  const int kw0 = kb * BKW + wave * KW;            // first key of this wave
+  const int kj = kw0 + l16;                        // this lane's key
   const bool kvalid = kj < a.S;
-  const int qstart = a.causal ? kb * 128 : 0;     // earlier queries see none of these keys
+  const int qstart = a.causal ? kb * BKW : 0;      // earlier queries see none of these keys
   const int nqblk = (a.S - qstart + QB - 1) / QB;
 
-  BlockCopier<D> cq, co;
+  BlockCopier<D, true> cq, co;
   cq.init(ld, wave, lane);
   co.init(ldo, wave, lane);
   const unsigned lds0 = lds_address(smem);
@@ -446,20 +491,28 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
   issue(0, 0);
   load_stats(qstart);
 
-  // K and V of this lane's key as the B operand (k = d) of S and dP.
-  bf16x8 kf[SH::KS], vf[SH::KS];
+  // K and V of this lane's key as the B operand of S and dP: d = 32 s + 8 g + 0..7.
+  bf16x8 kf[NS], vf[NS];
 #pragma unroll
-  for (int s = 0; s < SH::KS; ++s) {
-    kf[s] = kvalid ? *(const bf16x8*)(kbase + (int64_t)kj * ld + 16 * s + 8 * hh) : bf16x8{};
-    vf[s] = kvalid ? *(const bf16x8*)(vbase + (int64_t)kj * ld + 16 * s + 8 * hh) : bf16x8{};
+  for (int s = 0; s < NS; ++s) {
+    kf[s] = kvalid ? *(const bf16x8*)(kbase + (int64_t)kj * ld + 32 * s + 8 * g) : bf16x8{};
+    vf[s] = kvalid ? *(const bf16x8*)(vbase + (int64_t)kj * ld + 32 * s + 8 * g) : bf16x8{};
   }
-  const int g16 = lane >> 4, i16 = lane & 15;
-  KvReadOffsets<D> ro;  // row reads of Q / dO (.k), transposing reads of dO^T / Q^T (.va, .vb)
-  ro.init(l32, hh, 4 * (g16 >> 1) + (i16 >> 2), 16 * (g16 & 1) + 4 * (i16 & 3));
-
-  f32x16 dk[SH::DT], dv[SH::DT];
+  // Row reads: query 16 t + l16, chunk 4 s + g (the swizzle depends on the row
+  // mod 16 only, so t is an immediate).  Transposing reads of d block db: row
+  // 4 g + l16 / 4 (+ 16, + 32 kq: immediates), column 16 db + 4 (l16 mod 4).
+  int rowo[NS], tro[NDB];
 #pragma unroll
-  for (int t = 0; t < SH::DT; ++t) { dk[t] = f32x16{}; dv[t] = f32x16{}; }
+  for (int s = 0; s < NS; ++s) rowo[s] = l16 * RB + qd_slot<D>(4 * s + g, l16) * 16;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int r = 4 * g + (l16 >> 2);
+    tro[db] = r * RB + qd_slot<D>(2 * db + ((l16 >> 1) & 1), r) * 16 + (l16 & 1) * 8;
+  }
+
+  f32x4 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int t = 0; t < NDB; ++t) { dk[t] = f32x4{}; dv[t] = f32x4{}; }
 
   store_stats(0);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -478,95 +531,86 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
     const char* Qs = smem + BI * BUF;
     const char* Gs = Qs + SH::BLOCK_BYTES;
 
-    // S[query][key] and dP[query][key] for queries 32 t + (0..31) of the block;
-    // the Q and dO operands are read RD slices ahead of their MFMAs.
-    constexpr int RD = 2;
-    f32x16 sc[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-    bf16x8 qr[RD + 1][2], gr[RD + 1][2];
-    auto rows = [&](int s) {
+    // S and dP of queries 16 t + (0..15) of the block, t = n / NS, d slice
+    // s = n % NS; the Q and dO operands are read RD steps ahead.
+    constexpr int RD = 3, NSTEP = 4 * NS;
+    f32x4 sc[4], dp[4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int o = ro.k[s] + t * 32 * SH::ROW_BYTES;
-        qr[s % (RD + 1)][t] = *(const bf16x8*)(Qs + o);
-        gr[s % (RD + 1)][t] = *(const bf16x8*)(Gs + o);
-      }
+    for (int t = 0; t < 4; ++t) { sc[t] = f32x4{}; dp[t] = f32x4{}; }
+    bf16x8 qr[RD + 1], gr[RD + 1];
+    auto rows = [&](int n) {
+      const int o = rowo[n % NS] + (n / NS) * 16 * RB;
+      qr[n % (RD + 1)] = *(const bf16x8*)(Qs + o);
+      gr[n % (RD + 1)] = *(const bf16x8*)(Gs + o);
     };
 #pragma unroll
-    for (int s = 0; s < RD; ++s) rows(s);
+    for (int n = 0; n < RD; ++n) rows(n);
 #pragma unroll
-    for (int s = 0; s < SH::KS; ++s) {
-      if (s + RD < SH::KS) rows(s + RD);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        sc[t] = mfma(qr[s % (RD + 1)][t], kf[s], sc[t]);
-        dp[t] = mfma(gr[s % (RD + 1)][t], vf[s], dp[t]);
-      }
+    for (int n = 0; n < NSTEP; ++n) {
+      if (n + RD < NSTEP) rows(n + RD);
+      sc[n / NS] = mfma16(qr[n % (RD + 1)], kf[n % NS], sc[n / NS]);
+      dp[n / NS] = mfma16(gr[n % (RD + 1)], vf[n % NS], dp[n / NS]);
     }
-    // Keep the operand reads RD slices ahead (the scheduler would otherwise
-    // sink each read next to its MFMA and expose the LDS latency).
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 * RD, 0);
+    // Keep the operand reads RD steps ahead.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * RD, 0);
 #pragma unroll
-    for (int s = 0; s < SH::KS; ++s) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      if (s + RD < SH::KS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    for (int n = 0; n < NSTEP; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (n + RD < NSTEP) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     // Causal mask, only where some query of the block precedes one of this
-    // wave's keys: accumulator element (t, v) is query q0 + 4 hh + c(t, v).
-    if (a.causal && q0 < kw0 + 31) {
-      const int x = kj - q0 - 4 * hh;
+    // wave's keys: element (t, r) is query q0 + 16 t + 4 g + r.
+    if (a.causal && q0 < kw0 + KW - 1) {
+      const int x = kj - q0 - 4 * g;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int c = 32 * t + 8 * (v >> 2) + (v & 3);
-          sc[t][v] = c < x ? -INFINITY : sc[t][v];
-        }
+        for (int r = 0; r < 4; ++r) sc[t][r] = 16 * t + r < x ? -INFINITY : sc[t][r];
     }
-    // Per 16-query slice q (accumulator elements 8 q .. 8 q + 7, queries
-    // 16 q + {0..3, 8..11} + 4 hh): P and dS, then dV^T += dO^T P and
-    // dK^T += Q^T dS for that slice, so the vector work of slice q + 1 runs
-    // beside the MFMAs of slice q.  dO^T and Q^T are read with transposing
-    // reads in the same query order, VPD operand pairs ahead.
-    constexpr int NOP = 4 * SH::DT, VPD = 4;
+    // dO^T and Q^T operands of 32-query k block kq, d block db.
+    auto tr = [&](const char* base, int kq, int db) {
+      const char* p = base + tro[db] + 32 * kq * RB;
+      const bf16x4 lo = read_tr(p), hi = read_tr(p + 16 * RB);
+      bf16x8 v;
+      v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+      v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+      return v;
+    };
+    constexpr int NOP = 2 * NDB, VPD = 6;
     bf16x8 gv[VPD], qv[VPD];
     auto tr_pair = [&](int n) {
-      const int q = n / SH::DT, t = n % SH::DT;
-      const int oa = ro.va[t] + 16 * q * SH::ROW_BYTES, ob = ro.vb[t] + 16 * q * SH::ROW_BYTES;
-      const bf16x4 g_lo = read_tr(Gs + oa), g_hi = read_tr(Gs + ob);
-      const bf16x4 q_lo = read_tr(Qs + oa), q_hi = read_tr(Qs + ob);
-      bf16x8& g = gv[n % VPD];
-      bf16x8& qq = qv[n % VPD];
-      g[0] = g_lo[0]; g[1] = g_lo[1]; g[2] = g_lo[2]; g[3] = g_lo[3];
-      g[4] = g_hi[0]; g[5] = g_hi[1]; g[6] = g_hi[2]; g[7] = g_hi[3];
-      qq[0] = q_lo[0]; qq[1] = q_lo[1]; qq[2] = q_lo[2]; qq[3] = q_lo[3];
-      qq[4] = q_hi[0]; qq[5] = q_hi[1]; qq[6] = q_hi[2]; qq[7] = q_hi[3];
+      gv[n % VPD] = tr(Gs, n / NDB, n % NDB);
+      qv[n % VPD] = tr(Qs, n / NDB, n % NDB);
     };
 #pragma unroll
     for (int n = 0; n < VPD; ++n) tr_pair(n);
+    // P and dS of k block kq (score blocks t = 2 kq, 2 kq + 1).
+    bf16x8 pf[2], sf[2];
+    auto pds = [&](int kq, int u) {
+      const int t = 2 * kq + u;
+      const f32x4 l2 = *(const f32x4*)&stat[BI][0][16 * t + 4 * g];
+      const f32x4 dd = *(const f32x4*)&stat[BI][1][16 * t + 4 * g];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int t = q >> 1;
-      bf16x8 pf, sf;
-#pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        const int g = 2 * (q & 1) + gg;
-        const int qo = 32 * t + 8 * g + 4 * hh;
-        const f32x4 l2 = *(const f32x4*)&stat[BI][0][qo];
-        const f32x4 dd = *(const f32x4*)&stat[BI][1][qo];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int v = 4 * g + e;
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][v], a.scale_log2, -l2[e]));
-          pf[4 * gg + e] = (bf16)p;
-          sf[4 * gg + e] = (bf16)(p * (dp[t][v] - dd[e]));
-        }
+      for (int r = 0; r < 4; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][r], a.scale_log2, -l2[r]));
+        pf[kq][4 * u + r] = (bf16)p;
+        sf[kq][4 * u + r] = (bf16)(p * (dp[t][r] - dd[r]));
       }
+    };
+    pds(0, 0);
+    pds(0, 1);
 #pragma unroll
-      for (int d = 0; d < SH::DT; ++d) {
-        const int n = q * SH::DT + d;
-        dv[d] = mfma(gv[n % VPD], pf, dv[d]);
-        dk[d] = mfma(qv[n % VPD], sf, dk[d]);
+    for (int kq = 0; kq < 2; ++kq) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int n = kq * NDB + db;
+        dv[db] = mfma16(gv[n % VPD], pf[kq], dv[db]);
+        dk[db] = mfma16(qv[n % VPD], sf[kq], dk[db]);
         if (n + VPD < NOP) tr_pair(n + VPD);
+      }
+      if (kq == 0) {
+        pds(1, 0);
+        pds(1, 1);
       }
     }
     if (j + 1 < nqblk) store_stats(BI ^ 1);
@@ -583,18 +627,16 @@ __global__ void __launch_bounds__(NT, 1) attn_bwd_dkdv_kernel(BwdArgs a) {
     bf16* krow = a.dqkv + (row0 + kj) * ld + (int64_t)a.Hl * D + (int64_t)h * D;
     bf16* vrow = krow + (int64_t)a.Hl * D;
 #pragma unroll
-    for (int t = 0; t < SH::DT; ++t)
+    for (int db = 0; db < NDB; ++db) {
+      bf16x4 k4, v4;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 k4, v4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          k4[e] = (bf16)(dk[t][4 * g + e] * a.scale);
-          v4[e] = (bf16)dv[t][4 * g + e];
-        }
-        *(bf16x4*)(krow + 32 * t + 8 * g + 4 * hh) = k4;
-        *(bf16x4*)(vrow + 32 * t + 8 * g + 4 * hh) = v4;
+      for (int r = 0; r < 4; ++r) {
+        k4[r] = (bf16)(dk[db][r] * a.scale);
+        v4[r] = (bf16)dv[db][r];
       }
+      *(bf16x4*)(krow + 16 * db + 4 * g) = k4;
+      *(bf16x4*)(vrow + 16 * db + 4 * g) = v4;
+    }
   }
 }
 
@@ -834,8 +876,9 @@ hipError_t attention_bwd(const bf16* qkv, const bf16* o, const float* lse, const
   if (e != hipSuccess) return e;
   LaunchInfo i1{d128 ? "attn_bwd_dkdv_d128" : "attn_bwd_dkdv_d64", 2.0 * f, 3.0 * el + 4.0 * 2 * p.T * p.Hl + 2.0 * el};
   trace_begin(s);
-  if (d128) hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, grid, dim3(NT), 0, s, a);
-  else hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, grid, dim3(NT), 0, s, a);
+  const dim3 grid64((unsigned)((int64_t)((p.S + 63) / 64) * a.B * a.Hl));  // 64 keys per workgroup
+  if (d128) hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, grid64, dim3(NT), 0, s, a);
+  else hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, grid64, dim3(NT), 0, s, a);
   trace_end(s, i1);
   return hipGetLastError();
 }
