@@ -420,9 +420,9 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 // dK/dV with 16 keys per wave on 16 x 16 x 32 MFMAs.  A workgroup owns 64 keys
 // (4 waves x 16, one key per lane column); with K, V, dK, dV, S and dP of 16
-// keys a wave needs ~200 registers, so two workgroups share each CU and a SIMD
-// runs two waves of different workgroups, whose MFMAs cover each other's
-// softmax arithmetic and waits.  Per 64-query block (Q and dO copied HBM ->
+// keys a wave needs fewer than 256 registers, so two workgroups share each CU
+// and a SIMD runs two waves of different workgroups, which do not wait at each
+// other's barriers and whose MFMAs cover each other's softmax arithmetic.  Per 64-query block (Q and dO copied HBM ->
 // LDS directly, double-buffered, in the qd_slot layout):
 //  * S[q][key] and dP[q][key] for 4 blocks of 16 queries (A: Q / dO rows read
 //    from LDS, B: this wave's K / V in registers, k = d);
@@ -431,8 +431,6 @@ constexpr float LOG2E = 1.4426950408889634f;
 //    query 4 g + (e mod 4) + 16 (e / 4) of the k block, the order the score
 //    accumulators hold them, and dO^T / Q^T are read with transposing reads of
 //    rows 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3 in that same order.
-// The query / key pairs each product sums over, and their order, are those of
-// the 32-key kernel's; only the MFMA blocking differs.
 template <int D>
 __global__ void __launch_bounds__(NT, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
   using SH = Shape<D>;
