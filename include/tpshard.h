@@ -150,7 +150,12 @@ int tp_mlp_shard_fwd(const void* X, const void* A_i, const void* b1_i, const voi
  *   db2   [h]     fp32 = sum over tokens of dY (gradient of the row-parallel
  *                   output bias; compute it on one rank), or NULL to skip
  *   accumulate 0: overwrite dA_i, dB_i, db1_i, db2; 1: add to them.
- *   workspace: >= tp_workspace_size(TP_OP_MLP_SHARD_BWD, T, h, F, p, dtype) bytes.
+ *   workspace: >= tp_workspace_size(TP_OP_MLP_SHARD_BWD, T, h, F, p, dtype) bytes:
+ *   dZ, the bias-gradient partial rows, and (16-bit, where a weight gradient's
+ *   tiles would fill at most half of the CUs and T is at least 2048) the fp32
+ *   partial of that GEMM's K split: twice the workgroups each take half of the
+ *   tokens, and a second pass adds the second half to the first in a fixed
+ *   order (with accumulate: (old + first half) + second half).
  */
 int tp_mlp_shard_bwd(const void* X, const void* A_i, const void* B_i, const void* Z_i,
                      const void* H_i, const void* dY, void* dX_i, float* dA_i, float* db1_i,
@@ -163,8 +168,8 @@ int tp_mlp_shard_bwd(const void* X, const void* A_i, const void* B_i, const void
  * that cannot allocate device memory or hand out scratch: code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation.
  * Same arguments, outputs, kernels and results (bitwise) as tp_mlp_shard_bwd,
- * without workspace / workspace_bytes: the scratch (dZ, then the bias-gradient
- * partials) lives in a static device array of tp_noalloc_scratch_bytes()
+ * without workspace / workspace_bytes: the scratch (dZ, the bias-gradient
+ * partials, a K split's partial) lives in a static device array of tp_noalloc_scratch_bytes()
  * (96 MiB) that the library holds on each GPU it runs on until the process
  * ends.  A problem whose scratch, tp_workspace_size(TP_OP_MLP_SHARD_BWD, ...),
  * exceeds that size is rejected with TP_ERR_SCRATCH before anything is
@@ -211,7 +216,10 @@ int tp_mlp_shard_bwd_recompute(const void* X, const void* A_i, const void* b1_i,
  *   dX_partial [T x K]   dtype = dY_i W_i^T (summed over ranks outside)
  *   dW_i       [K x N/p] fp32  = X^T dY_i
  *   db_i       [N/p]     fp32  = sum over tokens of dY_i, or NULL
- *   accumulate as in tp_mlp_shard_bwd.  workspace: TP_OP_COLUMN_LINEAR_BWD.
+ *   accumulate as in tp_mlp_shard_bwd.  workspace: TP_OP_COLUMN_LINEAR_BWD bytes,
+ *   required with db_i.  A workspace of that size also lets a small dW_i (tiles
+ *   filling at most half of the CUs, T >= 2048) split its contraction as in
+ *   tp_mlp_shard_bwd; with none (db_i NULL) dW_i is computed unsplit.
  */
 int tp_column_linear_bwd(const void* X, const void* W_i, const void* dY_i, void* dX_partial,
                          float* dW_i, float* db_i, void* workspace, size_t workspace_bytes,
@@ -223,7 +231,8 @@ int tp_column_linear_bwd(const void* X, const void* W_i, const void* dY_i, void*
  *   dX_i [T x K/p] dtype = dY W_i^T (exact gradient of this rank's input block)
  *   dW_i [K/p x N] fp32  = X_i^T dY
  *   db   [N]       fp32  = sum over tokens of dY, or NULL (one rank only)
- *   accumulate as above.  workspace: TP_OP_ROW_LINEAR_BWD.
+ *   accumulate as above.  workspace: TP_OP_ROW_LINEAR_BWD bytes, required
+ *   with db; it also lets a small dW_i split its contraction, as above.
  */
 int tp_row_linear_bwd(const void* X_i, const void* W_i, const void* dY, void* dX_i,
                       float* dW_i, float* db, void* workspace, size_t workspace_bytes,

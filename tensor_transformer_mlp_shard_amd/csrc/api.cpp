@@ -152,12 +152,30 @@ size_t colsum_ws_bytes(int64_t T, int64_t N) { return round_up((size_t)colsum_ch
 // adds dY's columns while dY passes through it (GemmArgs::colsum) and leaves
 // one partial row per row of tiles; the fp32 path runs the column-sum pass.
 bool db_fused(int32_t dtype, int64_t M, int64_t N) {
-  return dtype != TP_FP32 && gemm16_colsum_rows((int)M, (int)N) > 0;
+  return dtype != TP_FP32 && gemm16_colsum_rows((int)M, (int)N, 1, false) > 0;
 }
 
 size_t db_ws_bytes(int32_t dtype, int64_t T, int64_t M, int64_t N) {
   if (!db_fused(dtype, M, N)) return colsum_ws_bytes(T, N);
-  return round_up((size_t)gemm16_colsum_rows((int)M, (int)N) * (size_t)N * 4);
+  return round_up((size_t)gemm16_colsum_rows((int)M, (int)N, (int)T, true) * (size_t)N * 4);
+}
+
+// Room for the fp32 partial of a weight gradient [M x N] whose GEMM splits its
+// contraction T in two (GemmArgs::kpart), after its bias-gradient partials.
+size_t kpart_bytes(int32_t dtype, int64_t T, int64_t M, int64_t N) {
+  return dtype != TP_FP32 && gemm16_ksplit((int)M, (int)N, (int)T) ? round_up((size_t)M * (size_t)N * 4) : 0;
+}
+
+// The MLP backward's weight-gradient scratch: the bias-gradient partials of
+// dB_i [f x h] or dA_i [h x f] (one at a time), then the K-split partial of
+// either; mlp_db_part_bytes is the offset of the latter.
+size_t mlp_db_part_bytes(int32_t dtype, int64_t T, int64_t h, int64_t f) {
+  const size_t c2 = db_ws_bytes(dtype, T, f, h), c1 = db_ws_bytes(dtype, T, h, f);
+  return c2 > c1 ? c2 : c1;
+}
+size_t mlp_wgrad_ws_bytes(int32_t dtype, int64_t T, int64_t h, int64_t f) {
+  const size_t k2 = kpart_bytes(dtype, T, f, h), k1 = kpart_bytes(dtype, T, h, f);
+  return mlp_db_part_bytes(dtype, T, h, f) + (k2 > k1 ? k2 : k1);
 }
 
 // db (+)= sum_t dY after the weight-gradient GEMM g (dW = X^T dY, B = dY) has
@@ -166,7 +184,8 @@ size_t db_ws_bytes(int32_t dtype, int64_t T, int64_t M, int64_t N) {
 hipError_t bias_grad_after_wgrad(const GemmArgs& g, const void* dY, float* db, float* part, int accumulate,
                                  int64_t T, int32_t dtype, hipStream_t s) {
   if (!db_fused(dtype, g.M, g.N)) return colsum(dY, elem_of(dtype), db, part, accumulate, T, g.N, s);
-  return sum_partials(part, db, g.N, gemm16_colsum_rows(g.M, g.N), accumulate, "colsum_finalize", s);
+  return sum_partials(part, db, g.N, gemm16_colsum_rows(g.M, g.N, g.K, g.kpart != nullptr), accumulate,
+                      "colsum_finalize", s);
 }
 
 // Shape checks shared by the attention entry points; fills p on success.
@@ -285,28 +304,27 @@ size_t tp_workspace_size(int32_t op, int64_t T, int64_t d_in, int64_t d_out, int
       if (d_in < 1 || d_in > kMaxDim) return 0;
       return colsum_ws_bytes(T, d_in);
     case TP_OP_COLUMN_LINEAR_BWD:
-      // db_i with dW_i = X^T dY_i [K x N/p]
+      // db_i with dW_i = X^T dY_i [K x N/p], then room for dW_i's K-split partial
       if (tp_size < 1 || d_in < 1 || d_out < 1 || d_in > kMaxDim || d_out > kMaxDim || d_out % tp_size) return 0;
-      return db_ws_bytes(dtype, T, d_in, d_out / tp_size);
+      return db_ws_bytes(dtype, T, d_in, d_out / tp_size) + kpart_bytes(dtype, T, d_in, d_out / tp_size);
     case TP_OP_ROW_LINEAR_BWD:
-      // db with dW_i = X_i^T dY [K/p x N]
+      // db with dW_i = X_i^T dY [K/p x N], then room for dW_i's K-split partial
       if (tp_size < 1 || d_in < 1 || d_out < 1 || d_in > kMaxDim || d_out > kMaxDim || d_in % tp_size) return 0;
-      return db_ws_bytes(dtype, T, d_in / tp_size, d_out);
+      return db_ws_bytes(dtype, T, d_in / tp_size, d_out) + kpart_bytes(dtype, T, d_in / tp_size, d_out);
     case TP_OP_MLP_SHARD_BWD: {
-      // dZ [T x f], then the partials of db2 (with dB_i [f x h]) or db1 (with dA_i [h x f]), one at a time
+      // dZ [T x f], then the partials of db2 (with dB_i [f x h]) or db1 (with dA_i [h x f]), one at a time,
+      // then room for either weight gradient's K-split partial
       if (tp_size < 1 || d_in < 1 || d_out < 1 || d_in > kMaxDim || d_out > kMaxDim || d_out % tp_size) return 0;
       const int64_t f = d_out / tp_size;
       const size_t dz = round_up((size_t)T * (size_t)f * elsize(dtype));
-      const size_t c2 = db_ws_bytes(dtype, T, f, d_in), c1 = db_ws_bytes(dtype, T, d_in, f);
-      return dz + (c2 > c1 ? c2 : c1);
+      return dz + mlp_wgrad_ws_bytes(dtype, T, d_in, f);
     }
     case TP_OP_MLP_SHARD_BWD_RECOMPUTE: {
-      // dZ, H and (when Z is not saved) Z [T x f], then the bias-gradient partials as above
+      // dZ, H and (when Z is not saved) Z [T x f], then the weight-gradient scratch as above
       if (tp_size < 1 || d_in < 1 || d_out < 1 || d_in > kMaxDim || d_out > kMaxDim || d_out % tp_size) return 0;
       const int64_t f = d_out / tp_size;
       const size_t act = round_up((size_t)T * (size_t)f * elsize(dtype));
-      const size_t c2 = db_ws_bytes(dtype, T, f, d_in), c1 = db_ws_bytes(dtype, T, d_in, f);
-      return 3 * act + (c2 > c1 ? c2 : c1);
+      return 3 * act + mlp_wgrad_ws_bytes(dtype, T, d_in, f);
     }
     case TP_OP_LAYERNORM_BWD:
       // dgamma and dbeta partial rows of every workgroup (d_in = h)
@@ -402,6 +420,8 @@ static int mlp_bwd_gemms(const void* X, const void* A_i, const void* B_i, const 
                   void* dX_i, float* dA_i, float* db1_i, float* dB_i, float* db2, void* dZ, float* part,
                   int32_t accumulate, int64_t T, int64_t h, int64_t f, int32_t dtype, hipStream_t s,
                   void* H_make = nullptr) {
+  // room for a K-split weight gradient's partial, after the bias-gradient partials
+  float* kp = (float*)((char*)part + mlp_db_part_bytes(dtype, T, h, f));
   // dZ = (dY B_i^T) * GeLU'(Z_i)          [T x f], contraction over h
   GemmArgs g1 = make_args(dY, h, B_i, h, T, f, h, dZ, f);
   g1.aux = Z_i;
@@ -415,12 +435,14 @@ static int mlp_bwd_gemms(const void* X, const void* A_i, const void* B_i, const 
   // dB_i = H_i^T dY                       [f x h], contraction over T; db2 = sum_t dY
   GemmArgs g2 = make_args(H_i, f, dY, h, f, h, T, dB_i, h);
   g2.accumulate = accumulate;
+  g2.kpart = kp;
   if (db2 && db_fused(dtype, f, h)) g2.colsum = part;
   HIP_TRY(gemm(dtype, g2, false, false, EPI_F32, s));
   if (db2) HIP_TRY(bias_grad_after_wgrad(g2, dY, db2, part, accumulate, T, dtype, s));
   // dA_i = X^T dZ                         [h x f], contraction over T; db1_i = sum_t dZ
   GemmArgs g3 = make_args(X, h, dZ, f, h, f, T, dA_i, f);
   g3.accumulate = accumulate;
+  g3.kpart = kp;
   if (db1_i && db_fused(dtype, h, f)) g3.colsum = part;
   HIP_TRY(gemm(dtype, g3, false, false, EPI_F32, s));
   if (db1_i) HIP_TRY(bias_grad_after_wgrad(g3, dZ, db1_i, part, accumulate, T, dtype, s));
@@ -563,10 +585,13 @@ int tp_column_linear_bwd(const void* X, const void* W_i, const void* dY_i, void*
   TP_TRY(check_ptrs_aligned({X, W_i, dY_i, dX_partial, dW_i, db_i, workspace}));
   const size_t need = db_i ? tp_workspace_size(TP_OP_COLUMN_LINEAR_BWD, T, K, N, tp_size, dtype) : 0;
   if (db_i && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
+  // dW_i's K split where the workspace has room for its partial (a caller without db may pass none)
+  const size_t dbb = db_ws_bytes(dtype, T, K, n), kpb = kpart_bytes(dtype, T, K, n);
+  const bool use_kp = kpb && workspace && workspace_bytes >= dbb + kpb;
   const int64_t es = elsize(dtype);
   TP_TRY(check_alias({{X, T * K * es}, {W_i, K * n * es}, {dY_i, T * n * es}},
                      {{dX_partial, T * K * es}, {dW_i, K * n * 4}, {db_i, db_i ? n * 4 : 0},
-                      {workspace, (int64_t)need}}));
+                      {workspace, (int64_t)(use_kp ? dbb + kpb : need)}}));
   hipStream_t s = (hipStream_t)stream;
   // dX = dY_i W_i^T  [T x K], contraction over n
   GemmArgs g1 = make_args(dY_i, n, W_i, n, T, K, n, dX_partial, K);
@@ -575,6 +600,7 @@ int tp_column_linear_bwd(const void* X, const void* W_i, const void* dY_i, void*
   GemmArgs g2 = make_args(X, K, dY_i, n, K, n, T, dW_i, n);
   g2.accumulate = accumulate;
   if (db_i && db_fused(dtype, K, n)) g2.colsum = (float*)workspace;
+  if (use_kp) g2.kpart = (float*)((char*)workspace + dbb);
   HIP_TRY(gemm(dtype, g2, false, false, EPI_F32, s));
   if (db_i) HIP_TRY(bias_grad_after_wgrad(g2, dY_i, db_i, (float*)workspace, accumulate, T, dtype, s));
   return TP_OK;
@@ -595,9 +621,13 @@ int tp_row_linear_bwd(const void* X_i, const void* W_i, const void* dY, void* dX
   TP_TRY(check_ptrs_aligned({X_i, W_i, dY, dX_i, dW_i, db, workspace}));
   const size_t need = db ? tp_workspace_size(TP_OP_ROW_LINEAR_BWD, T, K, N, tp_size, dtype) : 0;
   if (db && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
+  // dW_i's K split where the workspace has room for its partial (a caller without db may pass none)
+  const size_t dbb = db_ws_bytes(dtype, T, k, N), kpb = kpart_bytes(dtype, T, k, N);
+  const bool use_kp = kpb && workspace && workspace_bytes >= dbb + kpb;
   const int64_t es = elsize(dtype);
   TP_TRY(check_alias({{X_i, T * k * es}, {W_i, k * N * es}, {dY, T * N * es}},
-                     {{dX_i, T * k * es}, {dW_i, k * N * 4}, {db, db ? N * 4 : 0}, {workspace, (int64_t)need}}));
+                     {{dX_i, T * k * es}, {dW_i, k * N * 4}, {db, db ? N * 4 : 0},
+                      {workspace, (int64_t)(use_kp ? dbb + kpb : need)}}));
   hipStream_t s = (hipStream_t)stream;
   // dX_i = dY W_i^T  [T x k], contraction over N
   GemmArgs g1 = make_args(dY, N, W_i, N, T, k, N, dX_i, k);
@@ -606,6 +636,7 @@ int tp_row_linear_bwd(const void* X_i, const void* W_i, const void* dY, void* dX
   GemmArgs g2 = make_args(X_i, k, dY, N, k, N, T, dW_i, N);
   g2.accumulate = accumulate;
   if (db && db_fused(dtype, k, N)) g2.colsum = (float*)workspace;
+  if (use_kp) g2.kpart = (float*)((char*)workspace + dbb);
   HIP_TRY(gemm(dtype, g2, false, false, EPI_F32, s));
   if (db) HIP_TRY(bias_grad_after_wgrad(g2, dY, db, (float*)workspace, accumulate, T, dtype, s));
   return TP_OK;

@@ -31,10 +31,15 @@ struct GemmArgs {
   int64_t ldaux;
   int accumulate;     // EPI_F32 only
   // 16-bit EPI_F32 with B stored [K x N] only, nullable: partial column sums of
-  // B over K, gemm16_colsum_rows(M, N) rows of N floats (row r = the sum over
+  // B over K, gemm16_colsum_rows(M, N, K, kpart != nullptr) rows of N floats (row r = the sum over
   // a subset of K, the rows together cover K once).  Adding the rows gives the
   // bias gradient that goes with a weight gradient dW = X^T dY (db = sum_t dY).
   float* colsum;
+  // 16-bit EPI_F32 with both operands stored [K x *] only, nullable: room for an
+  // M x N fp32 partial.  When gemm16_ksplit(M, N, K), the launch splits K in two
+  // halves over twice the workgroups; the first half's tiles write C as usual,
+  // the second's write their partial here, and a second pass adds it to C.
+  float* kpart;
   int group_m;        // tile rows per group in the tile order (set by the launcher)
 };
 
@@ -49,7 +54,14 @@ hipError_t gemm_f32(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, 
 int64_t gemm16_work_items(int64_t M, int64_t N);
 int64_t gemm_f32_work_items(int64_t M, int64_t N);
 
-// Rows of GemmArgs::colsum written by the 16-bit GEMM for an M x N product.
-int gemm16_colsum_rows(int M, int N);
+// Rows of GemmArgs::colsum written by the 16-bit GEMM for an M x N product with
+// contraction K, with (kpart) or without room for a K split's partial.
+int gemm16_colsum_rows(int M, int N, int K, bool kpart);
+
+// Whether the 16-bit weight-gradient GEMM (EPI_F32, both operands [K x *])
+// splits K in two for an M x N product with contraction K, given kpart: when
+// its tiles would fill at most half of the CUs and K >= 2048 (each half keeps
+// at least 32 K steps).
+bool gemm16_ksplit(int M, int N, int K);
 
 }  // namespace tps

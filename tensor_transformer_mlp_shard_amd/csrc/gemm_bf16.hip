@@ -286,9 +286,10 @@ struct BColSum {
   int next;   // next K step this tile adds (wave-uniform)
   bool on;    // wave-uniform: sums wanted and this wave takes part
 
-  __device__ __forceinline__ void init(const GemmArgs& g, int wave, int tm) {
+  // kbeg: the first K step of this workgroup's range (0, or the second half's).
+  __device__ __forceinline__ void init(const GemmArgs& g, int wave, int tm, int tiles_m, int kbeg) {
     on = g.colsum != nullptr && wave * 64 < LANES;
-    next = tm;
+    next = kbeg > tm ? tm + (kbeg - tm + tiles_m - 1) / tiles_m * tiles_m : tm;
 #pragma unroll
     for (int e = 0; e < 4; ++e) s[e] = 0.0f;
   }
@@ -311,7 +312,8 @@ struct BColSum {
 #pragma unroll
       for (int e = 0; e < 4; ++e) s[e] += (float)v[u][e];
   }
-  // Add the 4 lanes of each column quad and write the tile's partial row.
+  // Add the 4 lanes of each column quad and write the tile's partial row (row
+  // tm, or tiles_m + tm for the second K half of a split launch).
   __device__ __forceinline__ void finish(const GemmArgs& g, int tm, int n0, int wave, int lane) {
     if (!on) return;
 #pragma unroll
@@ -504,11 +506,22 @@ gemm_kernel(GemmArgs g) {
 
   const int tiles_m = (g.M + C::BM - 1) / C::BM;
   const int tiles_n = (g.N + C::BN - 1) / C::BN;
+  // K split (weight gradients whose tiles fill at most half of the CUs, with
+  // g.kpart set by the launcher): workgroups [tiles, 2 tiles) take the second
+  // half of the K steps and write their partial to g.kpart.
+  int bid = (int)blockIdx.x, part = 0;
+  if (EPI == EPI_F32 && g.kpart != nullptr && bid >= tiles_m * tiles_n) {
+    bid -= tiles_m * tiles_n;
+    part = 1;
+  }
   int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, g.group_m, tm, tn);
+  tile_coords(bid, tiles_m, tiles_n, g.group_m, tm, tn);
   const int m0 = tm * C::BM;
   const int n0 = tn * C::BN;
-  const int nk = (g.K + KT - 1) / KT;
+  const int nk_all = (g.K + KT - 1) / KT;
+  const bool ksplit = EPI == EPI_F32 && g.kpart != nullptr;
+  const int kbeg = ksplit && part ? nk_all / 2 : 0;             // this workgroup's K steps [kbeg, nk)
+  const int nk = ksplit && !part ? nk_all / 2 : nk_all;
 
   if constexpr (C::NPROD > 0) {
     if (wave >= C::NCONS) {
@@ -518,10 +531,10 @@ gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int p = 0; p < PREF; ++p)
 #pragma unroll
-        for (int u = 0; u < NVM; ++u) cp.issue(p, u);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step 0 landed
+        for (int u = 0; u < NVM; ++u) cp.issue(kbeg + p, u);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step kbeg landed
       __syncthreads();
-      for (int kt = 0; kt < nk; ++kt) {
+      for (int kt = kbeg; kt < nk; ++kt) {
 #pragma unroll
         for (int u = 0; u < NVM; ++u) cp.issue(kt + PREF, u);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step kt+1 landed
@@ -537,7 +550,7 @@ gemm_kernel(GemmArgs g) {
   rd.init(wave, lane);
   constexpr bool CS = C::CSUM && !BKC && EPI == EPI_F32;   // B stored [K x N]: its column sums can ride along
   BColSum<C, E> cs;
-  if constexpr (CS) cs.init(g, wave, tm);
+  if constexpr (CS) cs.init(g, wave, tm, tiles_m, kbeg);
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -549,10 +562,10 @@ gemm_kernel(GemmArgs g) {
   auto mfma = [&](const V8* fa_, const V8* fb_, int i, int j) { acc[i][j] = mfma32(fb_[j], fa_[i], acc[i][j]); };
 
   if constexpr (C::NPROD > 0) {
-    __syncthreads();  // step 0 is in LDS
+    __syncthreads();  // step kbeg is in LDS
     V8 fa[2][FM], fb[2][FN];
-    rd.load(smem, 0, 0, fa[0], fb[0]);
-    for (int kt = 0; kt < nk; ++kt) {
+    rd.load(smem, kbeg, 0, fa[0], fb[0]);
+    for (int kt = kbeg; kt < nk; ++kt) {
       if constexpr (AK && BKC) __builtin_amdgcn_s_setprio(1);  // see the shared kernel below
 #pragma unroll
       for (int s = 0; s < NS - 1; ++s) {
@@ -600,14 +613,14 @@ gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int p = 0; p < PREF; ++p)
 #pragma unroll
-        for (int u = 0; u < NVM; ++u) cp.issue(p, u);
+        for (int u = 0; u < NVM; ++u) cp.issue(kbeg + p, u);
     }
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step 0 landed
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step kbeg landed
     __syncthreads();
     constexpr int PRE_MF = FM * FN * (NS - 1) + FM_HALF * FN;   // MFMAs before the barrier
     static_assert(PRE_MF >= NVM, "not enough MFMAs to spread the copies over");
     V8 fa[FM], fb[FN];
-    for (int kt = 0; kt < nk; ++kt) {
+    for (int kt = kbeg; kt < nk; ++kt) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         rd.load(smem, kt, s, fa, fb);
@@ -639,8 +652,14 @@ gemm_kernel(GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no copy into this workgroup's LDS outlives it
   }
 
-  if constexpr (CS) cs.finish(g, tm, n0, wave, lane);
+  if constexpr (CS) cs.finish(g, tm + part * tiles_m, n0, wave, lane);
   __syncthreads();  // every consumer is done with the ring (producer copies have drained)
+  if (EPI == EPI_F32 && part) {
+    // the second K half: its partial to g.kpart (ld = N), added to C afterwards
+    g.C = g.kpart;
+    g.ldc = g.N;
+    g.accumulate = 0;
+  }
   epilogue<C, EPI, E>(g, acc, m0, n0, wave, lane, smem);
 }
 
@@ -693,8 +712,26 @@ hipError_t launch_tile(const GemmArgs& g_in, hipStream_t s, const char** name) {
   // other kernels ran 1-3% slower with either.
   if (!AK && !BKC && C::BM == 192 && 2 * g.group_m <= tiles_m) g.group_m *= 2;
   if (AK && BKC && C::BM == 256 && C::BN == 384 && g.group_m > 1) g.group_m /= 2;
-  hipLaunchKernelGGL((gemm_kernel<C, AK, BKC, EPI, E>), dim3(tiles_m * tiles_n), dim3(C::NT), 0, s, g);
+  const int parts = (EPI == EPI_F32 && g.kpart != nullptr) ? 2 : 1;   // K split: two workgroups per tile
+  hipLaunchKernelGGL((gemm_kernel<C, AK, BKC, EPI, E>), dim3(tiles_m * tiles_n * parts), dim3(C::NT), 0, s, g);
   return hipGetLastError();
+}
+
+// The second pass of a K-split weight gradient: C[M x N] (row stride ldc) +=
+// P[M x N] (row stride N), 4 fp32 per work-item.  C then holds (C's first-half
+// value) + (second half), one fixed order.
+__global__ void __launch_bounds__(256) kpart_add_kernel(float* C, int64_t ldc, const float* P, int M, int N) {
+  const int64_t nq = N / 4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)M * nq) return;
+  const int64_t r = i / nq, c = (i - r * nq) * 4;
+  f32x4 v = *(const f32x4*)(C + r * ldc + c);
+  const f32x4 q = *(const f32x4*)(P + r * N + c);
+  v[0] += q[0];
+  v[1] += q[1];
+  v[2] += q[2];
+  v[3] += q[3];
+  *(f32x4*)(C + r * ldc + c) = v;
 }
 
 // Tile shape: the one with the least estimated time, counting whole waves of
@@ -743,26 +780,37 @@ hipError_t gemm16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hi
   LaunchInfo info;
   info.name = "gemm16";
   info.flops = 2.0 * g.M * (double)g.N * g.K;
-  const double out_bytes = (epi == EPI_F32 ? 4.0 * (g.accumulate ? 2 : 1) : 2.0) * g.M * (double)g.N;
+  // K split of a weight gradient whose tiles fill at most half of the CUs
+  GemmArgs gk = g;
+  const bool split = epi == EPI_F32 && !a_kcontig && !b_kcontig && g.kpart != nullptr && gemm16_ksplit(g.M, g.N, g.K);
+  if (!split) gk.kpart = nullptr;
+  const double out_bytes = (epi == EPI_F32 ? 4.0 * (g.accumulate ? 2 : 1) : 2.0) * g.M * (double)g.N +
+                           (split ? 4.0 * 4.0 * g.M * (double)g.N : 0.0);   // partial out and in, C again
   info.bytes = 2.0 * ((double)g.M * g.K + (double)g.K * g.N) + out_bytes +
                ((epi == EPI_BIAS_GELU && g.C2) ? 2.0 * g.M * (double)g.N : 0.0) +
                (epi == EPI_DGELU ? 2.0 * g.M * (double)g.N : 0.0) +
                (epi == EPI_DGELU_H ? 4.0 * g.M * (double)g.N : 0.0) +
-               (g.colsum ? 4.0 * g.N * (double)gemm16_colsum_rows(g.M, g.N) : 0.0);
+               (g.colsum ? 4.0 * g.N * (double)gemm16_colsum_rows(g.M, g.N, g.K, split) : 0.0);
   // Instantiated layout / epilogue pairs: forward (NN), data gradient (NT) and
   // weight gradient (TN).
   hipError_t e = hipErrorInvalidValue;
   // column sums: B stored [K x N], fp32 out, a tile that carries them
-  if (g.colsum != nullptr && (b_kcontig || epi != EPI_F32 || gemm16_colsum_rows(g.M, g.N) == 0)) return e;
+  if (g.colsum != nullptr && (b_kcontig || epi != EPI_F32 || gemm16_colsum_rows(g.M, g.N, g.K, split) == 0)) return e;
   trace_begin(s);
-  if (a_kcontig && !b_kcontig && epi == EPI_STORE) e = launch_shape<true, false, EPI_STORE, E>(g, s, &info.name);
+  if (a_kcontig && !b_kcontig && epi == EPI_STORE) e = launch_shape<true, false, EPI_STORE, E>(gk, s, &info.name);
   else if (a_kcontig && !b_kcontig && epi == EPI_BIAS_GELU)
-    e = launch_shape<true, false, EPI_BIAS_GELU, E>(g, s, &info.name);
-  else if (a_kcontig && b_kcontig && epi == EPI_STORE) e = launch_shape<true, true, EPI_STORE, E>(g, s, &info.name);
-  else if (a_kcontig && b_kcontig && epi == EPI_DGELU) e = launch_shape<true, true, EPI_DGELU, E>(g, s, &info.name);
+    e = launch_shape<true, false, EPI_BIAS_GELU, E>(gk, s, &info.name);
+  else if (a_kcontig && b_kcontig && epi == EPI_STORE) e = launch_shape<true, true, EPI_STORE, E>(gk, s, &info.name);
+  else if (a_kcontig && b_kcontig && epi == EPI_DGELU) e = launch_shape<true, true, EPI_DGELU, E>(gk, s, &info.name);
   else if (a_kcontig && b_kcontig && epi == EPI_DGELU_H && g.C2 != nullptr)
-    e = launch_shape<true, true, EPI_DGELU_H, E>(g, s, &info.name);
-  else if (!a_kcontig && !b_kcontig && epi == EPI_F32) e = launch_shape<false, false, EPI_F32, E>(g, s, &info.name);
+    e = launch_shape<true, true, EPI_DGELU_H, E>(gk, s, &info.name);
+  else if (!a_kcontig && !b_kcontig && epi == EPI_F32) e = launch_shape<false, false, EPI_F32, E>(gk, s, &info.name);
+  if (split && e == hipSuccess) {
+    const int64_t n = (int64_t)g.M * (g.N / 4);
+    hipLaunchKernelGGL(kpart_add_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (float*)g.C, g.ldc,
+                       (const float*)g.kpart, g.M, g.N);
+    e = hipGetLastError();
+  }
   trace_end(s, info);
   return e;
 }
@@ -791,10 +839,16 @@ int64_t gemm16_work_items(int64_t M, int64_t N) {
   return (M + t.bm - 1) / t.bm * ((N + t.bn - 1) / t.bn) * threads;
 }
 
-int gemm16_colsum_rows(int M, int N) {
+bool gemm16_ksplit(int M, int N, int K) {
+  const TileChoice t = choose_tile(M, N);
+  const int64_t tiles = (int64_t)((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+  return 2 * tiles <= 256 && K >= 2048;   // at least 32 K steps per half
+}
+
+int gemm16_colsum_rows(int M, int N, int K, bool kpart) {
   const TileChoice t = choose_tile(M, N);
   if (t.bm * t.bn >= 256 * 384) return 0;   // that tile does not carry the column sums (Cfg::CSUM)
-  return (M + t.bm - 1) / t.bm;
+  return (M + t.bm - 1) / t.bm * (kpart && gemm16_ksplit(M, N, K) ? 2 : 1);
 }
 
 }  // namespace tps

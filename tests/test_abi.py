@@ -299,3 +299,24 @@ def test_noalloc_rejects_problems_beyond_its_scratch(lib):
     # the ordinary checks come first
     assert lib.tp_mlp_shard_bwd_noalloc(X, A, B, Z, H, dY, dX, dA, db1, dB, None, 2, 4096, 2048, 8192, 1, 1, S) == -9
     assert lib.tp_mlp_shard_bwd_noalloc(X, A, B, Z, H, dY, X, dA, db1, dB, None, 0, 4096, 2048, 8192, 1, 1, S) == -6
+
+
+def test_workspace_holds_the_k_split_partial(lib):
+    """A 16-bit weight gradient whose tiles fill at most half of the CUs splits
+    its contraction in two; the workspace then holds its M x N fp32 partial
+    besides the bias-gradient rows.  Large weight gradients and the fp32 path do
+    not split."""
+    bf16, fp32 = 0, 1
+    # column shard dW [1024 x 1024], contraction 4096: 64 tiles of 128 x 128
+    need = lib.tp_workspace_size(_native.TP_OP_COLUMN_LINEAR_BWD, 4096, 1024, 2048, 2, bf16)
+    assert need >= 1024 * 1024 * 4
+    # row shard dW [512 x 2048], contraction 2080 (65 steps of 32)
+    assert lib.tp_workspace_size(_native.TP_OP_ROW_LINEAR_BWD, 2080, 1024, 2048, 2, bf16) >= 512 * 2048 * 4
+    # MLP at GPT h=1024 TP=2: dZ [4096 x 2048] bf16, then room for a [2048 x 1024] partial
+    assert lib.tp_workspace_size(_native.TP_OP_MLP_SHARD_BWD, 4096, 1024, 4096, 2, bf16) >= \
+        4096 * 2048 * 2 + 2048 * 1024 * 4
+    # 175B QKV weight gradient [12288 x 4608]: 768 tiles, no split
+    assert lib.tp_workspace_size(_native.TP_OP_COLUMN_LINEAR_BWD, 8192, 12288, 36864, 8, bf16) < 12288 * 4608
+    # a contraction under 64 steps of 32 does not split
+    assert lib.tp_workspace_size(_native.TP_OP_COLUMN_LINEAR_BWD, 2016, 1024, 2048, 2, bf16) < 1024 * 1024
+    assert lib.tp_workspace_size(_native.TP_OP_COLUMN_LINEAR_BWD, 4096, 1024, 2048, 2, fp32) < 1024 * 1024 * 4
