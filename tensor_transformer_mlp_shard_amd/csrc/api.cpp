@@ -129,6 +129,23 @@ hipError_t gemm(int32_t dtype, const GemmArgs& g, bool ak, bool bk, Epi epi, hip
   return dtype == TP_FP16 ? gemm_f16(g, ak, bk, epi, s) : gemm_bf16(g, ak, bk, epi, s);
 }
 
+// g1 and g2 in one launch where the 16-bit GEMM pairs them (see gemm.h);
+// hipErrorNotSupported, with nothing launched, where it does not.
+hipError_t gemm_pair(int32_t dtype, const GemmArgs& g1, Epi epi1, const GemmArgs& g2, hipStream_t s) {
+  if (dtype == TP_FP32) return hipErrorNotSupported;
+  return dtype == TP_FP16 ? gemm_f16_pair(g1, epi1, g2, s) : gemm_bf16_pair(g1, epi1, g2, s);
+}
+
+// The data gradient g1 and the independent weight gradient g2 of a backward:
+// one paired launch where it applies, else one after the other.
+hipError_t gemm_dgrad_wgrad(int32_t dtype, const GemmArgs& g1, Epi epi1, const GemmArgs& g2, hipStream_t s) {
+  const hipError_t e = gemm_pair(dtype, g1, epi1, g2, s);
+  if (e != hipErrorNotSupported) return e;
+  const hipError_t e1 = gemm(dtype, g1, true, true, epi1, s);
+  if (e1 != hipSuccess) return e1;
+  return gemm(dtype, g2, false, false, EPI_F32, s);
+}
+
 GemmArgs make_args(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N, int64_t K,
                    void* C, int64_t ldc) {
   GemmArgs g;
@@ -431,13 +448,18 @@ static int mlp_bwd_gemms(const void* X, const void* A_i, const void* B_i, const 
     g1.ldc2 = f;
     H_i = H_make;
   }
-  HIP_TRY(gemm(dtype, g1, true, true, H_make ? EPI_DGELU_H : EPI_DGELU, s));
   // dB_i = H_i^T dY                       [f x h], contraction over T; db2 = sum_t dY
   GemmArgs g2 = make_args(H_i, f, dY, h, f, h, T, dB_i, h);
   g2.accumulate = accumulate;
   g2.kpart = kp;
   if (db2 && db_fused(dtype, f, h)) g2.colsum = part;
-  HIP_TRY(gemm(dtype, g2, false, false, EPI_F32, s));
+  if (H_make) {
+    // H comes out of the dZ GEMM: dB_i after it
+    HIP_TRY(gemm(dtype, g1, true, true, EPI_DGELU_H, s));
+    HIP_TRY(gemm(dtype, g2, false, false, EPI_F32, s));
+  } else {
+    HIP_TRY(gemm_dgrad_wgrad(dtype, g1, EPI_DGELU, g2, s));
+  }
   if (db2) HIP_TRY(bias_grad_after_wgrad(g2, dY, db2, part, accumulate, T, dtype, s));
   // dA_i = X^T dZ                         [h x f], contraction over T; db1_i = sum_t dZ
   GemmArgs g3 = make_args(X, h, dZ, f, h, f, T, dA_i, f);
@@ -595,13 +617,12 @@ int tp_column_linear_bwd(const void* X, const void* W_i, const void* dY_i, void*
   hipStream_t s = (hipStream_t)stream;
   // dX = dY_i W_i^T  [T x K], contraction over n
   GemmArgs g1 = make_args(dY_i, n, W_i, n, T, K, n, dX_partial, K);
-  HIP_TRY(gemm(dtype, g1, true, true, EPI_STORE, s));
   // dW_i = X^T dY_i  [K x n], contraction over T; db_i = sum_t dY_i
   GemmArgs g2 = make_args(X, K, dY_i, n, K, n, T, dW_i, n);
   g2.accumulate = accumulate;
   if (db_i && db_fused(dtype, K, n)) g2.colsum = (float*)workspace;
   if (use_kp) g2.kpart = (float*)((char*)workspace + dbb);
-  HIP_TRY(gemm(dtype, g2, false, false, EPI_F32, s));
+  HIP_TRY(gemm_dgrad_wgrad(dtype, g1, EPI_STORE, g2, s));
   if (db_i) HIP_TRY(bias_grad_after_wgrad(g2, dY_i, db_i, (float*)workspace, accumulate, T, dtype, s));
   return TP_OK;
 }
@@ -631,13 +652,12 @@ int tp_row_linear_bwd(const void* X_i, const void* W_i, const void* dY, void* dX
   hipStream_t s = (hipStream_t)stream;
   // dX_i = dY W_i^T  [T x k], contraction over N
   GemmArgs g1 = make_args(dY, N, W_i, N, T, k, N, dX_i, k);
-  HIP_TRY(gemm(dtype, g1, true, true, EPI_STORE, s));
   // dW_i = X_i^T dY  [k x N], contraction over T; db = sum_t dY
   GemmArgs g2 = make_args(X_i, k, dY, N, k, N, T, dW_i, N);
   g2.accumulate = accumulate;
   if (db && db_fused(dtype, k, N)) g2.colsum = (float*)workspace;
   if (use_kp) g2.kpart = (float*)((char*)workspace + dbb);
-  HIP_TRY(gemm(dtype, g2, false, false, EPI_F32, s));
+  HIP_TRY(gemm_dgrad_wgrad(dtype, g1, EPI_STORE, g2, s));
   if (db) HIP_TRY(bias_grad_after_wgrad(g2, dY, db, (float*)workspace, accumulate, T, dtype, s));
   return TP_OK;
 }

@@ -49,6 +49,17 @@ hipError_t gemm_bf16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi,
 hipError_t gemm_f16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s);
 hipError_t gemm_f32(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s);
 
+// Two independent products in one launch: g1 a data gradient (both operands
+// K-contiguous, epi1 EPI_STORE or EPI_DGELU), g2 a weight gradient (both
+// operands [K x *], EPI_F32, its column sums optional, never K-split).
+// Returns hipErrorNotSupported, having launched nothing, unless
+// gemm16_pairs(g1.M, g1.N, g1.K, g2.M, g2.N, g2.K, ...) holds; the results are
+// those of the two launches made one after the other.
+hipError_t gemm_bf16_pair(const GemmArgs& g1, Epi epi1, const GemmArgs& g2, hipStream_t s);
+hipError_t gemm_f16_pair(const GemmArgs& g1, Epi epi1, const GemmArgs& g2, hipStream_t s);
+// Whether the pair runs as one launch (split2: g2.kpart is set).
+bool gemm16_pairs(int M1, int N1, int K1, int M2, int N2, int K2, bool split2);
+
 // Work-items of the launch gemm_bf16 / gemm_f16 (resp. gemm_f32) makes for an
 // M x N product: every launch must stay within the 32-bit dispatch size.
 int64_t gemm16_work_items(int64_t M, int64_t N);

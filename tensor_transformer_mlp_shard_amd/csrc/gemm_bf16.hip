@@ -53,6 +53,7 @@
 #include "gemm.h"
 #include "lds_dma.h"
 
+#include <algorithm>
 #include <string>
 
 namespace tps {
@@ -484,10 +485,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16 (&acc)[C::FM]
   }
 }
 
+// One workgroup's tile: workgroup id bid0 of the product g, LDS ring smem.
 template <class C, bool AK, bool BKC, int EPI, typename E>
-__global__ void __attribute__((amdgpu_flat_work_group_size(C::NT, C::NT),
-                               amdgpu_waves_per_eu(C::WAVES_PER_EU, C::WAVES_PER_EU)))
-gemm_kernel(GemmArgs g) {
+__device__ __forceinline__ void gemm_tile(GemmArgs g, int bid0, char* smem) {
   using V8 = typename Vec<E>::v8;
   constexpr int FM = C::FM, FN = C::FN, NVM = C::NVM, PREF = C::PREF;
   constexpr int NS = KT / 16;             // 16-wide k slices per step
@@ -499,8 +499,6 @@ gemm_kernel(GemmArgs g) {
   // faster (and the other layouts 1% slower).
   constexpr int FM_HALF = (C::NPROD == 0 && !AK && !BKC) ? 1 : (FM / 2 > 0 ? FM / 2 : 1);
 
-  __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGE];
-
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -509,7 +507,7 @@ gemm_kernel(GemmArgs g) {
   // K split (weight gradients whose tiles fill at most half of the CUs, with
   // g.kpart set by the launcher): workgroups [tiles, 2 tiles) take the second
   // half of the K steps and write their partial to g.kpart.
-  int bid = (int)blockIdx.x, part = 0;
+  int bid = bid0, part = 0;
   if (EPI == EPI_F32 && g.kpart != nullptr && bid >= tiles_m * tiles_n) {
     bid -= tiles_m * tiles_n;
     part = 1;
@@ -663,6 +661,29 @@ gemm_kernel(GemmArgs g) {
   epilogue<C, EPI, E>(g, acc, m0, n0, wave, lane, smem);
 }
 
+template <class C, bool AK, bool BKC, int EPI, typename E>
+__global__ void __attribute__((amdgpu_flat_work_group_size(C::NT, C::NT),
+                               amdgpu_waves_per_eu(C::WAVES_PER_EU, C::WAVES_PER_EU)))
+gemm_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) char smem[C::NSTAGE * C::STAGE];
+  gemm_tile<C, AK, BKC, EPI, E>(g, (int)blockIdx.x, smem);
+}
+
+// Two independent products in one launch: workgroups [0, n1) take the tiles
+// of g1, the rest those of g2.  The dispatcher hands out workgroups in id
+// order, so g1's (long) tiles start first, each on a CU of its own, and g2's
+// fill the other CUs and then those that g1 releases.
+template <class C1, bool AK1, bool BKC1, int EPI1, class C2, bool AK2, bool BKC2, int EPI2, typename E>
+__global__ void __attribute__((amdgpu_flat_work_group_size(C1::NT, C1::NT),
+                               amdgpu_waves_per_eu(C1::WAVES_PER_EU, C1::WAVES_PER_EU)))
+gemm_pair_kernel(GemmArgs g1, GemmArgs g2, int n1) {
+  static_assert(C1::NT == C2::NT && C1::WAVES_PER_EU == C2::WAVES_PER_EU, "one workgroup shape");
+  constexpr int L1 = C1::NSTAGE * C1::STAGE, L2 = C2::NSTAGE * C2::STAGE;
+  __shared__ __attribute__((aligned(1024))) char smem[L1 > L2 ? L1 : L2];
+  if ((int)blockIdx.x < n1) gemm_tile<C1, AK1, BKC1, EPI1, E>(g1, (int)blockIdx.x, smem);
+  else gemm_tile<C2, AK2, BKC2, EPI2, E>(g2, (int)blockIdx.x - n1, smem);
+}
+
 // Tile menu: split kernels (8 consumer + 4 producer waves) and shared kernels
 // (8 waves that copy and compute).
 using T256x192 = Cfg<256, 192, 4, 4>;
@@ -699,19 +720,25 @@ int choose_group_m(int tiles_m, int bm, int bn) {
   return best;
 }
 
-template <class C, bool AK, bool BKC, int EPI, typename E>
-hipError_t launch_tile(const GemmArgs& g_in, hipStream_t s, const char** name) {
-  *name = kname<C, AK, BKC, EPI, E>();
-  GemmArgs g = g_in;
-  const int tiles_m = (g.M + C::BM - 1) / C::BM, tiles_n = (g.N + C::BN - 1) / C::BN;
-  g.group_m = choose_group_m(tiles_m, C::BM, C::BN);
+template <class C, bool AK, bool BKC>
+int group_for(int tiles_m) {
+  int gm = choose_group_m(tiles_m, C::BM, C::BN);
   // Measured exceptions to the estimate: the 192 x 384 weight-gradient tile
   // (both operands M/N-contiguous) runs 2% faster with twice the height
   // (longer contiguous runs of each token row per K step), the 256 x 384
   // data-gradient tile (both K-contiguous) 0.6-0.9% faster with half; the
   // other kernels ran 1-3% slower with either.
-  if (!AK && !BKC && C::BM == 192 && 2 * g.group_m <= tiles_m) g.group_m *= 2;
-  if (AK && BKC && C::BM == 256 && C::BN == 384 && g.group_m > 1) g.group_m /= 2;
+  if (!AK && !BKC && C::BM == 192 && 2 * gm <= tiles_m) gm *= 2;
+  if (AK && BKC && C::BM == 256 && C::BN == 384 && gm > 1) gm /= 2;
+  return gm;
+}
+
+template <class C, bool AK, bool BKC, int EPI, typename E>
+hipError_t launch_tile(const GemmArgs& g_in, hipStream_t s, const char** name) {
+  *name = kname<C, AK, BKC, EPI, E>();
+  GemmArgs g = g_in;
+  const int tiles_m = (g.M + C::BM - 1) / C::BM, tiles_n = (g.N + C::BN - 1) / C::BN;
+  g.group_m = group_for<C, AK, BKC>(tiles_m);
   const int parts = (EPI == EPI_F32 && g.kpart != nullptr) ? 2 : 1;   // K split: two workgroups per tile
   hipLaunchKernelGGL((gemm_kernel<C, AK, BKC, EPI, E>), dim3(tiles_m * tiles_n * parts), dim3(C::NT), 0, s, g);
   return hipGetLastError();
@@ -815,7 +842,89 @@ hipError_t gemm16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hi
   return e;
 }
 
+// Pairing (gemm_pair_kernel) of a data-gradient product g1 (both operands
+// K-contiguous) with an independent weight gradient g2 (both operands [K x *],
+// fp32 out).  Alone, a g1 of one wave of 256 x 192 tiles (one per CU, the
+// tile with the most bytes per FLOP the launcher picks for long contractions
+// like the MLP's dH and the out-projection's dX) runs well below the big
+// tiles' rate; paired, g1 takes 256 x 384 tiles on at most half of the CUs
+// and g2 runs beside it.  Paired when the estimated time, in K steps of a
+// 256 x 384 tile, is lower: g1 alone as 256 x 192 tiles costs 0.6 of its
+// 256 x 384 time (measured rates), the pair the longer of g1's 256 x 384
+// tiles and both products' work spread over all CUs.
+constexpr int kPairCUs = 256;
+
+bool pair_plan(const GemmArgs& g1, const GemmArgs& g2, TileChoice* t2) {
+  const TileChoice t1 = choose_tile(g1.M, g1.N);
+  if (t1.bm != 256 || t1.bn != 192) return false;
+  const int64_t small1 = (int64_t)((g1.M + 255) / 256) * ((g1.N + 191) / 192);
+  const int64_t n1 = (int64_t)((g1.M + 255) / 256) * ((g1.N + 383) / 384);
+  if (small1 > kPairCUs || 2 * n1 > kPairCUs) return false;
+  *t2 = choose_tile(g2.M, g2.N);
+  if (!((t2->bm == 256 || t2->bm == 192) && t2->bn == 384)) return false;
+  if (g2.kpart != nullptr && gemm16_ksplit(g2.M, g2.N, g2.K)) return false;
+  const int64_t n2 = (int64_t)((g2.M + t2->bm - 1) / t2->bm) * ((g2.N + 383) / 384);
+  if ((n1 + n2) * 512 > (int64_t(1) << 32) - 1) return false;
+  const double T1 = (g1.K + KT - 1) / KT;
+  const double W2 = (double)n2 * ((g2.K + KT - 1) / KT) * (t2->bm / 256.0);
+  const double alone = 0.6 * T1 + W2 / kPairCUs;
+  const double paired = std::max(T1, (n1 * T1 + W2) / kPairCUs);
+  return paired < 0.97 * alone;
+}
+
+template <class C2, int EPI1, typename E>
+hipError_t launch_pair(const GemmArgs& g1_in, const GemmArgs& g2_in, hipStream_t s) {
+  GemmArgs g1 = g1_in, g2 = g2_in;
+  g2.kpart = nullptr;
+  const int tm1 = (g1.M + 255) / 256, tn1 = (g1.N + 383) / 384;
+  const int tm2 = (g2.M + C2::BM - 1) / C2::BM, tn2 = (g2.N + C2::BN - 1) / C2::BN;
+  g1.group_m = group_for<T256x384, true, true>(tm1);
+  g2.group_m = group_for<C2, false, false>(tm2);
+  const int n1 = tm1 * tn1;
+  hipLaunchKernelGGL((gemm_pair_kernel<T256x384, true, true, EPI1, C2, false, false, EPI_F32, E>),
+                     dim3(n1 + tm2 * tn2), dim3(T256x384::NT), 0, s, g1, g2, n1);
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t gemm16_pair(const GemmArgs& g1, Epi epi1, const GemmArgs& g2, hipStream_t s) {
+  TileChoice t2;
+  if (epi1 != EPI_STORE && epi1 != EPI_DGELU) return hipErrorNotSupported;
+  if (!pair_plan(g1, g2, &t2)) return hipErrorNotSupported;
+  LaunchInfo info;
+  info.name = t2.bm == 256 ? (epi1 == EPI_DGELU ? "gemm_pair_nt_dgelu_256x384+tn_f32_256x384" : "gemm_pair_nt_store_256x384+tn_f32_256x384")
+                           : (epi1 == EPI_DGELU ? "gemm_pair_nt_dgelu_256x384+tn_f32_192x384" : "gemm_pair_nt_store_256x384+tn_f32_192x384");
+  info.flops = 2.0 * g1.M * (double)g1.N * g1.K + 2.0 * g2.M * (double)g2.N * g2.K;
+  info.bytes = 2.0 * ((double)g1.M * g1.K + (double)g1.K * g1.N) + 2.0 * g1.M * (double)g1.N * (epi1 == EPI_DGELU ? 2 : 1) +
+               2.0 * ((double)g2.M * g2.K + (double)g2.K * g2.N) + 4.0 * g2.M * (double)g2.N * (g2.accumulate ? 2 : 1) +
+               (g2.colsum ? 4.0 * g2.N * (double)gemm16_colsum_rows(g2.M, g2.N, g2.K, false) : 0.0);
+  trace_begin(s);
+  hipError_t e;
+  if (t2.bm == 256) e = epi1 == EPI_DGELU ? launch_pair<T256x384, EPI_DGELU, E>(g1, g2, s) : launch_pair<T256x384, EPI_STORE, E>(g1, g2, s);
+  else e = epi1 == EPI_DGELU ? launch_pair<T192x384, EPI_DGELU, E>(g1, g2, s) : launch_pair<T192x384, EPI_STORE, E>(g1, g2, s);
+  trace_end(s, info);
+  return e;
+}
+
 }  // namespace
+
+hipError_t gemm_bf16_pair(const GemmArgs& g1, Epi epi1, const GemmArgs& g2, hipStream_t s) {
+  return gemm16_pair<bf16>(g1, epi1, g2, s);
+}
+
+hipError_t gemm_f16_pair(const GemmArgs& g1, Epi epi1, const GemmArgs& g2, hipStream_t s) {
+  return gemm16_pair<f16>(g1, epi1, g2, s);
+}
+
+bool gemm16_pairs(int M1, int N1, int K1, int M2, int N2, int K2, bool split2) {
+  GemmArgs g1{}, g2{};
+  g1.M = M1; g1.N = N1; g1.K = K1;
+  g2.M = M2; g2.N = N2; g2.K = K2;
+  float dummy;
+  g2.kpart = split2 ? &dummy : nullptr;
+  TileChoice t2;
+  return pair_plan(g1, g2, &t2);
+}
 
 hipError_t gemm_bf16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, Epi epi, hipStream_t s) {
   return gemm16<bf16>(g, a_kcontig, b_kcontig, epi, s);
