@@ -872,6 +872,14 @@ bool pair_plan(const GemmArgs& g1, const GemmArgs& g2, TileChoice* t2) {
   return paired < 0.97 * alone;
 }
 
+template <class C1, int EPI1, class C2, typename E>
+std::string pair_name() {
+  // the two kernels' names after their "gemm_<type>_" prefix
+  const std::string n1 = kname<C1, true, true, EPI1, E>(), n2 = kname<C2, false, false, EPI_F32, E>();
+  return std::string("gemm_") + Vec<E>::name + "_pair_" + n1.substr(n1.find('_', 5) + 1) + "+" +
+         n2.substr(n2.find('_', 5) + 1);
+}
+
 template <class C2, int EPI1, typename E>
 hipError_t launch_pair(const GemmArgs& g1_in, const GemmArgs& g2_in, hipStream_t s) {
   GemmArgs g1 = g1_in, g2 = g2_in;
@@ -891,9 +899,12 @@ hipError_t gemm16_pair(const GemmArgs& g1, Epi epi1, const GemmArgs& g2, hipStre
   TileChoice t2;
   if (epi1 != EPI_STORE && epi1 != EPI_DGELU) return hipErrorNotSupported;
   if (!pair_plan(g1, g2, &t2)) return hipErrorNotSupported;
+  // trace name, e.g. gemm_bf16_pair_nt_dgelu_256x384+tn_f32_256x384
+  static const std::string names[2][2] = {
+      {pair_name<T256x384, EPI_DGELU, T256x384, E>(), pair_name<T256x384, EPI_STORE, T256x384, E>()},
+      {pair_name<T256x384, EPI_DGELU, T192x384, E>(), pair_name<T256x384, EPI_STORE, T192x384, E>()}};
   LaunchInfo info;
-  info.name = t2.bm == 256 ? (epi1 == EPI_DGELU ? "gemm_pair_nt_dgelu_256x384+tn_f32_256x384" : "gemm_pair_nt_store_256x384+tn_f32_256x384")
-                           : (epi1 == EPI_DGELU ? "gemm_pair_nt_dgelu_256x384+tn_f32_192x384" : "gemm_pair_nt_store_256x384+tn_f32_192x384");
+  info.name = names[t2.bm == 256 ? 0 : 1][epi1 == EPI_DGELU ? 0 : 1].c_str();
   info.flops = 2.0 * g1.M * (double)g1.N * g1.K + 2.0 * g2.M * (double)g2.N * g2.K;
   info.bytes = 2.0 * ((double)g1.M * g1.K + (double)g1.K * g1.N) + 2.0 * g1.M * (double)g1.N * (epi1 == EPI_DGELU ? 2 : 1) +
                2.0 * ((double)g2.M * g2.K + (double)g2.K * g2.N) + 4.0 * g2.M * (double)g2.N * (g2.accumulate ? 2 : 1) +
