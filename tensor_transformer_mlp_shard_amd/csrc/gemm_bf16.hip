@@ -785,10 +785,51 @@ TileChoice choose_tile(int M, int N, bool shared_tiles = true) {
   return pick;
 }
 
+// Column split of a launch that would run as several waves of 256 x 192 tiles:
+// the first n1 columns on 256 x 384 tiles filling whole waves, the rest on
+// 256 x 192 tiles, when that estimate (the tile efficiencies of choose_tile) is
+// lower (the 8192 x 4608 QKV forward: one wave of each instead of three of the
+// small tile).  0: no split.
+int split_cols(int M, int N) {
+  const int64_t tm = (M + 255) / 256;
+  const int64_t waves = (tm * ((N + 191) / 192) + 255) / 256;
+  if (waves < 2) return 0;
+  int best = 0;
+  double best_t = (double)waves * 256 * 192;
+  for (int n1 = 384; n1 < N; n1 += 384) {
+    const int64_t t1 = tm * (n1 / 384), t2 = tm * ((N - n1 + 191) / 192);
+    if (t1 % 256 != 0) continue;
+    const double t = (double)(t1 / 256) * 256 * 384 / 1.12 + (double)((t2 + 255) / 256) * 256 * 192;
+    if (t < best_t * 0.97) { best_t = t; best = n1; }
+  }
+  return best;
+}
+
 template <bool AK, bool BKC, int EPI, typename E>
 hipError_t launch_shape(const GemmArgs& g, hipStream_t s, const char** name) {
   // GeLU' with H out stages two strips per wave: only the split tiles hold them
   const TileChoice t = EPI == EPI_DGELU_H ? choose_tile(g.M, g.N, false) : choose_tile(g.M, g.N);
+  if constexpr (EPI == EPI_STORE || EPI == EPI_BIAS_GELU || EPI == EPI_DGELU) {
+    const int n1 = (t.bm == 256 && t.bn == 192) ? split_cols(g.M, g.N) : 0;
+    if (n1 > 0) {
+      // columns [0, n1) and [n1, N): every operand and output of the second part
+      // starts n1 columns on (B stored [N x K] when BKC: n1 rows on)
+      GemmArgs g1 = g, g2 = g;
+      g1.N = n1;
+      g2.N = g.N - n1;
+      g2.B = (const E*)g.B + (BKC ? (int64_t)n1 * g.ldb : (int64_t)n1);
+      g2.C = (E*)g.C + n1;
+      if (g.C2) g2.C2 = (E*)g.C2 + n1;
+      if (g.bias) g2.bias = (const E*)g.bias + n1;
+      if (g.aux) g2.aux = (const E*)g.aux + n1;
+      static const std::string nm = std::string(kname<T256x384, AK, BKC, EPI, E>()) + "+256x192";
+      const char* unused;
+      hipError_t e = launch_tile<T256x384, AK, BKC, EPI, E>(g1, s, &unused);
+      if (e == hipSuccess) e = launch_tile<T256x192, AK, BKC, EPI, E>(g2, s, &unused);
+      *name = nm.c_str();
+      return e;
+    }
+  }
   if constexpr (EPI != EPI_DGELU_H) {
     if (t.bm == 256 && t.bn == 384) return launch_tile<T256x384, AK, BKC, EPI, E>(g, s, name);
     if (t.bm == 384 && t.bn == 256) return launch_tile<T384x256, AK, BKC, EPI, E>(g, s, name);
