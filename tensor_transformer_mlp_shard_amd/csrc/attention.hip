@@ -150,9 +150,10 @@ struct KvReadOffsets {
 // lane i of copy c landing at byte 1024 (wave NI + c) + 16 i, which is chunk
 // slot s of row r; it fetches the chunk that the swizzle puts there.  Rows at
 // or past `rows_left` read as zero through the buffer range check.
-template <int D, bool QD = false>
+template <int D, bool QD = false, int ROWS = BKEYS>
 struct BlockCopier {
-  static constexpr int NI = Shape<D>::BLOCK_BYTES / 1024 / AW;
+  static constexpr int NI = ROWS * Shape<D>::ROW_BYTES / 1024 / AW;
+  static_assert(NI * 1024 * AW == ROWS * Shape<D>::ROW_BYTES, "whole 1 KiB copies per wave per block");
   int off[NI];
   __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
 #pragma unroll
@@ -399,9 +400,10 @@ __global__ void __launch_bounds__(NT, 2) attn_fwd_kernel(FwdArgs a) {
 //    each lane holds one key's column, and P and dS feed dV^T += dO^T P and
 //    dK^T += Q^T dS from registers (queries in the accumulator order, dO^T and
 //    Q^T read from LDS with transposing reads in that order);
-//  * attn_bwd_dq: a workgroup owns 128 queries (32 per wave, one per lane
-//    column) as in the forward; keys and values are copied HBM -> LDS directly
-//    in double-buffered blocks of 64; S^T and dP^T = V dO^T give dS^T, which feeds dQ^T += K^T dS^T.
+//  * attn_bwd_dq, its mirror: a workgroup owns 64 queries (16 per wave, one per
+//    lane column, two workgroups per CU) whose Q and dO stay in registers; keys
+//    and values are copied HBM -> LDS directly in double-buffered blocks of 64;
+//    S^T and dP^T = V dO^T give dS^T, which feeds dQ^T += K^T dS^T.
 
 struct BwdArgs {
   const bf16* qkv;
@@ -411,7 +413,7 @@ struct BwdArgs {
   float* dt;        // [Hl x T]
   bf16* dqkv;
   int64_t T;
-  int S, Hl, B, nb, causal;  // nb: 128-row blocks per sequence
+  int S, Hl, B, causal;
   float scale_log2;           // log2(e) / sqrt(D)
   float scale;                // 1 / sqrt(D)
 };
@@ -638,16 +640,40 @@ __global__ void __launch_bounds__(NT, 2) attn_bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
-template <int D>
+// dQ with 16 queries per wave on 16 x 16 x 32 MFMAs, the mirror of the dK/dV
+// kernel: a workgroup owns 64 queries (4 waves x 16, one query per lane column),
+// whose Q and dO stay in registers; keys and values stream through LDS in
+// double-buffered blocks of 64 (qd_slot layout: K is read both as rows and with
+// transposing reads).  Per block:
+//  * S^T[key][q] and dP^T[key][q] for 4 tiles of 16 keys (A: K / V rows from
+//    LDS, B: this wave's Q / dO, k = d); a lane holds keys 16 t + 4 g + 0..3 of
+//    its query, so the softmax statistics (lse, Dt) are per-lane constants;
+//  * dS^T in registers as the B operand of dQ^T += K^T dS^T over 32-key k
+//    blocks, in the accumulator order (k slot 8 g + e is key 4 g + (e mod 4) +
+//    16 (e / 4) of the k block), K^T read with transposing reads in that order.
+// Dt = rowsum(dO * O) for the workgroup's queries is formed here from the dO
+// the lanes hold (32 of a row's d per lane, the 4 lanes of a query added in a
+// fixed order) and written for the dK/dV kernel.  Workgroups of 64 queries let
+// the longest causal rows (all keys) take less than a workgroup slot's mean load.
+template <int D, int KB>
 __global__ void __launch_bounds__(NT, 2) attn_bwd_dq_kernel(BwdArgs a) {
   using SH = Shape<D>;
-  constexpr int BUF = 2 * SH::BLOCK_BYTES;  // one buffer: a K block, then a V block
+  constexpr int QW16 = 16;                   // queries per wave
+  constexpr int BQ16 = AW * QW16;            // queries per workgroup
+  constexpr int KBYTES = KB * SH::ROW_BYTES; // one K (or V) block of KB keys
+  constexpr int BUF = 2 * KBYTES;            // one buffer: a K block, then a V block
+  constexpr int NTL = KB / 16;               // 16-key tiles per block
+  constexpr int NKQ = KB / 32;               // 32-key k blocks per block
+  constexpr int NS = D / 32;                 // 32-wide d slices: k of S^T and dP^T
+  constexpr int NDB = D / 16;                // 16-row d blocks of dQ^T
+  constexpr int RB = SH::ROW_BYTES;
   __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hh = lane >> 5;
+  const int l16 = lane & 15, g = lane >> 4;
   const int bh = a.B * a.Hl;
-  const int qb = a.nb - 1 - (int)(blockIdx.x / bh);  // longest causal query blocks first
+  const int nqb = (a.S + BQ16 - 1) / BQ16;
+  const int qb = nqb - 1 - (int)(blockIdx.x / bh);  // longest causal query blocks first
   const int b = (int)(blockIdx.x % bh) / a.Hl, h = (int)(blockIdx.x % bh) % a.Hl;
   const int64_t ld = 3LL * a.Hl * D;
   const int64_t row0 = (int64_t)b * a.S;
@@ -656,135 +682,142 @@ __global__ void __launch_bounds__(NT, 2) attn_bwd_dq_kernel(BwdArgs a) {
   const bf16* vbase = qbase + 2LL * a.Hl * D;
   const int64_t ldo = (int64_t)a.Hl * D;
   const bf16* dobase = a.dout + row0 * ldo + (int64_t)h * D;
-  const int q0 = qb * BQ;
-  const int wq0 = q0 + wave * QW;
-  const int qi = wq0 + l32;
+  const int q0 = qb * BQ16;
+  const int wq0 = q0 + wave * QW16;                  // first query of this wave
+  const int qi = wq0 + l16;                          // this lane's query
   const bool qvalid = qi < a.S;
-  const int kend = a.causal ? min(a.S, q0 + BQ) : a.S;
-  const int nkb = (kend + BKEYS - 1) / BKEYS;
+  const int kend = a.causal ? min(a.S, q0 + BQ16) : a.S;
+  const int nkb = (kend + KB - 1) / KB;
   const int lim = a.causal ? min(a.S, qi + 1) : a.S;  // keys at or past lim are masked
 
-  BlockCopier<D> cp;
+  BlockCopier<D, true, KB> cp;
   cp.init(ld, wave, lane);
   const unsigned lds0 = lds_address(smem);
   auto issue = [&](int j, int buf) {
-    const int k0 = j * BKEYS;
+    const int k0 = j * KB;
     cp.issue(kbase + (int64_t)k0 * ld, ld, a.S - k0, lds0 + buf * BUF, wave);
-    cp.issue(vbase + (int64_t)k0 * ld, ld, a.S - k0, lds0 + buf * BUF + SH::BLOCK_BYTES, wave);
+    cp.issue(vbase + (int64_t)k0 * ld, ld, a.S - k0, lds0 + buf * BUF + KBYTES, wave);
   };
   issue(0, 0);
 
-  // Q and dO of this lane's query as the B operand (k = d) of S^T and dP^T.
-  bf16x8 qf[SH::KS], gf[SH::KS];
+  // Q and dO of this lane's query as the B operand of S^T and dP^T: d = 32 s + 8 g + 0..7.
+  bf16x8 qf[NS], gf[NS];
 #pragma unroll
-  for (int s = 0; s < SH::KS; ++s) {
-    qf[s] = qvalid ? *(const bf16x8*)(qbase + (int64_t)qi * ld + 16 * s + 8 * hh) : bf16x8{};
-    gf[s] = qvalid ? *(const bf16x8*)(dobase + (int64_t)qi * ldo + 16 * s + 8 * hh) : bf16x8{};
+  for (int s = 0; s < NS; ++s) {
+    qf[s] = qvalid ? *(const bf16x8*)(qbase + (int64_t)qi * ld + 32 * s + 8 * g) : bf16x8{};
+    gf[s] = qvalid ? *(const bf16x8*)(dobase + (int64_t)qi * ldo + 32 * s + 8 * g) : bf16x8{};
   }
   const float lse2 = qvalid ? a.lse[(int64_t)h * a.T + row0 + qi] * LOG2E : INFINITY;
-  // Dt = rowsum(dO * O) for this lane's query: this lane holds half of the dO
-  // row (d = 16 s + 8 hh + 0..7), lane ^ 32 the other half; the two partial
-  // sums are added (the same value in both lanes: fp32 addition commutes) and
-  // written for the dK/dV kernel.
+  // Dt = rowsum(dO * O): this lane's 32 products, then the 4 lanes of the query
+  // (l16 + 16 g) added pairwise; fp32 addition commutes, so all four hold the same value.
   float dti = 0.0f;
   {
-    const bf16* orow = a.o + (row0 + qi) * ldo + (int64_t)h * D + 8 * hh;
+    const bf16* orow = a.o + (row0 + qi) * ldo + (int64_t)h * D + 8 * g;
 #pragma unroll
-    for (int s = 0; s < SH::KS; ++s) {
-      const bf16x8 ov = qvalid ? *(const bf16x8*)(orow + 16 * s) : bf16x8{};
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 ov = qvalid ? *(const bf16x8*)(orow + 32 * s) : bf16x8{};
 #pragma unroll
       for (int e = 0; e < 8; ++e) dti += (float)gf[s][e] * (float)ov[e];
     }
-    dti += other_half(dti, (lane ^ 32) * 4);
-    if (qvalid && hh == 0) a.dt[(int64_t)h * a.T + row0 + qi] = dti;
+    dti += __shfl_xor(dti, 16);
+    dti += __shfl_xor(dti, 32);
+    if (qvalid && g == 0) a.dt[(int64_t)h * a.T + row0 + qi] = dti;
   }
-  const int g16 = lane >> 4, i16 = lane & 15;
-  KvReadOffsets<D> ro;  // row reads of K / V (.k), transposing reads of K^T (.va, .vb)
-  ro.init(l32, hh, 4 * (g16 >> 1) + (i16 >> 2), 16 * (g16 & 1) + 4 * (i16 & 3));
-
-  f32x16 dq[SH::DT];
+  // Row reads: key 16 t + l16, chunk 4 s + g.  Transposing reads of d block db:
+  // key row 4 g + l16 / 4 (+ 16, + 32 kq: immediates), column 16 db + 4 (l16 mod 4).
+  int rowo[NS], tro[NDB];
 #pragma unroll
-  for (int t = 0; t < SH::DT; ++t) dq[t] = f32x16{};
+  for (int s = 0; s < NS; ++s) rowo[s] = l16 * RB + qd_slot<D>(4 * s + g, l16) * 16;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int r = 4 * g + (l16 >> 2);
+    tro[db] = r * RB + qd_slot<D>(2 * db + ((l16 >> 1) & 1), r) * 16 + (l16 & 1) * 8;
+  }
+
+  f32x4 dq[NDB];
+#pragma unroll
+  for (int t = 0; t < NDB; ++t) dq[t] = f32x4{};
 
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
 
   auto block = [&](int j, auto bic) {
     constexpr int BI = decltype(bic)::value;
-    const int k0 = j * BKEYS;
+    const int k0 = j * KB;
     if (j + 1 < nkb) issue(j + 1, BI ^ 1);
     const char* Ks = smem + BI * BUF;
-    const char* Vs = Ks + SH::BLOCK_BYTES;
+    const char* Vs = Ks + KBYTES;
 
-    // S^T[key][query] and dP^T[key][query] = (V dO^T) for keys 32 t + (0..31);
-    // the K and V operands are read RD slices ahead of their MFMAs.
-    constexpr int RD = 2;
-    f32x16 sc[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-    bf16x8 kr[RD + 1][2], vr[RD + 1][2];
-    auto rows = [&](int s) {
+    // S^T and dP^T of keys 16 t + (0..15) of the block, t = n / NS, d slice
+    // s = n % NS; the K and V operands are read RD steps ahead.
+    constexpr int RD = 3, NSTEP = NTL * NS;
+    f32x4 sc[NTL], dp[NTL];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int o = ro.k[s] + t * 32 * SH::ROW_BYTES;
-        kr[s % (RD + 1)][t] = *(const bf16x8*)(Ks + o);
-        vr[s % (RD + 1)][t] = *(const bf16x8*)(Vs + o);
-      }
+    for (int t = 0; t < NTL; ++t) { sc[t] = f32x4{}; dp[t] = f32x4{}; }
+    bf16x8 kr[RD + 1], vr[RD + 1];
+    auto rows = [&](int n) {
+      const int o = rowo[n % NS] + (n / NS) * 16 * RB;
+      kr[n % (RD + 1)] = *(const bf16x8*)(Ks + o);
+      vr[n % (RD + 1)] = *(const bf16x8*)(Vs + o);
     };
 #pragma unroll
-    for (int s = 0; s < RD; ++s) rows(s);
+    for (int n = 0; n < RD; ++n) rows(n);
 #pragma unroll
-    for (int s = 0; s < SH::KS; ++s) {
-      if (s + RD < SH::KS) rows(s + RD);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        sc[t] = mfma(kr[s % (RD + 1)][t], qf[s], sc[t]);
-        dp[t] = mfma(vr[s % (RD + 1)][t], gf[s], dp[t]);
-      }
+    for (int n = 0; n < NSTEP; ++n) {
+      if (n + RD < NSTEP) rows(n + RD);
+      sc[n / NS] = mfma16(kr[n % (RD + 1)], qf[n % NS], sc[n / NS]);
+      dp[n / NS] = mfma16(vr[n % (RD + 1)], gf[n % NS], dp[n / NS]);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 * RD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * RD, 0);
 #pragma unroll
-    for (int s = 0; s < SH::KS; ++s) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      if (s + RD < SH::KS) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    for (int n = 0; n < NSTEP; ++n) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (n + RD < NSTEP) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    // Mask (only blocks that reach past the sequence end or this wave's first
-    // query): accumulator element (t, v) is key k0 + 4 hh + c(t, v).
-    if ((k0 + BKEYS > a.S) || (a.causal && k0 + BKEYS - 1 > wq0)) {
-      const int x = lim - k0 - 4 * hh;
+    // Mask (blocks reaching past the sequence end or this wave's first query):
+    // element (t, r) is key k0 + 16 t + 4 g + r.
+    if (k0 + KB > a.S || (a.causal && k0 + KB - 1 > wq0)) {
+      const int x = lim - k0 - 4 * g;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < NTL; ++t)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int c = 32 * t + 8 * (v >> 2) + (v & 3);
-          sc[t][v] = c >= x ? -INFINITY : sc[t][v];
-        }
+        for (int r = 0; r < 4; ++r) sc[t][r] = 16 * t + r < x ? sc[t][r] : -INFINITY;
     }
-    // dS^T = P^T * (dP^T - Dt) as the B operand of 16-key slice q (accumulator order).
-    bf16x8 sf[4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][v], a.scale_log2, -lse2));
-        sf[2 * t + (v >> 3)][v & 7] = (bf16)(p * (dp[t][v] - dti));
-      }
-    // dQ^T += K^T dS^T (k = the block's keys in accumulator order), K^T read
-    // with transposing reads VPD operands ahead.
-    constexpr int NOP = 4 * SH::DT, VPD = 4;
-    bf16x8 kv[VPD];
-    auto ktr = [&](int n) {
-      const int q = n / SH::DT, t = n % SH::DT;
-      const bf16x4 lo = read_tr(Ks + ro.va[t] + 16 * q * SH::ROW_BYTES);
-      const bf16x4 hi = read_tr(Ks + ro.vb[t] + 16 * q * SH::ROW_BYTES);
-      bf16x8& v = kv[n % VPD];
+    // K^T operand of 32-key k block kq, d block db.
+    auto tr = [&](int kq, int db) {
+      const char* p = Ks + tro[db] + 32 * kq * RB;
+      const bf16x4 lo = read_tr(p), hi = read_tr(p + 16 * RB);
+      bf16x8 v;
       v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
       v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+      return v;
     };
+    constexpr int NOP = NKQ * NDB, VPD = 4;
+    bf16x8 kv[VPD];
 #pragma unroll
-    for (int n = 0; n < VPD; ++n) ktr(n);
+    for (int n = 0; n < VPD; ++n) kv[n] = tr(n / NDB, n % NDB);
+    // dS^T of k block kq (score tiles t = 2 kq, 2 kq + 1).
+    bf16x8 sf[NKQ];
+    auto pds = [&](int kq) {
 #pragma unroll
-    for (int n = 0; n < NOP; ++n) {
-      dq[n % SH::DT] = mfma(kv[n % VPD], sf[n / SH::DT], dq[n % SH::DT]);
-      if (n + VPD < NOP) ktr(n + VPD);
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 2 * kq + u;
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][r], a.scale_log2, -lse2));
+          sf[kq][4 * u + r] = (bf16)(p * (dp[t][r] - dti));
+        }
+    };
+    pds(0);
+#pragma unroll
+    for (int kq = 0; kq < NKQ; ++kq) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int n = kq * NDB + db;
+        dq[db] = mfma16(kv[n % VPD], sf[kq], dq[db]);
+        if (n + VPD < NOP) kv[n % VPD] = tr((n + VPD) / NDB, (n + VPD) % NDB);
+      }
+      if (kq + 1 < NKQ) pds(kq + 1);
     }
     // This wave's copies have landed and every wave is done with this buffer.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -798,14 +831,12 @@ __global__ void __launch_bounds__(NT, 2) attn_bwd_dq_kernel(BwdArgs a) {
   if (qvalid) {
     bf16* qrow = a.dqkv + (row0 + qi) * ld + (int64_t)h * D;
 #pragma unroll
-    for (int t = 0; t < SH::DT; ++t)
+    for (int db = 0; db < NDB; ++db) {
+      bf16x4 q4;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 q4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) q4[e] = (bf16)(dq[t][4 * g + e] * a.scale);
-        *(bf16x4*)(qrow + 32 * t + 8 * g + 4 * hh) = q4;
-      }
+      for (int r = 0; r < 4; ++r) q4[r] = (bf16)(dq[db][r] * a.scale);
+      *(bf16x4*)(qrow + 16 * db + 4 * g) = q4;
+    }
   }
 }
 
@@ -854,21 +885,20 @@ hipError_t attention_bwd(const bf16* qkv, const bf16* o, const float* lse, const
   a.S = p.S;
   a.Hl = p.Hl;
   a.B = (int)(p.T / p.S);
-  a.nb = (p.S + 127) / 128;
   a.causal = p.causal ? 1 : 0;
   a.scale = (float)(1.0 / std::sqrt((double)p.D));
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p.D));
   const double el = 2.0 * p.T * p.Hl * p.D;   // bytes of one [T x Hl*D] bf16 tensor
   const bool d128 = p.D == 128;
   const double f = attention_fwd_flops(p);   // 2 products per allowed pair
-  const dim3 grid((unsigned)((int64_t)a.nb * a.B * a.Hl));
   // dQ: S^T, dP^T, dQ (3 products), and Dt for dK/dV (reads O as well);
   // dK, dV: S, dP, dV, dK (4 products)
   LaunchInfo i2{d128 ? "attn_bwd_dq_d128" : "attn_bwd_dq_d64", 1.5 * f,
                 4.0 * el + 4.0 * p.T * p.Hl + el};
   trace_begin(s);
-  if (d128) hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, grid, dim3(NT), 0, s, a);
-  else hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, grid, dim3(NT), 0, s, a);
+  const dim3 grid64q((unsigned)((int64_t)((p.S + 63) / 64) * a.B * a.Hl));  // 64 queries per workgroup
+  if (d128) hipLaunchKernelGGL((attn_bwd_dq_kernel<128, 64>), grid64q, dim3(NT), 0, s, a);
+  else hipLaunchKernelGGL((attn_bwd_dq_kernel<64, 64>), grid64q, dim3(NT), 0, s, a);
   trace_end(s, i2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
