@@ -55,6 +55,7 @@
 
 #include <algorithm>
 #include <string>
+#include <type_traits>
 
 namespace tps {
 namespace {
@@ -199,18 +200,21 @@ struct Copier {
   }
 
   // Copy u (0 <= u < NVM) of K step kt into LDS stage kt % NSTAGE.  Past the last
-  // step the copies read only zeros into a stage that is not used again.
+  // step the copies read only zeros into a stage that is not used again.  TAIL:
+  // the step may reach past K (K-contiguous chunks at or past K read as zeros);
+  // without it the caller guarantees (kt + 1) * KT <= K.
+  template <bool TAIL = true>
   __device__ __forceinline__ void issue(int kt, int u) const {
     const int k0 = kt * KT;
     const unsigned st = smem_addr + (unsigned)((kt % C::NSTAGE) * C::STAGE);
     if (u < C::A_INS) {
       const int j = u;
       const i32x4 r = make_rsrc(a_base + kt * a_step, a_total - kt * a_step);
-      lds_dma16(r, (AK && k0 + a_kc[j] >= K) ? OOB : a_off[j], st + (cw * C::A_INS + j) * 1024);
+      lds_dma16(r, (TAIL && AK && k0 + a_kc[j] >= K) ? OOB : a_off[j], st + (cw * C::A_INS + j) * 1024);
     } else {
       const int j = u - C::A_INS;
       const i32x4 r = make_rsrc(b_base + kt * b_step, b_total - kt * b_step);
-      lds_dma16(r, (BKC && k0 + b_kc[j] >= K) ? OOB : b_off[j], st + C::A_BYTES + (cw * C::B_INS + j) * 1024);
+      lds_dma16(r, (TAIL && BKC && k0 + b_kc[j] >= K) ? OOB : b_off[j], st + C::A_BYTES + (cw * C::B_INS + j) * 1024);
     }
   }
 };
@@ -532,12 +536,18 @@ __device__ __forceinline__ void gemm_tile(GemmArgs g, int bid0, char* smem) {
         for (int u = 0; u < NVM; ++u) cp.issue(kbeg + p, u);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step kbeg landed
       __syncthreads();
-      for (int kt = kbeg; kt < nk; ++kt) {
+      // steps before ksafe prefetch a step that lies wholly inside K: no tail check
+      const int ksafe = (AK && BKC) ? max(kbeg, min(nk, g.K / KT - PREF)) : kbeg;
+      auto pstep = [&](int kt, auto tail) {
 #pragma unroll
-        for (int u = 0; u < NVM; ++u) cp.issue(kt + PREF, u);
+        for (int u = 0; u < NVM; ++u) cp.template issue<decltype(tail)::value>(kt + PREF, u);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step kt+1 landed
         __syncthreads();
-      }
+      };
+      int kt = kbeg;
+      if constexpr (AK && BKC)
+        for (; kt < ksafe; ++kt) pstep(kt, std::false_type{});
+      for (; kt < nk; ++kt) pstep(kt, std::true_type{});
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no copy into this workgroup's LDS outlives it
       return;
     }
@@ -618,7 +628,8 @@ __device__ __forceinline__ void gemm_tile(GemmArgs g, int bid0, char* smem) {
     constexpr int PRE_MF = FM * FN * (NS - 1) + FM_HALF * FN;   // MFMAs before the barrier
     static_assert(PRE_MF >= NVM, "not enough MFMAs to spread the copies over");
     V8 fa[FM], fb[FN];
-    for (int kt = kbeg; kt < nk; ++kt) {
+    auto kstep = [&](int kt, auto tail) {
+      constexpr bool TAIL = decltype(tail)::value;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         rd.load(smem, kt, s, fa, fb);
@@ -633,8 +644,8 @@ __device__ __forceinline__ void gemm_tile(GemmArgs g, int bid0, char* smem) {
 #pragma unroll
             for (int u = 0; u < NVM; ++u)
               if ((u * PRE_MF) / NVM == t) {
-                if constexpr (ALL_COPY) cp.issue(kt + PREF, u);
-                else if (copier) cp.issue(kt + PREF, u);
+                if constexpr (ALL_COPY) cp.template issue<TAIL>(kt + PREF, u);
+                else if (copier) cp.template issue<TAIL>(kt + PREF, u);
               }
           }
       }
@@ -646,7 +657,15 @@ __device__ __forceinline__ void gemm_tile(GemmArgs g, int bid0, char* smem) {
       for (int i = FM_HALF; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) mfma(fa, fb, i, j);
-    }
+    };
+    // Steps before ksafe prefetch a step that lies wholly inside K: no tail check
+    // (both operands K-contiguous, where every copy would carry it; on the other
+    // layouts the second copy of the loop costs registers).
+    const int ksafe = (AK && BKC) ? max(kbeg, min(nk, g.K / KT - PREF)) : kbeg;
+    int kt = kbeg;
+    if constexpr (AK && BKC)
+      for (; kt < ksafe; ++kt) kstep(kt, std::false_type{});
+    for (; kt < nk; ++kt) kstep(kt, std::true_type{});
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no copy into this workgroup's LDS outlives it
   }
 
