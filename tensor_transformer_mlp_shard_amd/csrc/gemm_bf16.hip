@@ -154,6 +154,11 @@ struct Copier {
   const char* a_base;
   const char* b_base;
   int64_t a_total, b_total, a_step, b_step;
+  // Record counts in 32-bit arithmetic: bytes from step kt's base to the end of
+  // the operand are total - kt * step; the first *_hi steps have more than OOB
+  // (clamped to OOB: every in-range offset is then inside the operand), after
+  // that the count fits in an int and is taken from the low 32 bits.
+  int a_hi, b_hi, a_tot32, b_tot32, a_step32, b_step32;
   int a_off[C::A_INS], a_kc[C::A_INS], b_off[C::B_INS], b_kc[C::B_INS];
   unsigned smem_addr;
   int cw, K;
@@ -168,6 +173,12 @@ struct Copier {
     b_total = 2 * ((BKC ? (int64_t)g.N : (int64_t)g.K) * g.ldb - (BKC ? (int64_t)n0 * g.ldb : n0));
     a_step = AK ? 2 * KT : 2 * (int64_t)KT * g.lda;
     b_step = BKC ? 2 * KT : 2 * (int64_t)KT * g.ldb;
+    a_hi = a_total > OOB ? (int)((a_total - OOB - 1) / a_step + 1) : 0;
+    b_hi = b_total > OOB ? (int)((b_total - OOB - 1) / b_step + 1) : 0;
+    a_tot32 = (int)(uint32_t)a_total;
+    b_tot32 = (int)(uint32_t)b_total;
+    a_step32 = (int)a_step;
+    b_step32 = (int)b_step;
 #pragma unroll
     for (int j = 0; j < C::A_INS; ++j) {
       const int q = (cw * C::A_INS + j) * 64 + lane;  // 16-byte chunk index in the stage's A panel
@@ -209,11 +220,13 @@ struct Copier {
     const unsigned st = smem_addr + (unsigned)((kt % C::NSTAGE) * C::STAGE);
     if (u < C::A_INS) {
       const int j = u;
-      const i32x4 r = make_rsrc(a_base + kt * a_step, a_total - kt * a_step);
+      const int n = kt < a_hi ? OOB : max(0, (int)((uint32_t)a_tot32 - (uint32_t)kt * (uint32_t)a_step32));
+      const i32x4 r = make_rsrc_n(a_base + kt * a_step, n);
       lds_dma16(r, (TAIL && AK && k0 + a_kc[j] >= K) ? OOB : a_off[j], st + (cw * C::A_INS + j) * 1024);
     } else {
       const int j = u - C::A_INS;
-      const i32x4 r = make_rsrc(b_base + kt * b_step, b_total - kt * b_step);
+      const int n = kt < b_hi ? OOB : max(0, (int)((uint32_t)b_tot32 - (uint32_t)kt * (uint32_t)b_step32));
+      const i32x4 r = make_rsrc_n(b_base + kt * b_step, n);
       lds_dma16(r, (TAIL && BKC && k0 + b_kc[j] >= K) ? OOB : b_off[j], st + C::A_BYTES + (cw * C::B_INS + j) * 1024);
     }
   }

@@ -47,4 +47,16 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
   return r;
 }
 
+// The same resource with a record count the caller has already clamped to
+// [0, OOB] (wave-uniform), so that no 64-bit compare is made per copy.
+__device__ __forceinline__ i32x4 make_rsrc_n(const void* base, int n) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(a & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff));
+  r[2] = __builtin_amdgcn_readfirstlane(n);
+  r[3] = 0x00020000;
+  return r;
+}
+
 }  // namespace tps
