@@ -145,6 +145,14 @@ struct Cfg {
   static_assert((PREF - 1) * NVM <= 63, "vmcnt range");
 };
 
+// LDS stage of K step kt (kt >= 0): unsigned modulo where the ring is a power of
+// two (one scalar AND), signed otherwise (the compiler's multiply-shift for the
+// unsigned form of a 5-stage ring lands in vector registers).
+template <class C>
+__device__ __forceinline__ int stage_of(int kt) {
+  return (C::NSTAGE & (C::NSTAGE - 1)) == 0 ? (int)((unsigned)kt % C::NSTAGE) : kt % C::NSTAGE;
+}
+
 // One copying wave's share of every K step's copies.  Every in-range offset of
 // one K step stays below the record-count cap of make_rsrc: the largest is row
 // 383 of a 384-row panel whose rows are 2^21 elements (the feature-dimension
@@ -162,6 +170,11 @@ struct Copier {
   int a_off[C::A_INS], a_kc[C::A_INS], b_off[C::B_INS], b_kc[C::B_INS];
   unsigned smem_addr;
   int cw, K;
+  // The step whose copies issue() makes (kcur), its two buffer resources and
+  // unclamped 32-bit remaining byte counts, advanced one step at a time.
+  int kcur, a_rem, b_rem;
+  unsigned st_cur;   // LDS address of stage kcur % NSTAGE
+  i32x4 ra, rb;
 
   __device__ __forceinline__ void init(const GemmArgs& g, int m0, int n0, int cw_, int lane, const char* smem) {
     constexpr int KCH = KT / 8;  // 16-byte chunks per row of a K-contiguous panel
@@ -210,24 +223,46 @@ struct Copier {
     smem_addr = lds_address(smem);
   }
 
-  // Copy u (0 <= u < NVM) of K step kt into LDS stage kt % NSTAGE.  Past the last
-  // step the copies read only zeros into a stage that is not used again.  TAIL:
-  // the step may reach past K (K-contiguous chunks at or past K read as zeros);
-  // without it the caller guarantees (kt + 1) * KT <= K.
+  // Make step kt the one issue() copies.
+  __device__ __forceinline__ void start(int kt) {
+    kcur = kt;
+    st_cur = smem_addr + stage_of<C>(kt) * C::STAGE;
+    a_rem = (int)((uint32_t)a_tot32 - (uint32_t)kt * (uint32_t)a_step32);
+    b_rem = (int)((uint32_t)b_tot32 - (uint32_t)kt * (uint32_t)b_step32);
+    ra = make_rsrc_n(a_base + kt * a_step, kt < a_hi ? OOB : max(0, a_rem));
+    rb = make_rsrc_n(b_base + kt * b_step, kt < b_hi ? OOB : max(0, b_rem));
+  }
+  // On to step kcur + 1: the bases move by one step (a 64-bit add in the first
+  // two resource words; a buffer's base stays below 2^48), the counts shrink.
+  __device__ __forceinline__ void advance() {
+    ++kcur;
+    st_cur = st_cur + C::STAGE == smem_addr + C::NSTAGE * C::STAGE ? smem_addr : st_cur + C::STAGE;
+    const uint64_t a = ((uint64_t)(uint32_t)ra[1] << 32 | (uint32_t)ra[0]) + (uint64_t)a_step;
+    const uint64_t b = ((uint64_t)(uint32_t)rb[1] << 32 | (uint32_t)rb[0]) + (uint64_t)b_step;
+    a_rem -= a_step32;
+    b_rem -= b_step32;
+    ra[0] = (int)(uint32_t)a;
+    ra[1] = (int)(uint32_t)(a >> 32);
+    ra[2] = kcur < a_hi ? OOB : max(0, a_rem);
+    rb[0] = (int)(uint32_t)b;
+    rb[1] = (int)(uint32_t)(b >> 32);
+    rb[2] = kcur < b_hi ? OOB : max(0, b_rem);
+  }
+
+  // Copy u (0 <= u < NVM) of K step kcur into LDS stage kcur % NSTAGE.  Past the
+  // last step the copies read only zeros into a stage that is not used again.
+  // TAIL: the step may reach past K (K-contiguous chunks at or past K read as
+  // zeros); without it the caller guarantees (kcur + 1) * KT <= K.
   template <bool TAIL = true>
-  __device__ __forceinline__ void issue(int kt, int u) const {
-    const int k0 = kt * KT;
-    const unsigned st = smem_addr + (unsigned)((kt % C::NSTAGE) * C::STAGE);
+  __device__ __forceinline__ void issue(int u) const {
+    const int k0 = kcur * KT;
+    const unsigned st = st_cur;
     if (u < C::A_INS) {
       const int j = u;
-      const int n = kt < a_hi ? OOB : max(0, (int)((uint32_t)a_tot32 - (uint32_t)kt * (uint32_t)a_step32));
-      const i32x4 r = make_rsrc_n(a_base + kt * a_step, n);
-      lds_dma16(r, (TAIL && AK && k0 + a_kc[j] >= K) ? OOB : a_off[j], st + (cw * C::A_INS + j) * 1024);
+      lds_dma16(ra, (TAIL && AK && k0 + a_kc[j] >= K) ? OOB : a_off[j], st + (cw * C::A_INS + j) * 1024);
     } else {
       const int j = u - C::A_INS;
-      const int n = kt < b_hi ? OOB : max(0, (int)((uint32_t)b_tot32 - (uint32_t)kt * (uint32_t)b_step32));
-      const i32x4 r = make_rsrc_n(b_base + kt * b_step, n);
-      lds_dma16(r, (TAIL && BKC && k0 + b_kc[j] >= K) ? OOB : b_off[j], st + C::A_BYTES + (cw * C::B_INS + j) * 1024);
+      lds_dma16(rb, (TAIL && BKC && k0 + b_kc[j] >= K) ? OOB : b_off[j], st + C::A_BYTES + (cw * C::B_INS + j) * 1024);
     }
   }
 };
@@ -272,7 +307,7 @@ struct Reader {
   }
   // Operands of 16-wide k slice s of K step kt.
   __device__ __forceinline__ void load(const char* smem, int kt, int s, V8* fa, V8* fb) const {
-    const char* sa = smem + (kt % C::NSTAGE) * C::STAGE;
+    const char* sa = smem + stage_of<C>(kt) * C::STAGE;
     const char* sb = sa + C::A_BYTES;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
@@ -321,7 +356,7 @@ struct BColSum {
     const int L = wave * 64 + lane, q = L >> 2, j = L & 3;
     // rows j + 4 u all have row j's chunk swizzle (it depends on the row mod 4)
     const int off = j * (C::BN * 2) + (((q >> 1) ^ mn_swz<C::BN>(j)) * 16) + (q & 1) * 8;
-    const char* sb = smem + (kt % C::NSTAGE) * C::STAGE + C::A_BYTES + off;
+    const char* sb = smem + stage_of<C>(kt) * C::STAGE + C::A_BYTES + off;
     V4 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) v[u] = *(const V4*)(sb + u * 4 * C::BN * 2);
@@ -543,17 +578,21 @@ __device__ __forceinline__ void gemm_tile(GemmArgs g, int bid0, char* smem) {
       // -------------------------------------------------------- producer wave
       Copier<C, AK, BKC> cp;
       cp.init(g, m0, n0, wave - C::NCONS, lane, smem);
+      cp.start(kbeg);
 #pragma unroll
-      for (int p = 0; p < PREF; ++p)
+      for (int p = 0; p < PREF; ++p) {
 #pragma unroll
-        for (int u = 0; u < NVM; ++u) cp.issue(kbeg + p, u);
+        for (int u = 0; u < NVM; ++u) cp.issue(u);
+        cp.advance();
+      }
       __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step kbeg landed
       __syncthreads();
       // steps before ksafe prefetch a step that lies wholly inside K: no tail check
       const int ksafe = (AK && BKC) ? max(kbeg, min(nk, g.K / KT - PREF)) : kbeg;
       auto pstep = [&](int kt, auto tail) {
 #pragma unroll
-        for (int u = 0; u < NVM; ++u) cp.template issue<decltype(tail)::value>(kt + PREF, u);
+        for (int u = 0; u < NVM; ++u) cp.template issue<decltype(tail)::value>(u);   // step kt + PREF
+        cp.advance();
         __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step kt+1 landed
         __syncthreads();
       };
@@ -630,11 +669,14 @@ __device__ __forceinline__ void gemm_tile(GemmArgs g, int bid0, char* smem) {
     const bool copier = ALL_COPY || wave < C::NCOPY;
     Copier<C, AK, BKC> cp;
     cp.init(g, m0, n0, wave, lane, smem);
-    if (copier) {
+    cp.start(kbeg);
 #pragma unroll
-      for (int p = 0; p < PREF; ++p)
+    for (int p = 0; p < PREF; ++p) {
+      if (copier) {
 #pragma unroll
-        for (int u = 0; u < NVM; ++u) cp.issue(kbeg + p, u);
+        for (int u = 0; u < NVM; ++u) cp.issue(u);
+      }
+      cp.advance();
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step kbeg landed
     __syncthreads();
@@ -657,12 +699,13 @@ __device__ __forceinline__ void gemm_tile(GemmArgs g, int bid0, char* smem) {
 #pragma unroll
             for (int u = 0; u < NVM; ++u)
               if ((u * PRE_MF) / NVM == t) {
-                if constexpr (ALL_COPY) cp.template issue<TAIL>(kt + PREF, u);
-                else if (copier) cp.template issue<TAIL>(kt + PREF, u);
+                if constexpr (ALL_COPY) cp.template issue<TAIL>(u);   // step kt + PREF
+                else if (copier) cp.template issue<TAIL>(u);
               }
           }
       }
       __builtin_amdgcn_s_setprio(0);
+      cp.advance();
       if constexpr (CS) cs.step(smem, kt, tiles_m, wave, lane);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step kt+1 landed
       __syncthreads();
