@@ -273,6 +273,9 @@ struct Reader {
   using V8 = typename Vec<E>::v8;
   using V4 = typename Vec<E>::v4;
   int wm, wn, l32, hi, kswz, tr_row, tr_col, tr_swz_a, tr_swz_b;
+  // K-contiguous operands: this lane's byte offset in the stage for k slice s
+  // of its first fragment; fragment i sits 32 i rows (an immediate) further.
+  int ka[KT / 16], kb[KT / 16];
 
   __device__ __forceinline__ void init(int wave, int lane) {
     wm = wave / C::CN;
@@ -280,6 +283,12 @@ struct Reader {
     l32 = lane & 31;
     hi = lane >> 5;
     kswz = (l32 >> 2) & 3;                      // K-contig slot swizzle of this lane's row
+#pragma unroll
+    for (int s = 0; s < KT / 16; ++s) {
+      const int slot = (2 * s + hi) ^ kswz;     // rows 32 i apart have the same swizzle
+      ka[s] = (wm * C::WM + l32) * (KT * 2) + slot * 16;
+      kb[s] = C::A_BYTES + (wn * C::WN + l32) * (KT * 2) + slot * 16;
+    }
     const int grp = lane >> 4, i16 = lane & 15; // transpose read: 16-lane group, lane in it
     tr_row = 8 * (grp >> 1) + (i16 >> 2);
     tr_col = 16 * (grp & 1) + 4 * (i16 & 3);
@@ -309,12 +318,17 @@ struct Reader {
   __device__ __forceinline__ void load(const char* smem, int kt, int s, V8* fa, V8* fb) const {
     const char* sa = smem + stage_of<C>(kt) * C::STAGE;
     const char* sb = sa + C::A_BYTES;
+    // (the producer/consumer kernels keep the per-fragment form: in their
+    // register budget the per-slice bases measured slower)
+    constexpr bool BASES = C::NPROD == 0;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
-      fa[i] = AK ? frag_k(sa, wm * C::WM + 32 * i, s) : frag_mn(sa, C::BM * 2, tr_swz_a, wm * C::WM + 32 * i, s);
+      fa[i] = !AK ? frag_mn(sa, C::BM * 2, tr_swz_a, wm * C::WM + 32 * i, s)
+                  : BASES ? *(const V8*)(sa + ka[s] + 32 * i * (KT * 2)) : frag_k(sa, wm * C::WM + 32 * i, s);
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
-      fb[j] = BKC ? frag_k(sb, wn * C::WN + 32 * j, s) : frag_mn(sb, C::BN * 2, tr_swz_b, wn * C::WN + 32 * j, s);
+      fb[j] = !BKC ? frag_mn(sb, C::BN * 2, tr_swz_b, wn * C::WN + 32 * j, s)
+                   : BASES ? *(const V8*)(sa + kb[s] + 32 * j * (KT * 2)) : frag_k(sb, wn * C::WN + 32 * j, s);
   }
 };
 
