@@ -276,6 +276,10 @@ struct Reader {
   // K-contiguous operands: this lane's byte offset in the stage for k slice s
   // of its first fragment; fragment i sits 32 i rows (an immediate) further.
   int ka[KT / 16], kb[KT / 16];
+  // M/N-contiguous operands: this lane's byte offset in the stage of the first
+  // transposing read of fragment i (j) in k slice 0; slice s and the second read
+  // are immediates further (16 s and 16 s + 4 k-rows).
+  int ma[C::FM], mb[C::FN];
 
   __device__ __forceinline__ void init(int wave, int lane) {
     wm = wave / C::CN;
@@ -294,6 +298,16 @@ struct Reader {
     tr_col = 16 * (grp & 1) + 4 * (i16 & 3);
     tr_swz_a = mn_swz<C::BM>(i16 >> 2);
     tr_swz_b = mn_swz<C::BN>(i16 >> 2);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+      const int col = wm * C::WM + 32 * i + tr_col;
+      ma[i] = tr_row * (C::BM * 2) + ((col >> 3) ^ tr_swz_a) * 16 + (col & 7) * 2;
+    }
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int col = wn * C::WN + 32 * j + tr_col;
+      mb[j] = C::A_BYTES + tr_row * (C::BN * 2) + ((col >> 3) ^ tr_swz_b) * 16 + (col & 7) * 2;
+    }
   }
   __device__ __forceinline__ V8 frag_k(const char* panel, int row0, int s) const {
     const int r = row0 + l32;
@@ -314,20 +328,37 @@ struct Reader {
     v[4] = hi_b[0]; v[5] = hi_b[1]; v[6] = hi_b[2]; v[7] = hi_b[3];
     return v;
   }
+  // The transposing reads of one M/N-contiguous fragment from its lane offset.
+  __device__ __forceinline__ V8 frag_mn_at(const char* p0, int row_bytes) const {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p0);
+    const i16x4 hv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(p0 + 4 * row_bytes));
+    const V4 lo_b = __builtin_bit_cast(V4, lo);
+    const V4 hi_b = __builtin_bit_cast(V4, hv);
+    V8 v;
+    v[0] = lo_b[0]; v[1] = lo_b[1]; v[2] = lo_b[2]; v[3] = lo_b[3];
+    v[4] = hi_b[0]; v[5] = hi_b[1]; v[6] = hi_b[2]; v[7] = hi_b[3];
+    return v;
+  }
   // Operands of 16-wide k slice s of K step kt.
   __device__ __forceinline__ void load(const char* smem, int kt, int s, V8* fa, V8* fb) const {
-    const char* sa = smem + stage_of<C>(kt) * C::STAGE;
+    load_at(smem + stage_of<C>(kt) * C::STAGE, s, fa, fb);
+  }
+  // The same from the stage at sa.
+  __device__ __forceinline__ void load_at(const char* sa, int s, V8* fa, V8* fb) const {
     const char* sb = sa + C::A_BYTES;
     // (the producer/consumer kernels keep the per-fragment form: in their
     // register budget the per-slice bases measured slower)
     constexpr bool BASES = C::NPROD == 0;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
-      fa[i] = !AK ? frag_mn(sa, C::BM * 2, tr_swz_a, wm * C::WM + 32 * i, s)
+      fa[i] = !AK ? (BASES ? frag_mn_at(sa + ma[i] + 16 * s * (C::BM * 2), C::BM * 2)
+                           : frag_mn(sa, C::BM * 2, tr_swz_a, wm * C::WM + 32 * i, s))
                   : BASES ? *(const V8*)(sa + ka[s] + 32 * i * (KT * 2)) : frag_k(sa, wm * C::WM + 32 * i, s);
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
-      fb[j] = !BKC ? frag_mn(sb, C::BN * 2, tr_swz_b, wn * C::WN + 32 * j, s)
+      fb[j] = !BKC ? (BASES ? frag_mn_at(sa + mb[j] + 16 * s * (C::BN * 2), C::BN * 2)
+                            : frag_mn(sb, C::BN * 2, tr_swz_b, wn * C::WN + 32 * j, s))
                    : BASES ? *(const V8*)(sa + kb[s] + 32 * j * (KT * 2)) : frag_k(sb, wn * C::WN + 32 * j, s);
   }
 };
@@ -638,12 +669,16 @@ __device__ __forceinline__ void gemm_tile(GemmArgs g, int bid0, char* smem) {
   if constexpr (C::NPROD > 0) {
     __syncthreads();  // step kbeg is in LDS
     V8 fa[2][FM], fb[2][FN];
-    rd.load(smem, kbeg, 0, fa[0], fb[0]);
+    // stages of steps kt and kt + 1, advanced around the ring once per step
+    const char* const ring_end = smem + C::NSTAGE * C::STAGE;
+    const char* st_k = smem + stage_of<C>(kbeg) * C::STAGE;
+    const char* st_n = st_k + C::STAGE == ring_end ? smem : st_k + C::STAGE;
+    rd.load_at(st_k, 0, fa[0], fb[0]);
     for (int kt = kbeg; kt < nk; ++kt) {
       if constexpr (AK && BKC) __builtin_amdgcn_s_setprio(1);  // see the shared kernel below
 #pragma unroll
       for (int s = 0; s < NS - 1; ++s) {
-        rd.load(smem, kt, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+        rd.load_at(st_k, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -659,7 +694,9 @@ __device__ __forceinline__ void gemm_tile(GemmArgs g, int bid0, char* smem) {
       if constexpr (AK && BKC) __builtin_amdgcn_s_setprio(0);
       if constexpr (CS) cs.step(smem, kt, tiles_m, wave, lane);
       __syncthreads();
-      rd.load(smem, kt + 1, 0, fa[LB ^ 1], fb[LB ^ 1]);
+      rd.load_at(st_n, 0, fa[LB ^ 1], fb[LB ^ 1]);
+      st_k = st_n;
+      st_n = st_n + C::STAGE == ring_end ? smem : st_n + C::STAGE;
 #pragma unroll
       for (int i = FM_HALF; i < FM; ++i)
 #pragma unroll
