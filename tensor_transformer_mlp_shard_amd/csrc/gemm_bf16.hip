@@ -734,8 +734,11 @@ __device__ __forceinline__ void gemm_tile(GemmArgs g, int bid0, char* smem) {
     constexpr int PRE_MF = FM * FN * (NS - 1) + FM_HALF * FN;   // MFMAs before the barrier
     static_assert(PRE_MF >= NVM, "not enough MFMAs to spread the copies over");
     V8 fa[FM], fb[FN];
-    auto kstep = [&](int kt, auto tail) {
+    // cpy: this wave issues copies (a constant: waves that copy and waves that
+    // do not run separate copies of the loop, so no copy sits behind a branch)
+    auto kstep = [&](int kt, auto tail, auto cpy) {
       constexpr bool TAIL = decltype(tail)::value;
+      constexpr bool CPY = decltype(cpy)::value;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         rd.load(smem, kt, s, fa, fb);
@@ -750,13 +753,12 @@ __device__ __forceinline__ void gemm_tile(GemmArgs g, int bid0, char* smem) {
 #pragma unroll
             for (int u = 0; u < NVM; ++u)
               if ((u * PRE_MF) / NVM == t) {
-                if constexpr (ALL_COPY) cp.template issue<TAIL>(u);   // step kt + PREF
-                else if (copier) cp.template issue<TAIL>(u);
+                if constexpr (CPY) cp.template issue<TAIL>(u);   // step kt + PREF
               }
           }
       }
       __builtin_amdgcn_s_setprio(0);
-      cp.advance();
+      if constexpr (CPY) cp.advance();
       if constexpr (CS) cs.step(smem, kt, tiles_m, wave, lane);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step kt+1 landed
       __syncthreads();
@@ -769,10 +771,15 @@ __device__ __forceinline__ void gemm_tile(GemmArgs g, int bid0, char* smem) {
     // (both operands K-contiguous, where every copy would carry it; on the other
     // layouts the second copy of the loop costs registers).
     const int ksafe = (AK && BKC) ? max(kbeg, min(nk, g.K / KT - PREF)) : kbeg;
-    int kt = kbeg;
-    if constexpr (AK && BKC)
-      for (; kt < ksafe; ++kt) kstep(kt, std::false_type{});
-    for (; kt < nk; ++kt) kstep(kt, std::true_type{});
+    auto kloop = [&](auto cpy) {
+      int kt = kbeg;
+      if constexpr (AK && BKC)
+        for (; kt < ksafe; ++kt) kstep(kt, std::false_type{}, cpy);
+      for (; kt < nk; ++kt) kstep(kt, std::true_type{}, cpy);
+    };
+    if constexpr (ALL_COPY) kloop(std::true_type{});
+    else if (copier) kloop(std::true_type{});
+    else kloop(std::false_type{});
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no copy into this workgroup's LDS outlives it
   }
 
