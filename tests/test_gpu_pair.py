@@ -85,3 +85,39 @@ def test_pair_row_linear_bwd_against_oracle(dtype):
     _rel("dX", f64(gr["dX"]), ref["dX"])
     _rel("dW", f64(gr["dW"]), ref["dW"])
     _rel("db", f64(gr["db"]), ref["db"], 1e-5)
+
+
+def test_pair_accumulate_adds():
+    # accumulate = 1 on the paired launches: the weight gradient beside the data
+    # gradient adds its product to the fp32 values already there (dB_i of the
+    # MLP, dW_i of the row linear), the bias gradients to theirs; one product is
+    # deterministic, so base + product matches the eager sum of the two exactly
+    T, h, F, p = 1000, 1536, 11264, 1
+    print(f"case MLP accumulate T={T} h={h} F={F}", flush=True)
+    d = synth.mlp_inputs(T, h, F, p, "bf16", 0.03, seed=223, full=False)
+    Xd, Ad, b1d, Bd, dYd = (dev(d[k]) for k in ("X", "A", "b1", "B", "dY"))
+    Z, H, _ = tps.mlp_shard_fwd(Xd, Ad, b1d, Bd, tp_size=p)
+    g1 = tps.mlp_shard_bwd(Xd, Ad, Bd, Z, H, dYd, tp_size=p, want_db2=True)
+    base = {k: torch.full_like(g1[k], 0.5) for k in ("dA", "dB", "db1", "db2")}
+    acc = {k: v.clone() for k, v in base.items()}
+    _, names = _traced(lambda: tps.mlp_shard_bwd(Xd, Ad, Bd, Z, H, dYd, tp_size=p, want_db2=True, accumulate=True,
+                                                 out=acc))
+    assert "gemm_bf16_pair_nt_dgelu_256x384+tn_f32_192x384" in names
+    for k in ("dA", "dB"):
+        assert torch.equal(acc[k], base[k] + g1[k]), k
+    for k in ("db1", "db2"):
+        torch.testing.assert_close(acc[k], base[k] + g1[k], rtol=1e-6, atol=1e-6)
+
+    T, K, N = 3000, 3328, 5120
+    print(f"case row linear accumulate T={T} k={K} N={N}", flush=True)
+    g = synth.seeded(311)
+    Xi = dev(synth.randn(g, (T, K), 1.0, "bf16"))
+    Wi = dev(synth.randn(g, (K, N), 0.02, "bf16"))
+    dY = dev(synth.randn(g, (T, N), 1.0, "bf16"))
+    r1 = tps.row_linear_bwd(Xi, Wi, dY, tp_size=1)
+    base = {k: torch.full_like(r1[k], -0.25) for k in ("dW", "db")}
+    acc = {k: v.clone() for k, v in base.items()}
+    _, names = _traced(lambda: tps.row_linear_bwd(Xi, Wi, dY, tp_size=1, accumulate=True, out=acc))
+    assert "gemm_bf16_pair_nt_store_256x384+tn_f32_192x384" in names
+    assert torch.equal(acc["dW"], base["dW"] + r1["dW"])
+    torch.testing.assert_close(acc["db"], base["db"] + r1["db"], rtol=1e-6, atol=1e-6)
