@@ -731,18 +731,20 @@ __device__ __forceinline__ void gemm_tile(GemmArgs g, int bid0, char* smem) {
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step kbeg landed
     __syncthreads();
-    constexpr int PRE_MF = FM * FN * (NS - 1) + FM_HALF * FN;   // MFMAs before the barrier
-    static_assert(PRE_MF >= NVM, "not enough MFMAs to spread the copies over");
     V8 fa[FM], fb[FN];
     // cpy: this wave issues copies (a constant: waves that copy and waves that
-    // do not run separate copies of the loop, so no copy sits behind a branch)
-    auto kstep = [&](int kt, auto tail, auto cpy) {
+    // do not run separate copies of the loop, so no copy sits behind a branch);
+    // fmh: rows of the last slice's MFMAs before the barrier
+    auto kstep = [&](int kt, auto tail, auto cpy, auto fmh) {
       constexpr bool TAIL = decltype(tail)::value;
       constexpr bool CPY = decltype(cpy)::value;
+      constexpr int FMH = decltype(fmh)::value;
+      constexpr int PRE_MF = FM * FN * (NS - 1) + FMH * FN;   // MFMAs before the barrier
+      static_assert(!CPY || PRE_MF >= NVM, "not enough MFMAs to spread the copies over");
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         rd.load(smem, kt, s, fa, fb);
-        const int i_end = (s == NS - 1) ? FM_HALF : FM;
+        const int i_end = (s == NS - 1) ? FMH : FM;
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < i_end; ++i)
@@ -763,7 +765,7 @@ __device__ __forceinline__ void gemm_tile(GemmArgs g, int bid0, char* smem) {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm((PREF - 1) * NVM));  // step kt+1 landed
       __syncthreads();
 #pragma unroll
-      for (int i = FM_HALF; i < FM; ++i)
+      for (int i = FMH; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) mfma(fa, fb, i, j);
     };
@@ -771,15 +773,26 @@ __device__ __forceinline__ void gemm_tile(GemmArgs g, int bid0, char* smem) {
     // (both operands K-contiguous, where every copy would carry it; on the other
     // layouts the second copy of the loop costs registers).
     const int ksafe = (AK && BKC) ? max(kbeg, min(nk, g.K / KT - PREF)) : kbeg;
-    auto kloop = [&](auto cpy) {
+    auto kloop = [&](auto cpy, auto fmh) {
       int kt = kbeg;
       if constexpr (AK && BKC)
-        for (; kt < ksafe; ++kt) kstep(kt, std::false_type{}, cpy);
-      for (; kt < nk; ++kt) kstep(kt, std::true_type{}, cpy);
+        for (; kt < ksafe; ++kt) kstep(kt, std::false_type{}, cpy, fmh);
+      for (; kt < nk; ++kt) kstep(kt, std::true_type{}, cpy, fmh);
     };
-    if constexpr (ALL_COPY) kloop(std::true_type{});
-    else if (copier) kloop(std::true_type{});
-    else kloop(std::false_type{});
+    // The first wave on each SIMD (waves 0-3, dispatched first) wins the matrix
+    // pipe while both have MFMAs ready, reaches the barrier ~460 cycles before
+    // the second (a cycle-stamped build of the 256 x 384 data gradient) and
+    // waits there.  Where A is K-contiguous and four rows of fragments are held,
+    // the second wave runs one row fewer before the barrier (and one more after
+    // it): 2 / 1 rows measured 0.7-1.7% faster than 2 / 2 on the NN / NT
+    // kernels (3 / 1 no better, 4 / 0 slower); the weight-gradient kernels keep
+    // one row on both waves (moving rows there was mixed).
+    constexpr int FHA = FM_HALF;
+    constexpr int FHB = (AK && FM >= 4) ? FM_HALF - 1 : FM_HALF;
+    static_assert(C::NCOPY == C::NCONS || C::NCOPY == 4, "copying waves are all, or the first on each SIMD");
+    if (wave < 4) kloop(std::true_type{}, std::integral_constant<int, FHA>{});
+    else if constexpr (ALL_COPY) kloop(std::true_type{}, std::integral_constant<int, FHB>{});
+    else kloop(std::false_type{}, std::integral_constant<int, FHB>{});
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no copy into this workgroup's LDS outlives it
   }
 
