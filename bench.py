@@ -542,7 +542,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU's shard; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path: run with --gpus 1)", file=sys.stderr)
+              "(the library has no multi-GPU path: run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch
